@@ -1,0 +1,266 @@
+"""Seeded synthetic inputs for the fused MoE router.
+
+This module only *builds inputs*: activations, gate matrices, selection biases
+and pre-computed logit rows.  It holds none of the router's arithmetic (no dot
+products, no scoring, no selection, no renormalisation), so both the HIP path
+and the CPU oracle can draw from it without sharing any of the method.
+
+Every generator is a pure function of its seed (numpy PCG64).  bf16 tensors are
+returned as their raw uint16 bit patterns (round-to-nearest-even from fp32).
+
+The shapes and distributions follow the workloads the router pages talk about:
+a 256-expert gate at hidden sizes 4096 and 7168, top-8 (softmax) and top-6
+(sqrt-softplus plus selection bias, the DeepSeek-V4 style), decode verify widths
+M in {1, 2, 8} and up to 64, and an 8192-token prefill.  No model weights exist
+here, so gate matrices are N(0, 1/H) and activations N(0, 1), which gives logits
+of unit scale, as a trained router's pre-activation logits roughly are.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+SOFTMAX = 0
+SQRT_SOFTPLUS = 1
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (input encoding only)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); return uint16 bits.
+
+    Inputs are finite by construction, so the NaN case is not handled.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = u + np.uint32(0x7FFF) + lsb
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 values (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class RouterCase:
+    """One router invocation's inputs (host arrays) and its settings."""
+    x: np.ndarray            # uint16 [M, H]  bf16 bits
+    w: np.ndarray            # uint16 [E, H]  bf16 bits
+    bias: Optional[np.ndarray]  # float32 [E] or None
+    k: int
+    scoring: int
+    renorm: bool
+    name: str = ""
+
+    @property
+    def M(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def E(self) -> int:
+        return int(self.w.shape[0])
+
+
+@dataclasses.dataclass
+class LogitsCase:
+    """One logits-to-top-k invocation's inputs."""
+    logits: np.ndarray       # float32 [M, E]
+    bias: Optional[np.ndarray]
+    k: int
+    scoring: int
+    renorm: bool
+    row_kind: np.ndarray     # int8 [M]: 0 plain, 1 exact tie, 2 one-ulp chain, 3 all equal
+    name: str = ""
+
+
+def _rng(seed: int, stream: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64([int(seed), int(stream)]))
+
+
+def gaussian_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    return f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def rms_normalised_bf16(rng: np.random.Generator, M: int, H: int, eps: float = 1e-6) -> np.ndarray:
+    """N(0,1) rows scaled to unit RMS (fp64, no gain), then rounded to bf16.
+
+    Stands in for the post-RMSNorm hidden state that feeds a decode router.
+    """
+    x = rng.standard_normal((M, H))
+    x = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    return f32_to_bf16_bits(x.astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# Router workloads
+# --------------------------------------------------------------------------
+def tiny_case(seed: int = 0) -> RouterCase:
+    """M=4, H=256, E=16, k=2, softmax, no bias, renorm."""
+    rng = _rng(seed, 1)
+    M, H, E = 4, 256, 16
+    x = gaussian_bf16(rng, (M, H), 1.0)
+    w = gaussian_bf16(rng, (E, H), 1.0 / np.sqrt(H))
+    return RouterCase(x, w, None, 2, SOFTMAX, True, name=f"tiny/seed{seed}")
+
+
+def tiny_tie_cases(seed: int = 0) -> list:
+    """Four single-token routers whose logits hold exact ties near the k=2 cut.
+
+    Ties are made structurally: two or three experts get *the same* bf16 gate
+    row, so any correct dot product gives bitwise-equal logits for them.  The
+    shared row is a scaled copy of the token so that the tied logits sit far
+    above the N(0,1) background; a further expert with twice that row is
+    placed above them when the tie must straddle the cut.
+
+      kind 0: one expert above, pair tied at ranks 2/3, lower index is the smaller one
+      kind 1: same, with the copy placed on the lower index
+      kind 2: pair tied at the very top (both selected, order by index)
+      kind 3: three-way tie at ranks 2/3/4
+    """
+    rng = _rng(seed, 2)
+    H, E = 256, 16
+    out = []
+    for kind in range(4):
+        xf = rng.standard_normal(H).astype(np.float32)
+        x = f32_to_bf16_bits(xf)
+        xb = bf16_bits_to_f32(x).astype(np.float64)
+        w = gaussian_bf16(rng, (E, H), 1.0 / np.sqrt(H))
+        c = 6.0 / float(xb @ xb)          # shared row logit ~ +6
+        shared = f32_to_bf16_bits((c * xb).astype(np.float32))
+        double = f32_to_bf16_bits((2.0 * c * xb).astype(np.float32))
+        experts = rng.permutation(E)
+        if kind in (0, 1):
+            a, b, d = (int(v) for v in experts[:3])
+            lo, hi = min(b, d), max(b, d)
+            src, dst = (lo, hi) if kind == 0 else (hi, lo)
+            w[a] = double
+            w[src] = shared
+            w[dst] = w[src]
+        elif kind == 2:
+            b, d = (int(v) for v in experts[:2])
+            w[b] = shared
+            w[d] = shared
+        else:
+            a, b, d, f = (int(v) for v in experts[:4])
+            w[a] = double
+            w[b] = shared
+            w[d] = shared
+            w[f] = shared
+        out.append(RouterCase(x[None, :], w, None, 2, SOFTMAX, True,
+                              name=f"tiny-tie/kind{kind}/seed{seed}"))
+    return out
+
+
+def decode_case(M: int, H: int = 4096, seed: int = 0, E: int = 256, k: int = 8) -> RouterCase:
+    """Verify-width decode router: unit-RMS activations, softmax, no bias, renorm."""
+    rng = _rng(seed, 3)
+    x = rms_normalised_bf16(rng, M, H)
+    w = gaussian_bf16(rng, (E, H), 1.0 / np.sqrt(H))
+    return RouterCase(x, w, None, k, SOFTMAX, True, name=f"decode/M{M}/H{H}/seed{seed}")
+
+
+def decode_gate_pool(n: int, H: int, seed: int, E: int = 256) -> np.ndarray:
+    """n distinct gate matrices (one per MoE layer), uint16 [n, E, H]."""
+    rng = _rng(seed, 4)
+    return gaussian_bf16(rng, (n, E, H), 1.0 / np.sqrt(H))
+
+
+def biased_case(M: int, seed: int = 0, H: int = 4096, E: int = 256, k: int = 6,
+                force_shared: Optional[bool] = None) -> RouterCase:
+    """DeepSeek-V4-style router: sqrt-softplus scores, U(-0.05,0.05) selection bias.
+
+    At M=2, seeds with seed % 10 < 3 (or force_shared=True) overwrite 1..6 gate
+    rows with a scaled copy of (x0/|x0|^2 + x1/|x1|^2), which puts those
+    experts' logits near +4 for *both* tokens, so the two tokens share them.
+    """
+    rng = _rng(seed, 5)
+    x = gaussian_bf16(rng, (M, H), 1.0)
+    w = gaussian_bf16(rng, (E, H), 1.0 / np.sqrt(H))
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    if force_shared is None:
+        force_shared = (M == 2 and seed % 10 < 3)
+    if force_shared:
+        assert M == 2
+        xb = bf16_bits_to_f32(x).astype(np.float64)
+        xhat = xb[0] / (xb[0] @ xb[0]) + xb[1] / (xb[1] @ xb[1])
+        s = int(rng.integers(1, 7))
+        rows = rng.choice(E, size=s, replace=False)
+        for r in rows:
+            alpha = 4.0 + 0.25 * rng.standard_normal()
+            w[r] = f32_to_bf16_bits((alpha * xhat).astype(np.float32))
+    return RouterCase(x, w, bias, k, SQRT_SOFTPLUS, True, name=f"biased/M{M}/seed{seed}")
+
+
+def prefill_case(M: int = 8192, H: int = 7168, seed: int = 0, E: int = 256, k: int = 8) -> RouterCase:
+    """Prefill router: softmax scores with U(-0.02,0.02) selection-only bias."""
+    rng = _rng(seed, 6)
+    x = gaussian_bf16(rng, (M, H), 1.0)
+    w = gaussian_bf16(rng, (E, H), 1.0 / np.sqrt(H))
+    bias = rng.uniform(-0.02, 0.02, E).astype(np.float32)
+    return RouterCase(x, w, bias, k, SOFTMAX, True, name=f"prefill/M{M}/H{H}/seed{seed}")
+
+
+def metric_case(seed: int = 0) -> RouterCase:
+    """Single-token decode at H=7168 (the latency headline shape)."""
+    c = decode_case(1, H=7168, seed=seed)
+    c.name = f"decode/M1/H7168/seed{seed}"
+    return c
+
+
+# --------------------------------------------------------------------------
+# Logits workloads (adversarial rows for the standalone top-k)
+# --------------------------------------------------------------------------
+PLAIN, EXACT_TIE, ULP_CHAIN, ALL_EQUAL = 0, 1, 2, 3
+
+
+def adversarial_logits(M: int, seed: int = 0, E: int = 256, k: int = 8,
+                       std: float = float(np.sqrt(2.0))) -> LogitsCase:
+    """fp32 logits ~ N(0, 2) with engineered rows around the k-th rank.
+
+    25% of rows: 2-4 entries straddling rank k are set exactly equal.
+    25% of rows: 2-4 entries straddling rank k form a chain 1 ulp apart,
+                 assigned to the experts in random order (so the larger value
+                 sometimes sits on the higher index).
+    10% of rows: all entries equal.
+    40% of rows: plain.
+    Placing the group needs the row's rank order, found with np.argsort; that
+    is input construction only (the expected output comes from the oracle).
+    """
+    rng = _rng(seed, 7)
+    logits = (rng.standard_normal((M, E)) * std).astype(np.float32)
+    u = rng.random(M)
+    kind = np.where(u < 0.25, EXACT_TIE, np.where(u < 0.5, ULP_CHAIN,
+                    np.where(u < 0.6, ALL_EQUAL, PLAIN))).astype(np.int8)
+    for r in range(M):
+        if kind[r] == ALL_EQUAL:
+            logits[r, :] = np.float32(rng.standard_normal() * std)
+            continue
+        if kind[r] == PLAIN:
+            continue
+        order = np.argsort(-logits[r].astype(np.float64), kind="stable")
+        g = int(rng.integers(2, 5))
+        g = min(g, E)
+        # group occupies ranks [s, s+g) with s <= k-1 < s+g-1, i.e. it straddles the cut
+        s_lo = max(0, k - g + 1)
+        s_hi = min(k - 1, E - g)
+        if s_hi < s_lo:
+            continue
+        s = int(rng.integers(s_lo, s_hi + 1))
+        members = order[s:s + g]
+        top = np.float32(logits[r, members[0]])
+        if kind[r] == EXACT_TIE:
+            logits[r, members] = top
+        else:
+            chain = [top]
+            for _ in range(g - 1):
+                chain.append(np.nextafter(chain[-1], np.float32(-np.inf), dtype=np.float32))
+            logits[r, rng.permutation(members)] = np.array(chain, dtype=np.float32)
+    return LogitsCase(logits, None, k, SOFTMAX, True, kind, name=f"adv-logits/M{M}/seed{seed}")

@@ -1,0 +1,145 @@
+"""CPU oracle for the fused MoE router — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (``gate_projection_top_amd``) never
+imports it and never falls back to it.
+
+The arithmetic lives in ``oracle.c`` (plain single-threaded C99, fp64); this
+module builds it with gcc if needed and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+SOURCES = [os.path.join(HERE, "oracle.c")]
+
+SOFTMAX = 0
+SQRT_SOFTPLUS = 1
+
+# -O2, no fast-math, no FMA contraction: every double operation rounds as written.
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-Wall", "-Wextra"]
+
+
+def build(out: str = LIB_PATH, sources=None, extra_flags=()) -> str:
+    """Compile the oracle with gcc into a shared library; return its path."""
+    srcs = list(sources) if sources is not None else SOURCES
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, *srcs, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+class Oracle:
+    """ctypes binding of one compiled oracle library."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            build(path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        ci = ctypes.c_int
+        lib.oracle_logits.argtypes = [P, P, i64, i64, i64, P, P]
+        lib.oracle_topk_from_logits.argtypes = [P, P, i64, i64, ci, ci, ci, P, P]
+        lib.oracle_router.argtypes = [P, P, P, i64, i64, i64, ci, ci, ci, P, P, P, P]
+        lib.oracle_route_table_m2.argtypes = [P, ci, P, P, P, P]
+        lib.oracle_row_scores.argtypes = [P, i64, ci, P, P]
+        for f in (lib.oracle_logits, lib.oracle_topk_from_logits, lib.oracle_router,
+                  lib.oracle_route_table_m2, lib.oracle_row_scores):
+            f.restype = ci
+        self.lib = lib
+
+    @staticmethod
+    def _ptr(a: Optional[np.ndarray]):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    def logits(self, x: np.ndarray, w: np.ndarray):
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        M, H = x.shape
+        E = w.shape[0]
+        assert w.shape[1] == H
+        out = np.empty((M, E), np.float32)
+        absdot = np.empty((M, E), np.float64)
+        rc = self.lib.oracle_logits(self._ptr(x), self._ptr(w), M, H, E, self._ptr(out),
+                                    self._ptr(absdot))
+        if rc:
+            raise ValueError(f"oracle_logits failed: {rc}")
+        return out, absdot
+
+    def topk_from_logits(self, logits: np.ndarray, bias: Optional[np.ndarray], k: int,
+                         scoring: int, renorm: bool):
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        M, E = logits.shape
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        inds = np.empty((M, k), np.int32)
+        wts = np.empty((M, k), np.float32)
+        rc = self.lib.oracle_topk_from_logits(self._ptr(logits), self._ptr(b), M, E, k,
+                                              int(scoring), int(bool(renorm)),
+                                              self._ptr(inds), self._ptr(wts))
+        if rc:
+            raise ValueError(f"oracle_topk_from_logits failed: {rc}")
+        return inds, wts
+
+    def router(self, x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], k: int,
+               scoring: int, renorm: bool):
+        """Return (inds, weights, logits, absdot)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        M, H = x.shape
+        E = w.shape[0]
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        inds = np.empty((M, k), np.int32)
+        wts = np.empty((M, k), np.float32)
+        lg = np.empty((M, E), np.float32)
+        ad = np.empty((M, E), np.float64)
+        rc = self.lib.oracle_router(self._ptr(x), self._ptr(w), self._ptr(b), M, H, E, k,
+                                    int(scoring), int(bool(renorm)), self._ptr(inds),
+                                    self._ptr(wts), self._ptr(lg), self._ptr(ad))
+        if rc:
+            raise ValueError(f"oracle_router failed: {rc}")
+        return inds, wts, lg, ad
+
+    def route_table_m2(self, inds: np.ndarray):
+        inds = np.ascontiguousarray(inds, dtype=np.int32)
+        assert inds.shape[0] == 2
+        k = inds.shape[1]
+        ids = np.empty(2 * k, np.int32)
+        mask = np.empty(2 * k, np.int32)
+        s2u = np.empty(2 * k, np.int32)
+        cnt = np.empty(1, np.int32)
+        rc = self.lib.oracle_route_table_m2(self._ptr(inds), k, self._ptr(ids), self._ptr(mask),
+                                            self._ptr(s2u), self._ptr(cnt))
+        if rc:
+            raise ValueError(f"oracle_route_table_m2 failed: {rc}")
+        return ids, mask, s2u, int(cnt[0])
+
+    def row_scores(self, row: np.ndarray, scoring: int):
+        row = np.ascontiguousarray(row, dtype=np.float32)
+        E = row.shape[0]
+        s = np.empty(E, np.float64)
+        u = np.empty(E, np.float64)
+        rc = self.lib.oracle_row_scores(self._ptr(row), E, int(scoring), self._ptr(s), self._ptr(u))
+        if rc:
+            raise ValueError(f"oracle_row_scores failed: {rc}")
+        return s, u
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The oracle built from oracle.c (built on first use if missing)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

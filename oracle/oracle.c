@@ -1,0 +1,234 @@
+/*
+ * CPU oracle for the fused MoE router — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests/, the smoke check and the benchmark's CPU-baseline leg may load
+ * this.  It is deliberately plain: one row at a time, fp64 throughout, no
+ * blocking, no fusion, no reordering beyond what each step's definition says.
+ * It shares no code with the HIP path.
+ *
+ * Sources (pages on the fused MoE router):
+ *  - qwisp issue #145, "Observation"/"Change": the gate matvec postNorm[H] ->
+ *    gateLogits[E=256] followed by a top-8 producing inds and scores.
+ *  - qwisp issue #145, "Bit-exactness": the tie order of the top-k selection is
+ *    part of the contract.  Here: keys descending, equal keys to the lower
+ *    expert index, emitted in that order.
+ *  - dense_router_decode commit notes ("DenseRouterDecodeKernel"): score is
+ *    sqrt(softplus(logit)) with the stable softplus max(x,0)+log(1+exp(-|x|));
+ *    selection is on score plus a per-expert bias; the heap carries the
+ *    unbiased activation beside the selection key, and the winners'
+ *    unbiased values are renormalised.
+ *  - b70 lab MTP1 note, "Unique-route router screen": the M=2 table of
+ *    encounter-ordered unique experts, per-expert token masks, slot-to-unique
+ *    map and unique count, leaving ids and weights untouched.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *  - logits are fp32: the exact dot product of the bf16 operands (summed in
+ *    double, in index order) rounded once to fp32;
+ *  - scores are computed in double from the fp32 logit and rounded once to
+ *    fp32 where they form a key; softplus uses log1p;
+ *  - with no bias the selection key is the logit itself (both scorings are
+ *    strictly increasing in it); with a bias the key is fl32(fl32(score)+bias),
+ *    the score being the softmax probability or the sqrt-softplus value;
+ *  - -0 and +0 are the same key;
+ *  - renormalised weight j = u_j / sum of the winners' u in rank order, with u
+ *    = exp(l - max l) for softmax and the sqrt-softplus value otherwise; without
+ *    renormalisation the weight is the full-row probability (softmax) or the
+ *    sqrt-softplus value; the bias never enters a weight;
+ *  - table: slots walked token-major then rank; an expert's position is the
+ *    order of its first appearance; mask bit t set when token t picked it;
+ *    unused ids are -1 and unused masks 0.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_logits(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, int64_t E,
+                  float* logits, double* absdot)
+{
+    if (M < 0 || H < 1 || E < 1 || (M > 0 && (!x || !w || !logits))) return ORACLE_EINVAL;
+    for (int64_t t = 0; t < M; ++t) {
+        const uint16_t* xr = x + t * H;
+        for (int64_t e = 0; e < E; ++e) {
+            const uint16_t* wr = w + e * H;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t i = 0; i < H; ++i) {
+                /* a product of two bf16 values is exact in double */
+                double p = bf16_value(xr[i]) * bf16_value(wr[i]);
+                acc += p;
+                mag += fabs(p);
+            }
+            logits[t * E + e] = (float)acc;
+            if (absdot) absdot[t * E + e] = mag;
+        }
+    }
+    return 0;
+}
+
+int oracle_row_scores(const float* l, int64_t E, int scoring, double* score, double* unbiased)
+{
+    if (E < 1 || !l || !score || !unbiased) return ORACLE_EINVAL;
+    if (scoring == ORACLE_SOFTMAX) {
+        double m = (double)l[0];
+        for (int64_t e = 1; e < E; ++e)
+            if ((double)l[e] > m) m = (double)l[e];
+        double Z = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            unbiased[e] = exp((double)l[e] - m);
+            Z += unbiased[e];
+        }
+        for (int64_t e = 0; e < E; ++e) score[e] = unbiased[e] / Z;
+    } else if (scoring == ORACLE_SQRT_SOFTPLUS) {
+        for (int64_t e = 0; e < E; ++e) {
+            double v = (double)l[e];
+            double softplus = fmax(v, 0.0) + log1p(exp(-fabs(v)));
+            score[e] = sqrt(softplus);
+            unbiased[e] = score[e];
+        }
+    } else {
+        return ORACLE_EINVAL;
+    }
+    return 0;
+}
+
+/* Does expert a (key ka) come before expert b (key kb) in the selection order? */
+static int precedes(float ka, int32_t a, float kb, int32_t b)
+{
+    if (ka > kb) return 1;
+    if (ka < kb) return 0;
+    return a < b;
+}
+
+int oracle_topk_from_logits(const float* logits, const float* bias, int64_t M, int64_t E,
+                            int k, int scoring, int renorm, int32_t* inds, float* weights)
+{
+    if (M < 0 || E < 1 || k < 1 || k > E) return ORACLE_EINVAL;
+    if (scoring != ORACLE_SOFTMAX && scoring != ORACLE_SQRT_SOFTPLUS) return ORACLE_EINVAL;
+    if (M > 0 && (!logits || !inds || !weights)) return ORACLE_EINVAL;
+
+    double* score = (double*)malloc((size_t)E * sizeof(double));
+    double* unb = (double*)malloc((size_t)E * sizeof(double));
+    float* key = (float*)malloc((size_t)E * sizeof(float));
+    float* top_key = (float*)malloc((size_t)k * sizeof(float));
+    int32_t* top_idx = (int32_t*)malloc((size_t)k * sizeof(int32_t));
+    int rc = 0;
+    if (!score || !unb || !key || !top_key || !top_idx) {
+        rc = ORACLE_ENOMEM;
+        goto done;
+    }
+
+    for (int64_t t = 0; t < M; ++t) {
+        const float* l = logits + t * E;
+        rc = oracle_row_scores(l, E, scoring, score, unb);
+        if (rc) goto done;
+
+        /* selection key */
+        for (int64_t e = 0; e < E; ++e) {
+            float kv;
+            if (bias) {
+                float s32 = (float)score[e];
+                kv = s32 + bias[e]; /* one fp32 addition, round to nearest */
+            } else {
+                kv = l[e];
+            }
+            if (!isfinite(kv)) {
+                rc = ORACLE_ENONFINITE;
+                goto done;
+            }
+            if (kv == 0.0f) kv = 0.0f; /* -0 and +0 are one key */
+            key[e] = kv;
+        }
+
+        /* top-k by insertion into a ranked list */
+        int filled = 0;
+        for (int64_t e = 0; e < E; ++e) {
+            int32_t idx = (int32_t)e;
+            float kv = key[e];
+            if (filled == k && !precedes(kv, idx, top_key[k - 1], top_idx[k - 1])) continue;
+            int pos = (filled < k) ? filled : k - 1;
+            /* walk up while the new entry precedes the one above it */
+            while (pos > 0 && precedes(kv, idx, top_key[pos - 1], top_idx[pos - 1])) {
+                top_key[pos] = top_key[pos - 1];
+                top_idx[pos] = top_idx[pos - 1];
+                --pos;
+            }
+            top_key[pos] = kv;
+            top_idx[pos] = idx;
+            if (filled < k) ++filled;
+        }
+
+        /* weights of the winners: unbiased values, optionally renormalised */
+        double total = 0.0;
+        for (int j = 0; j < k; ++j) total += unb[top_idx[j]];
+        for (int j = 0; j < k; ++j) {
+            int32_t e = top_idx[j];
+            double wgt;
+            if (renorm)
+                wgt = unb[e] / total;
+            else
+                wgt = score[e];
+            inds[t * k + j] = e;
+            weights[t * k + j] = (float)wgt;
+        }
+    }
+
+done:
+    free(score);
+    free(unb);
+    free(key);
+    free(top_key);
+    free(top_idx);
+    return rc;
+}
+
+int oracle_router(const uint16_t* x, const uint16_t* w, const float* bias, int64_t M,
+                  int64_t H, int64_t E, int k, int scoring, int renorm, int32_t* inds,
+                  float* weights, float* logits_out, double* absdot_out)
+{
+    if (M < 0 || H < 1 || E < 1 || k < 1 || k > E) return ORACLE_EINVAL;
+    if (M == 0) return 0;
+    float* l = logits_out ? logits_out : (float*)malloc((size_t)(M * E) * sizeof(float));
+    if (!l) return ORACLE_ENOMEM;
+    int rc = oracle_logits(x, w, M, H, E, l, absdot_out);
+    if (!rc) rc = oracle_topk_from_logits(l, bias, M, E, k, scoring, renorm, inds, weights);
+    if (!logits_out) free(l);
+    return rc;
+}
+
+int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* token_mask,
+                          int32_t* slot_to_unique, int32_t* count)
+{
+    if (k < 1 || !inds || !ids || !token_mask || !slot_to_unique || !count) return ORACLE_EINVAL;
+    int n = 2 * k;
+    int u = 0;
+    for (int i = 0; i < n; ++i) {
+        ids[i] = -1;
+        token_mask[i] = 0;
+    }
+    for (int s = 0; s < n; ++s) {
+        int token = s / k;
+        int pos = -1;
+        for (int q = 0; q < u; ++q)
+            if (ids[q] == inds[s]) {
+                pos = q;
+                break;
+            }
+        if (pos < 0) {
+            pos = u;
+            ids[u++] = inds[s];
+        }
+        slot_to_unique[s] = pos;
+        token_mask[pos] |= 1 << token;
+    }
+    *count = u;
+    return 0;
+}

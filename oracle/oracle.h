@@ -1,0 +1,68 @@
+/*
+ * CPU oracle for the fused MoE router — TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, single-threaded C99 in fp64.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the product path
+ * (librouter and its Python binding) never does.  It shares no source with
+ * the HIP path.
+ *
+ * What it computes is the plain definition of the router, taken from the
+ * pages on the fused route kernel (qwisp issue #145: the gate matvec
+ * postNorm[H] -> gateLogits[E] followed by a top-8 whose tie order is part of
+ * the contract), the dense-router decode notes (sqrt(softplus) activation,
+ * selection on score plus bias with unbiased weights kept beside the key,
+ * renormalised winners) and the B70 MTP1 M=2 note (the unique-route table).
+ *
+ * All functions return 0 on success and a negative value on bad arguments.
+ */
+#ifndef ROUTER_ORACLE_H
+#define ROUTER_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_SOFTMAX 0
+#define ORACLE_SQRT_SOFTPLUS 1
+
+#define ORACLE_EINVAL (-1)
+#define ORACLE_ENONFINITE (-2)
+#define ORACLE_ENOMEM (-3)
+
+/* logits[t,e] = fl32( sum_i x[t,i] * w[e,i] ), summed in i order in double;
+ * absdot[t,e] = sum_i |x[t,i] * w[e,i]| in double (may be NULL).
+ * x: bf16 bits [M,H]; w: bf16 bits [E,H]; both row-major. */
+int oracle_logits(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, int64_t E,
+                  float* logits, double* absdot);
+
+/* Scoring, key, top-k selection and weights on fp32 logits [M,E].
+ * bias: fp32 [E] or NULL (NULL selects on the logit itself).
+ * inds: int32 [M,k]; weights: fp32 [M,k]. */
+int oracle_topk_from_logits(const float* logits, const float* bias, int64_t M, int64_t E,
+                            int k, int scoring, int renorm, int32_t* inds, float* weights);
+
+/* The whole router: logits then oracle_topk_from_logits.  logits_out [M,E]
+ * and absdot_out [M,E] are optional (NULL). */
+int oracle_router(const uint16_t* x, const uint16_t* w, const float* bias, int64_t M,
+                  int64_t H, int64_t E, int k, int scoring, int renorm, int32_t* inds,
+                  float* weights, float* logits_out, double* absdot_out);
+
+/* Unique-route table for two tokens.  inds: [2,k] as produced by the router.
+ * ids [2k], token_mask [2k], slot_to_unique [2k], count [1]. */
+int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* token_mask,
+                          int32_t* slot_to_unique, int32_t* count);
+
+/* Per-row scores in double, as used by the key and the weights (exposed for
+ * the self-checks).  score[e]: softmax probability or sqrt-softplus value;
+ * unbiased[e]: the quantity renormalisation divides (exp(l-max) for softmax,
+ * the sqrt-softplus value otherwise). */
+int oracle_row_scores(const float* logits_row, int64_t E, int scoring, double* score,
+                      double* unbiased);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,409 @@
+"""Pins for the CPU oracle: checks against facts the mathematics fixes.
+
+Each pin is a function of an oracle instance that raises AssertionError when
+the oracle disagrees with a closed form, an exact computation, a brute-force
+enumeration, an independent library routine or an invariant.  None of them
+retypes the oracle's own code path:
+
+  * logits: exact integer / rational dot products (Python ints, Fractions),
+    one-hot gate rows, and numpy's BLAS float64 product;
+  * scores: softplus(0) = ln 2, softplus(x) -> x, softplus(x) ~ e^x, numpy's
+    logaddexp; softmax of equal logits is 1/E;
+  * selection: brute force over every k-subset (E <= 16) against the
+    contract "every selected expert precedes every unselected one", a stable
+    descending sort, k=1 = first argmax, k=E = the whole order;
+  * weights: renormalised weights sum to 1, equal winners get 1/k, softmax
+    renormalisation equals a softmax over the winners alone, the bias moves
+    the selection but never a weight;
+  * table: encounter order equals dict.fromkeys, hand-worked identical and
+    disjoint token pairs, structural invariants.
+
+tests/test_oracle_mutants.py plants plausible mistakes in copies of oracle.c
+and requires every planted mistake to fail at least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+
+from gate_projection_top_amd import workloads as W
+
+SOFTMAX, SQRT_SOFTPLUS = 0, 1
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+def fraction_to_f32(F: Fraction) -> np.float32:
+    """Round an exact rational to the nearest fp32 (ties to even)."""
+    c = np.float32(float(F))
+    best, best_err = None, None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        err = abs(Fraction(float(cand)) - F)
+        if best is None or err < best_err or (
+                err == best_err and (int(np.float32(cand).view(np.uint32)) & 1) == 0):
+            best, best_err = cand, err
+    return np.float32(best)
+
+
+def bf16_fraction(bits: int) -> Fraction:
+    return Fraction(float(W.bf16_bits_to_f32(np.array([bits], np.uint16))[0]))
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|bit-pattern distance| between same-sign fp32 arrays."""
+    ia = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+def precedence_matrix(keys: np.ndarray) -> np.ndarray:
+    """P[e, f] = expert e comes before expert f (key larger, or equal and lower index)."""
+    k = np.asarray(keys, np.float64)
+    E = k.shape[0]
+    idx = np.arange(E)
+    greater = k[:, None] > k[None, :]
+    equal = k[:, None] == k[None, :]
+    return greater | (equal & (idx[:, None] < idx[None, :]))
+
+
+def brute_force_topk(keys: np.ndarray, k: int) -> list:
+    """The unique k-subset whose every member precedes every non-member, in order."""
+    E = keys.shape[0]
+    P = precedence_matrix(keys)
+    found = []
+    for S in itertools.combinations(range(E), k):
+        inside = np.zeros(E, bool)
+        inside[list(S)] = True
+        if P[np.ix_(inside, ~inside)].all():
+            found.append(S)
+    assert len(found) == 1, f"contract admits {len(found)} subsets"
+    S = list(found[0])
+    # order inside the subset: e before f iff P[e, f]; count predecessors
+    return sorted(S, key=lambda e: sum(P[f, e] for f in S))
+
+
+def stable_desc_order(keys: np.ndarray) -> np.ndarray:
+    k = np.asarray(keys, np.float64).copy()
+    k[k == 0.0] = 0.0
+    return np.argsort(-k, kind="stable")
+
+
+# --------------------------------------------------------------------------
+# logits
+# --------------------------------------------------------------------------
+def pin_logits_small_integers(o):
+    """Small integers are exact in bf16; their dot product is an exact integer."""
+    rng = np.random.default_rng(11)
+    M, H, E = 3, 64, 5
+    xi = rng.integers(-8, 9, size=(M, H))
+    wi = rng.integers(-8, 9, size=(E, H))
+    x = W.f32_to_bf16_bits(xi.astype(np.float32))
+    w = W.f32_to_bf16_bits(wi.astype(np.float32))
+    lg, ad = o.logits(x, w)
+    for t in range(M):
+        for e in range(E):
+            exact = sum(int(a) * int(b) for a, b in zip(xi[t], wi[e]))
+            mag = sum(abs(int(a) * int(b)) for a, b in zip(xi[t], wi[e]))
+            assert lg[t, e] == np.float32(exact), (t, e, lg[t, e], exact)
+            assert ad[t, e] == float(mag), (t, e, ad[t, e], mag)
+
+
+def pin_logits_rational(o):
+    """Random bf16 operands: the logit is the exact rational dot rounded once to fp32."""
+    rng = np.random.default_rng(12)
+    M, H, E = 2, 32, 3
+    x = W.gaussian_bf16(rng, (M, H), 1.0)
+    w = W.gaussian_bf16(rng, (E, H), 0.3)
+    lg, ad = o.logits(x, w)
+    for t in range(M):
+        for e in range(E):
+            prods = [bf16_fraction(int(x[t, i])) * bf16_fraction(int(w[e, i])) for i in range(H)]
+            exact = sum(prods, Fraction(0))
+            assert lg[t, e] == fraction_to_f32(exact), (t, e)
+            assert Fraction(ad[t, e]) == sum((abs(p) for p in prods), Fraction(0)), (t, e)
+
+
+def pin_logits_one_hot(o):
+    """A one-hot gate row picks one activation: logit[t,e] = x[t, pos(e)]."""
+    rng = np.random.default_rng(13)
+    M, H, E = 3, 24, 7
+    x = W.gaussian_bf16(rng, (M, H), 1.0)
+    pos = rng.choice(H, size=E, replace=False)
+    wf = np.zeros((E, H), np.float32)
+    wf[np.arange(E), pos] = 1.0
+    lg, _ = o.logits(x, W.f32_to_bf16_bits(wf))
+    xf = W.bf16_bits_to_f32(x)
+    assert np.array_equal(lg, xf[:, pos]), (lg, xf[:, pos])
+
+
+def pin_logits_blas(o):
+    """numpy's float64 matmul (its own BLAS) agrees to rounding on unit-scale data."""
+    rng = np.random.default_rng(14)
+    M, H, E = 4, 512, 32
+    x = W.gaussian_bf16(rng, (M, H), 1.0)
+    w = W.gaussian_bf16(rng, (E, H), 1.0 / math.sqrt(H))
+    lg, _ = o.logits(x, w)
+    ref = W.bf16_bits_to_f32(x).astype(np.float64) @ W.bf16_bits_to_f32(w).astype(np.float64).T
+    assert np.all(np.abs(lg - ref) <= 1e-6 * np.maximum(1.0, np.abs(ref))), np.abs(lg - ref).max()
+
+
+# --------------------------------------------------------------------------
+# scores
+# --------------------------------------------------------------------------
+def pin_softplus_closed_forms(o):
+    """softplus(0)=ln2; softplus(40)=40 to double precision; softplus(-30)~e^-30."""
+    row = np.array([0.0, 40.0, -30.0, 1.0], np.float32)
+    s, u = o.row_scores(row, SQRT_SOFTPLUS)
+    assert abs(s[0] - math.sqrt(math.log(2.0))) <= 2e-16, s[0]
+    assert abs(s[1] - math.sqrt(40.0)) <= 2e-15, s[1]
+    assert abs(s[2] / math.exp(-15.0) - 1.0) <= 1e-12, s[2]
+    assert np.array_equal(s, u)
+    # softplus(1) = ln(1+e)
+    assert abs(s[3] - math.sqrt(math.log(1.0 + math.e))) <= 4e-16, s[3]
+
+
+def pin_softplus_logaddexp(o):
+    """sqrt(logaddexp(0, x)) (numpy's own routine) agrees to double rounding."""
+    rng = np.random.default_rng(15)
+    row = (rng.standard_normal(256) * 6.0).astype(np.float32)
+    s, _ = o.row_scores(row, SQRT_SOFTPLUS)
+    ref = np.sqrt(np.logaddexp(0.0, row.astype(np.float64)))
+    assert np.all(np.abs(s - ref) <= 8e-16 * ref), np.abs(s / ref - 1).max()
+
+
+def pin_softmax_closed_forms(o):
+    """Equal logits give 1/E; [0, c] gives 1/(1+e^-c); probabilities sum to 1."""
+    s, u = o.row_scores(np.full(8, 0.37, np.float32), SOFTMAX)
+    assert np.all(s == 0.125) and np.all(u == 1.0)
+    c = np.float32(math.log(3.0))
+    s, u = o.row_scores(np.array([0.0, c], np.float32), SOFTMAX)
+    assert abs(s[1] - 1.0 / (1.0 + math.exp(-float(c)))) <= 2e-16
+    assert abs(s[0] - math.exp(-float(c)) / (1.0 + math.exp(-float(c)))) <= 2e-16
+    rng = np.random.default_rng(16)
+    row = (rng.standard_normal(256) * 3).astype(np.float32)
+    s, u = o.row_scores(row, SOFTMAX)
+    assert abs(math.fsum(s) - 1.0) < 1e-14
+    assert u.max() == 1.0
+
+
+# --------------------------------------------------------------------------
+# selection
+# --------------------------------------------------------------------------
+def _tie_rows(rng, E, n):
+    """Rows drawn from a handful of values (so ties are everywhere), with +-0."""
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0, 2.0, 3.5], np.float32)
+    rows = [rng.choice(vals, size=E) for _ in range(n)]
+    rows.append(np.full(E, 0.5, np.float32))
+    rows.append(np.where(np.arange(E) % 2 == 0, np.float32(-0.0), np.float32(0.0)))
+    rows.append((rng.standard_normal(E)).astype(np.float32))
+    return np.stack(rows).astype(np.float32)
+
+
+def pin_topk_brute_force(o):
+    """E<=16: the oracle's set is the unique k-subset the contract admits, in order."""
+    rng = np.random.default_rng(17)
+    for E, ks in ((16, (1, 2, 3, 8, 15, 16)), (6, range(1, 7))):
+        rows = _tie_rows(rng, E, 6)
+        for k in ks:
+            inds, _ = o.topk_from_logits(rows, None, k, SOFTMAX, True)
+            for r in range(rows.shape[0]):
+                want = brute_force_topk(rows[r], k)
+                assert list(inds[r]) == want, (E, k, r, rows[r], inds[r], want)
+
+
+def pin_topk_stable_sort(o):
+    """First k of a stable descending sort (lower index first among equals)."""
+    rng = np.random.default_rng(18)
+    case = W.adversarial_logits(64, seed=3)
+    rows = np.concatenate([case.logits, _tie_rows(rng, 256, 4)])
+    for k in (1, 8, 13):
+        inds, _ = o.topk_from_logits(rows, None, k, SOFTMAX, True)
+        for r in range(rows.shape[0]):
+            assert np.array_equal(inds[r], stable_desc_order(rows[r])[:k]), (k, r)
+
+
+def pin_topk_extremes(o):
+    """k=1 is the first argmax; k=E lists every expert in contract order."""
+    rng = np.random.default_rng(19)
+    rows = _tie_rows(rng, 12, 5)
+    i1, _ = o.topk_from_logits(rows, None, 1, SOFTMAX, True)
+    assert np.array_equal(i1[:, 0], np.argmax(rows, axis=1))
+    iE, _ = o.topk_from_logits(rows, None, 12, SOFTMAX, True)
+    for r in range(rows.shape[0]):
+        assert sorted(iE[r]) == list(range(12))
+        assert list(iE[r]) == brute_force_topk(rows[r], 12)
+
+
+def pin_unbiased_key_is_exact_score_order(o):
+    """No bias: the order is that of the exact scores, i.e. of the logits.
+
+    Softmax and sqrt-softplus are strictly increasing, so a logit one ulp
+    above another has the larger exact score, even where both scores round to
+    the same fp32 value (which happens near zero, where a logit ulp is far
+    below a probability ulp).  The larger logit must win although it sits on
+    the higher index.
+    """
+    lo = np.float32(0.01)
+    hi = np.nextafter(lo, np.float32(np.inf))
+    row = np.full((1, 16), -5.0, np.float32)
+    row[0, 3], row[0, 9] = lo, hi
+    s, _ = o.row_scores(row[0], SOFTMAX)
+    assert np.float32(s[3]) == np.float32(s[9])  # the fp32 scores do collide
+    for scoring in (SOFTMAX, SQRT_SOFTPLUS):
+        inds, _ = o.topk_from_logits(row, None, 1, scoring, True)
+        assert inds[0, 0] == 9, (scoring, inds)
+        inds, _ = o.topk_from_logits(row, None, 2, scoring, True)
+        assert list(inds[0]) == [9, 3], (scoring, inds)
+
+
+def pin_all_equal_rows(o):
+    """All-equal logits: experts 0..k-1, weights 1/k (renorm) or 1/E (softmax, no renorm)."""
+    row = np.full((1, 256), -0.75, np.float32)
+    for scoring in (SOFTMAX, SQRT_SOFTPLUS):
+        inds, w = o.topk_from_logits(row, None, 8, scoring, True)
+        assert list(inds[0]) == list(range(8)) and np.all(w == np.float32(0.125))
+    inds, w = o.topk_from_logits(row, None, 8, SOFTMAX, False)
+    assert np.all(w == np.float32(1.0 / 256))
+
+
+def pin_bias_orders_equal_scores(o):
+    """Equal logits + distinct biases: selection follows the bias, weights stay equal."""
+    E, k = 32, 6
+    bias = (np.arange(E, dtype=np.float32) % 7) * np.float32(0.01) - np.float32(0.03)
+    row = np.full((1, E), 0.2, np.float32)
+    for scoring in (SOFTMAX, SQRT_SOFTPLUS):
+        inds, w = o.topk_from_logits(row, bias, k, scoring, True)
+        want = stable_desc_order(bias)[:k]
+        assert np.array_equal(inds[0], want), (scoring, inds[0], want)
+        assert np.all(w == np.float32(1.0 / k))
+
+
+def pin_bias_flips_but_weights_unbiased(o):
+    """Bias can put a lower-scored expert first; its weight stays the unbiased one."""
+    E = 8
+    row = np.array([[2.0, 1.0, -3, -3, -3, -3, -3, -3]], np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[1] = 0.5  # more than the score gap between experts 0 and 1
+    for scoring in (SOFTMAX, SQRT_SOFTPLUS):
+        inds, w = o.topk_from_logits(row, bias, 2, scoring, True)
+        assert list(inds[0]) == [1, 0], (scoring, inds)
+        if scoring == SOFTMAX:
+            e1 = math.exp(1.0 - 2.0)
+            want = [e1 / (e1 + 1.0), 1.0 / (e1 + 1.0)]
+        else:
+            s0 = math.sqrt(math.log1p(math.exp(2.0)))
+            s1 = math.sqrt(math.log1p(math.exp(1.0)))
+            want = [s1 / (s0 + s1), s0 / (s0 + s1)]
+        assert np.all(ulp_distance(w[0], np.array(want, np.float32)) <= 1), (w, want)
+
+
+def pin_bias_invariance(o):
+    """Two biases that pick the same ordered set give byte-identical weights."""
+    case = W.biased_case(4, seed=5, H=256)
+    lg, _ = o.logits(case.x, case.w)
+    for scoring in (SOFTMAX, SQRT_SOFTPLUS):
+        inds, w = o.topk_from_logits(lg, case.bias, case.k, scoring, True)
+        for r in range(lg.shape[0]):
+            b2 = case.bias.copy()
+            losers = np.setdiff1d(np.arange(case.E), inds[r])
+            b2[losers] -= np.float32(1.0)     # losers stay losers
+            i2, w2 = o.topk_from_logits(lg[r:r + 1], b2, case.k, scoring, True)
+            assert np.array_equal(i2[0], inds[r])
+            assert np.array_equal(w2[0].view(np.uint32), w[r].view(np.uint32))
+        # and bias-free selection of the same row gives the same weight for a shared winner set
+        i0, w0 = o.topk_from_logits(lg, None, case.k, scoring, True)
+        for r in range(lg.shape[0]):
+            if np.array_equal(i0[r], inds[r]):
+                assert np.array_equal(w0[r].view(np.uint32), w[r].view(np.uint32))
+
+
+def pin_renorm_sums_and_softmax_identity(o):
+    """Renormalised weights sum to 1; softmax renorm = softmax over the winners alone."""
+    case = W.adversarial_logits(32, seed=9)
+    for scoring in (SOFTMAX, SQRT_SOFTPLUS):
+        inds, w = o.topk_from_logits(case.logits, None, 8, scoring, True)
+        assert np.all(np.abs(w.astype(np.float64).sum(axis=1) - 1.0) <= 1e-6)
+    inds, w = o.topk_from_logits(case.logits, None, 8, SOFTMAX, True)
+    for r in range(case.logits.shape[0]):
+        sel = [float(case.logits[r, e]) for e in inds[r]]
+        ex = [math.exp(v) for v in sel]
+        tot = math.fsum(ex)
+        want = np.array([v / tot for v in ex], np.float32)
+        assert np.all(ulp_distance(w[r], want) <= 1), (r, w[r], want)
+
+
+def pin_softmax_no_renorm_is_probability(o):
+    """Without renormalisation a softmax weight is the full-row probability."""
+    rng = np.random.default_rng(20)
+    rows = (rng.standard_normal((8, 64)) * 2).astype(np.float32)
+    inds, w = o.topk_from_logits(rows, None, 4, SOFTMAX, False)
+    for r in range(rows.shape[0]):
+        ex = [math.exp(float(v)) for v in rows[r]]
+        tot = math.fsum(ex)
+        want = np.array([ex[e] / tot for e in inds[r]], np.float32)
+        assert np.all(ulp_distance(w[r], want) <= 1), (r, w[r], want)
+    inds, w = o.topk_from_logits(rows, None, 4, SQRT_SOFTPLUS, False)
+    for r in range(rows.shape[0]):
+        want = np.array([math.sqrt(math.log1p(math.exp(float(rows[r, e])))) for e in inds[r]],
+                        np.float32)
+        assert np.all(ulp_distance(w[r], want) <= 1), (r, w[r], want)
+
+
+# --------------------------------------------------------------------------
+# the M=2 unique-route table
+# --------------------------------------------------------------------------
+def pin_table_hand_cases(o):
+    """Identical tokens: k unique, masks 0b11; disjoint tokens: 2k unique, masks 1 then 2."""
+    k = 6
+    t0 = [7, 3, 200, 41, 0, 99]
+    same = np.array([t0, [3, 41, 7, 0, 99, 200]], np.int32)
+    ids, mask, s2u, cnt = o.route_table_m2(same)
+    assert cnt == k and list(ids[:k]) == t0 and list(ids[k:]) == [-1] * k
+    assert list(mask) == [3] * k + [0] * k
+    assert list(s2u[:k]) == list(range(k))
+    assert list(s2u[k:]) == [t0.index(e) for e in same[1]]
+    disjoint = np.array([t0, [1, 2, 4, 5, 6, 8]], np.int32)
+    ids, mask, s2u, cnt = o.route_table_m2(disjoint)
+    assert cnt == 2 * k and list(ids) == t0 + [1, 2, 4, 5, 6, 8]
+    assert list(mask) == [1] * k + [2] * k and list(s2u) == list(range(2 * k))
+    partial = np.array([[5, 9], [9, 4]], np.int32)
+    ids, mask, s2u, cnt = o.route_table_m2(partial)
+    assert cnt == 3 and list(ids) == [5, 9, 4, -1] and list(mask) == [1, 3, 2, 0]
+    assert list(s2u) == [0, 1, 1, 2]
+
+
+def pin_table_invariants(o):
+    """Random pairs: dict.fromkeys order, ids[s2u[s]] == slot id, mask bits = token membership."""
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        k = int(rng.integers(1, 9))
+        pool = rng.choice(256, size=int(rng.integers(k, 2 * k + 1)), replace=False)
+        inds = np.stack([rng.choice(pool, size=k, replace=False),
+                         rng.choice(pool, size=k, replace=False)]).astype(np.int32)
+        ids, mask, s2u, cnt = o.route_table_m2(inds)
+        slots = list(inds.reshape(-1))
+        uniq = list(dict.fromkeys(slots))
+        assert cnt == len(uniq) and list(ids[:cnt]) == uniq
+        assert np.all(ids[cnt:] == -1) and np.all(mask[cnt:] == 0)
+        for s, e in enumerate(slots):
+            assert ids[s2u[s]] == e
+        for q in range(cnt):
+            want = (1 if ids[q] in inds[0] else 0) | (2 if ids[q] in inds[1] else 0)
+            assert mask[q] == want
+        assert k <= cnt <= 2 * k
+        assert sum(bin(int(m)).count("1") for m in mask) == 2 * k
+
+
+ALL_PINS = [
+    pin_logits_small_integers, pin_logits_rational, pin_logits_one_hot, pin_logits_blas,
+    pin_softplus_closed_forms, pin_softplus_logaddexp, pin_softmax_closed_forms,
+    pin_topk_brute_force, pin_topk_stable_sort, pin_topk_extremes,
+    pin_unbiased_key_is_exact_score_order, pin_all_equal_rows,
+    pin_bias_orders_equal_scores, pin_bias_flips_but_weights_unbiased, pin_bias_invariance,
+    pin_renorm_sums_and_softmax_identity, pin_softmax_no_renorm_is_probability,
+    pin_table_hand_cases, pin_table_invariants,
+]

@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in copies of oracle.c; every one must fail a pin.
+
+This shows the pins are discriminating: a dropped term, a wrong sign, a wrong
+index, a transposed operand or a flipped tie-break anywhere in the oracle is
+caught by at least one check against the mathematics.  Mutants are built in a
+temporary directory on the CPU; the real oracle is untouched.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("tie_to_higher_index", "return a < b;", "return a > b;"),
+    ("tie_not_strict", "if (ka > kb) return 1;", "if (ka >= kb) return 1;"),
+    ("dot_drops_last_term", "for (int64_t i = 0; i < H; ++i) {", "for (int64_t i = 0; i + 1 < H; ++i) {"),
+    ("dot_transposed_operand", "const uint16_t* wr = w + e * H;", "const uint16_t* wr = w + (e % (M > 0 ? M : 1)) * H;"),
+    ("dot_wrong_x_row", "const uint16_t* xr = x + t * H;", "const uint16_t* xr = x;"),
+    ("absdot_signed", "mag += fabs(p);", "mag += p;"),
+    ("softplus_drops_linear_term", "double softplus = fmax(v, 0.0) + log1p(exp(-fabs(v)));",
+     "double softplus = log1p(exp(-fabs(v)));"),
+    ("softplus_sign_flip", "double softplus = fmax(v, 0.0) + log1p(exp(-fabs(v)));",
+     "double softplus = fmax(v, 0.0) + log1p(exp(fabs(v)));"),
+    ("softplus_no_sqrt", "score[e] = sqrt(softplus);", "score[e] = softplus;"),
+    ("softmax_no_normalise", "for (int64_t e = 0; e < E; ++e) score[e] = unbiased[e] / Z;",
+     "for (int64_t e = 0; e < E; ++e) score[e] = unbiased[e];"),
+    ("softmax_wrong_shift_sign", "unbiased[e] = exp((double)l[e] - m);", "unbiased[e] = exp(m - (double)l[e]);"),
+    ("key_ignores_bias", "kv = s32 + bias[e];", "kv = s32;"),
+    ("key_bias_on_logit", "kv = s32 + bias[e];", "kv = l[e] + bias[e];"),
+    ("key_is_score_without_bias", "kv = l[e];", "kv = (float)score[e] + 0.0f * l[e];"),
+    ("weights_use_key", "wgt = unb[e] / total;", "wgt = key[e] / total;"),
+    ("renorm_over_all_experts", "for (int j = 0; j < k; ++j) total += unb[top_idx[j]];",
+     "for (int j = 0; j < E; ++j) total += unb[j];"),
+    ("no_renorm_uses_unnormalised", "wgt = score[e];", "wgt = unb[e];"),
+    ("insertion_skips_top_slot", "while (pos > 0 && precedes(", "while (pos > 1 && precedes("),
+    ("insertion_ignores_full_list", "if (filled == k && !precedes(", "if (filled == k && precedes("),
+    ("table_token_from_rank", "int token = s / k;", "int token = s % 2;"),
+    ("table_tail_zero", "ids[i] = -1;", "ids[i] = 0;"),
+    ("table_mask_overwrite", "token_mask[pos] |= 1 << token;", "token_mask[pos] = 1 << token;"),
+    ("table_slot_map_raw", "slot_to_unique[s] = pos;", "slot_to_unique[s] = s;"),
+]
+
+
+@pytest.fixture(scope="module")
+def src_text():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, src_text, name, old, new):
+    assert src_text.count(old) == 1, f"mutation anchor not unique/absent: {old!r}"
+    mutated = src_text.replace(old, new)
+    path = tmp_path / "oracle_mut.c"
+    path.write_text(mutated)
+    lib = str(tmp_path / f"liboracle_{name}.so")
+    oracle.build(lib, sources=[str(path)], extra_flags=["-w"])
+    orc = oracle.Oracle(lib)
+    failures = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError, ZeroDivisionError, OverflowError) as exc:
+            failures.append((pin.__name__, type(exc).__name__))
+    assert failures, f"planted mistake {name} passed every pin"
