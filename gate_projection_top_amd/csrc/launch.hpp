@@ -1,0 +1,59 @@
+// Internal launch interface between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt {
+
+struct TopkLaunch {
+    const float* logits;
+    const float* bias;
+    int64_t M;
+    int E, k, scoring, renorm;
+    int vector_rows;  // rows are 16-byte aligned and E % 4 == 0
+    int32_t* inds;
+    float* weights;
+};
+
+// Decode: M <= 64 tokens.  Grid = R row blocks x B expert blocks x S H-splits.
+struct DecodeLaunch {
+    const uint16_t* x;
+    const uint16_t* w;
+    const float* bias;
+    int M, H, E, k, scoring, renorm;
+    int32_t* inds;
+    float* weights;
+    float* logits_out;      // optional
+    int32_t* table_ids;     // M == 2 table (all four set or all NULL)
+    int32_t* table_mask;
+    int32_t* table_s2u;
+    int32_t* table_count;
+    float* partials;        // workspace [S][M][E]
+    uint32_t* counters;     // workspace [R], zero between calls
+    int S;                  // H splits
+    int ks_per_split;       // 32-wide k-steps per split
+};
+
+struct PrefillLaunch {
+    const uint16_t* x;
+    const uint16_t* w;
+    const float* bias;
+    int64_t M;
+    int H, E, k, scoring, renorm;
+    int32_t* inds;
+    float* weights;
+    float* logits_out;      // optional
+};
+
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+
+// Decode geometry shared by the host (workspace sizing) and the launcher.
+constexpr int kDecodeTile = 16;        // rows per row block, experts per expert block
+constexpr int kDecodeMaxSplits = 16;   // H splits
+constexpr int kDecodeMaxM = 64;
+constexpr int kDecodeMaxRowBlocks = kDecodeMaxM / kDecodeTile;
+
+}  // namespace gpt

@@ -1,0 +1,279 @@
+// Device-side routing of one row: scoring, selection key, top-k under the
+// tie contract, weights, and the M=2 unique-route table.
+//
+// Every kernel (decode, prefill, standalone top-k) routes a row through
+// route_row(), so fused and unfused paths give bit-identical results on
+// identical logits (qwisp issue #145, gate G-A: fused vs unfused must agree
+// bit for bit, including exact and near ties at the top-8 cut).
+//
+// Layout contract: one 64-lane wavefront per row, lane L holding the logits of
+// experts 4L..4L+3 (E <= 256).  Because lanes are in expert order, the lowest
+// lane holding the maximum key also holds the lowest expert index among the
+// tied maxima, which is how ties go to the lower index without a 64-bit key.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt {
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 16;
+constexpr int kPerLane = kMaxE / kWave;  // 4 experts per lane
+
+enum : int { kSoftmax = 0, kSqrtSoftplus = 1 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// cross-lane primitives (full wavefront active)
+// ---------------------------------------------------------------------------
+// DPP controls: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+// row_ror:4 = 0x124, row_ror:8 = 0x128.  After these four steps every lane
+// holds the reduction over its 16-lane row; the four rows are then combined
+// through scalar registers in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = readlane_u32((uint32_t)u, lane);
+    const uint32_t hi = readlane_u32((uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp_u32<CTRL>((uint32_t)u);
+    const uint32_t hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x124>(v));
+    v = max(v, dpp_u32<0x128>(v));
+    const uint32_t a = readlane_u32(v, 0), b = readlane_u32(v, 16);
+    const uint32_t c = readlane_u32(v, 32), d = readlane_u32(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ float wave_max_f32(float f)
+{
+    uint32_t v = __float_as_uint(f);
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0xB1>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x4E>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x124>(v))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x128>(v))));
+    const float a = __uint_as_float(readlane_u32(v, 0)), b = __uint_as_float(readlane_u32(v, 16));
+    const float c = __uint_as_float(readlane_u32(v, 32)), d = __uint_as_float(readlane_u32(v, 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Sum over the wavefront in a fixed association: the 16-lane row sums are
+// read from lanes 0, 16, 32, 48 and added in that order, so the result is a
+// deterministic function of the 64 inputs.
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    v = v + dpp_f64<0xB1>(v);
+    v = v + dpp_f64<0x4E>(v);
+    v = v + dpp_f64<0x124>(v);
+    v = v + dpp_f64<0x128>(v);
+    const double a = readlane_f64(v, 0), b = readlane_f64(v, 16);
+    const double c = readlane_f64(v, 32), d = readlane_f64(v, 48);
+    return ((a + b) + c) + d;
+}
+
+// ---------------------------------------------------------------------------
+// scoring and keys
+// ---------------------------------------------------------------------------
+// Monotone map from a finite fp32 key to uint32 (larger key -> larger code),
+// with -0 folded onto +0.  Code 0 is below every finite key and marks an
+// entry that is absent or already selected.
+__device__ __forceinline__ uint32_t order_code(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u = (f == 0.0f) ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// sqrt(softplus(l)) with the stable softplus max(l,0) + log1p(exp(-|l|))
+// (dense_router_decode notes, "Numerically stable softplus"), in double.
+__device__ __forceinline__ double sqrt_softplus(float l)
+{
+    const double v = (double)l;
+    return sqrt(fmax(v, 0.0) + log1p(exp(-fabs(v))));
+}
+
+struct RowSpec {
+    int E;
+    int k;
+    int scoring;
+    int renorm;
+    int has_bias;
+};
+
+struct RowResult {
+    int idx;    // lane j < k: expert of rank j
+    float w;    // lane j < k: its weight
+};
+
+// Route one row.  v[j]: logit of expert 4*lane+j (ignored when >= E);
+// bv[j]: its selection bias (used only when s.has_bias).
+__device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
+                                               const float (&bv)[kPerLane], const RowSpec& s)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    bool valid[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) valid[j] = (lane * kPerLane + j) < s.E;
+
+    const bool softmax = s.scoring == kSoftmax;
+    float mx = -__builtin_inff();
+    if (softmax) {
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j)
+            if (valid[j]) mx = fmaxf(mx, v[j]);
+        mx = wave_max_f32(mx);
+    }
+
+    // Scores for every expert are needed only when they form the key or when
+    // a softmax weight is the full-row probability.
+    const bool need_all = s.has_bias || (softmax && !s.renorm);
+    double Z = 1.0;
+    double sc[kPerLane] = {0.0, 0.0, 0.0, 0.0};
+    if (need_all) {
+        if (softmax) {
+            double z[kPerLane];
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j)
+                z[j] = valid[j] ? exp((double)v[j] - (double)mx) : 0.0;
+            Z = wave_sum_f64(((z[0] + z[1]) + z[2]) + z[3]);
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) sc[j] = z[j] / Z;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) sc[j] = valid[j] ? sqrt_softplus(v[j]) : 0.0;
+        }
+    }
+
+    uint32_t code[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        float key = v[j];
+        if (s.has_bias) {
+            const float s32 = (float)sc[j];
+            key = s32 + bv[j];
+        }
+        code[j] = valid[j] ? order_code(key) : 0u;
+    }
+
+    // k rounds of wave arg-max.  The winner is the largest code; among equal
+    // codes the lowest lane, and inside a lane the lowest slot (strict >
+    // below), i.e. the lowest expert index.
+    int my_idx = 0;
+    float my_logit = 0.0f;
+    for (int it = 0; it < s.k; ++it) {
+        uint32_t best = code[0];
+        int bj = 0;
+        float bl = v[0];
+#pragma unroll
+        for (int j = 1; j < kPerLane; ++j) {
+            const bool gt = code[j] > best;
+            best = gt ? code[j] : best;
+            bj = gt ? j : bj;
+            bl = gt ? v[j] : bl;
+        }
+        const uint32_t top = wave_max_u32(best);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(best == top);
+        const int L = (int)__builtin_ctzll(hit);
+        const int wj = __builtin_amdgcn_readlane(bj, L);
+        const float wl = __uint_as_float(readlane_u32(__float_as_uint(bl), L));
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) code[j] = (lane == L && j == wj) ? 0u : code[j];
+        if (lane == it) {
+            my_idx = L * kPerLane + wj;
+            my_logit = wl;
+        }
+    }
+
+    // Weights from the unbiased scores; the bias never enters here.
+    double u = 0.0;
+    if (lane < s.k) u = softmax ? exp((double)my_logit - (double)mx) : sqrt_softplus(my_logit);
+    float w;
+    if (s.renorm) {
+        double total = 0.0;
+        for (int j = 0; j < s.k; ++j) total += readlane_f64(u, j);
+        w = (float)(u / total);
+    } else {
+        w = softmax ? (float)(u / Z) : (float)u;
+    }
+    return RowResult{my_idx, w};
+}
+
+// ---------------------------------------------------------------------------
+// M=2 unique-route table (b70 lab MTP1 note, "Unique-route router screen")
+// ---------------------------------------------------------------------------
+// One wavefront; slot s = t*k + j holds inds[t][j] (2k <= 64 slots).  Stable
+// de-duplication by first appearance, ranks by a prefix count of first
+// appearances, token masks gathered onto each first appearance.
+__device__ __forceinline__ void emit_route_table_m2(const int32_t* slot_ids, int k,
+                                                    int32_t* ids, int32_t* mask,
+                                                    int32_t* slot_to_unique, int32_t* count)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = 2 * k;
+    const bool active = lane < n;
+    const int id = active ? slot_ids[lane] : -1 - lane;  // inactive lanes never match
+
+    int first = -1;
+    for (int j = 0; j < n; ++j) {
+        const int idj = __builtin_amdgcn_readlane(id, j);
+        if (first < 0 && idj == id) first = j;
+    }
+    const uint64_t firsts = __builtin_amdgcn_ballot_w64(active && first == lane);
+    const int unique = __builtin_popcountll(firsts);
+    const int rank = active ? __builtin_popcountll(firsts & ((1ull << first) - 1ull)) : 0;
+
+    int token_bits = 0;
+    for (int j = 0; j < n; ++j) {
+        const int fj = __builtin_amdgcn_readlane(first, j);
+        if (lane == fj) token_bits |= 1 << (j / k);
+    }
+
+    if (active) {
+        slot_to_unique[lane] = rank;
+        if (first == lane) {
+            ids[rank] = id;
+            mask[rank] = token_bits;
+        }
+        if (lane >= unique) {
+            ids[lane] = -1;
+            mask[lane] = 0;
+        }
+    }
+    if (lane == 0) count[0] = unique;
+}
+
+// 16-byte load of 8 bf16 values.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
+{
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+}  // namespace gpt

@@ -1,0 +1,238 @@
+// C-ABI layer of librouter: argument validation, the per-device workspace,
+// and the choice between the decode and prefill kernels.  No arithmetic of
+// the router happens here; every step runs in the HIP kernels.
+#include "router.h"
+
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+struct DeviceWorkspace {
+    float* partials = nullptr;     // decode H-split partial logits [S][M][E]
+    uint32_t* counters = nullptr;  // decode arrival counters, one per row block
+};
+
+constexpr int kMaxDevices = 64;
+constexpr size_t kPartialFloats =
+    (size_t)gpt::kDecodeMaxSplits * gpt::kDecodeMaxM * ROUTER_MAX_E;  // 1 MiB
+constexpr int kCounters = 64;
+
+DeviceWorkspace g_ws[kMaxDevices];
+std::mutex g_ws_mutex;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int init_device(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> guard(g_ws_mutex);
+    if (g_ws[dev].partials) return ROUTER_OK;
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return ROUTER_ERR_HIP;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) return ROUTER_ERR_HIP;
+
+    float* partials = nullptr;
+    uint32_t* counters = nullptr;
+    hipError_t e = hipMalloc((void**)&partials, kPartialFloats * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&counters, kCounters * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(counters, 0, kCounters * sizeof(uint32_t));
+    // The counters must read zero before any stream (blocking or not) runs a
+    // decode kernel; init is rare, so a device-wide wait is acceptable here.
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (prev != dev) (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+        if (partials) (void)hipFree(partials);
+        if (counters) (void)hipFree(counters);
+        return ROUTER_ERR_NO_WORKSPACE;
+    }
+    g_ws[dev].partials = partials;
+    g_ws[dev].counters = counters;
+    return ROUTER_OK;
+}
+
+int current_workspace(DeviceWorkspace* out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ROUTER_ERR_HIP;
+    const int rc = init_device(dev);
+    if (rc != ROUTER_OK) return rc;
+    *out = g_ws[dev];
+    return ROUTER_OK;
+}
+
+int check_common(int64_t M, int E, int k, int scoring, int renorm)
+{
+    if (scoring != ROUTER_SCORING_SOFTMAX && scoring != ROUTER_SCORING_SQRT_SOFTPLUS)
+        return ROUTER_ERR_INVALID_ARGUMENT;
+    if (renorm != 0 && renorm != 1) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (M < 0 || E < 1 || k < 1 || k > E) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (E > ROUTER_MAX_E || k > ROUTER_MAX_K) return ROUTER_ERR_UNSUPPORTED;
+    return ROUTER_OK;
+}
+
+int check_hidden(int H)
+{
+    if (H < 1) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (H % 8 != 0) return ROUTER_ERR_UNSUPPORTED;
+    return ROUTER_OK;
+}
+
+int check_projection(const void* x, const void* w)
+{
+    if (!x || !w) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w)) return ROUTER_ERR_MISALIGNED;
+    return ROUTER_OK;
+}
+
+// Decode split choice: aim for >= 256 workgroups (one per CU) with at least
+// one k-step per wave in every split.
+void decode_splits(int M, int H, int E, int* S_out, int* ks_per_split_out)
+{
+    const int R = (M + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
+    const int B = (E + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
+    const int KS = (H + 31) / 32;
+    int S = (256 + R * B - 1) / (R * B);
+    const int by_work = KS / 4 > 1 ? KS / 4 : 1;
+    if (S > by_work) S = by_work;
+    if (S > gpt::kDecodeMaxSplits) S = gpt::kDecodeMaxSplits;
+    if (S < 1) S = 1;
+    const int per = (KS + S - 1) / S;
+    *ks_per_split_out = per;
+    *S_out = (KS + per - 1) / per;
+}
+
+int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
+              int scoring, int renorm, int32_t* inds, float* weights, float* logits,
+              int32_t* t_ids, int32_t* t_mask, int32_t* t_s2u, int32_t* t_count,
+              hipStream_t stream)
+{
+    hipError_t e;
+    if (M <= ROUTER_DECODE_MAX_M) {
+        DeviceWorkspace ws;
+        const int rc = current_workspace(&ws);
+        if (rc != ROUTER_OK) return rc;
+        gpt::DecodeLaunch a{};
+        a.x = static_cast<const uint16_t*>(x);
+        a.w = static_cast<const uint16_t*>(w);
+        a.bias = bias;
+        a.M = (int)M;
+        a.H = H;
+        a.E = E;
+        a.k = k;
+        a.scoring = scoring;
+        a.renorm = renorm;
+        a.inds = inds;
+        a.weights = weights;
+        a.logits_out = logits;
+        a.table_ids = t_ids;
+        a.table_mask = t_mask;
+        a.table_s2u = t_s2u;
+        a.table_count = t_count;
+        a.partials = ws.partials;
+        a.counters = ws.counters;
+        decode_splits((int)M, H, E, &a.S, &a.ks_per_split);
+        e = gpt::launch_decode(a, stream);
+    } else {
+        gpt::PrefillLaunch a{};
+        a.x = static_cast<const uint16_t*>(x);
+        a.w = static_cast<const uint16_t*>(w);
+        a.bias = bias;
+        a.M = M;
+        a.H = H;
+        a.E = E;
+        a.k = k;
+        a.scoring = scoring;
+        a.renorm = renorm;
+        a.inds = inds;
+        a.weights = weights;
+        a.logits_out = logits;
+        e = gpt::launch_prefill(a, stream);
+    }
+    return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int router_init(int device)
+{
+    if (device < 0) {
+        if (hipGetDevice(&device) != hipSuccess) return ROUTER_ERR_HIP;
+    }
+    return init_device(device);
+}
+
+int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
+               int scoring, int renorm, int32_t* out_inds, float* out_weights,
+               float* opt_out_logits, hipStream_t stream)
+{
+    int rc = check_common(M, E, k, scoring, renorm);
+    if (rc == ROUTER_OK) rc = check_hidden(H);
+    if (rc != ROUTER_OK) return rc;
+    if (M == 0) return ROUTER_OK;
+    rc = check_projection(x, w);
+    if (rc != ROUTER_OK) return rc;
+    if (!out_inds || !out_weights) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (M > 0x7fffffffLL / 256) return ROUTER_ERR_UNSUPPORTED;
+    return run_fused(x, w, bias, M, H, E, k, scoring, renorm, out_inds, out_weights,
+                     opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+int router_fwd_m2_table(const void* x, const void* w, const float* bias, int H, int E, int k,
+                        int scoring, int renorm, int32_t* out_inds, float* out_weights,
+                        float* opt_out_logits, int32_t* out_unique_ids,
+                        int32_t* out_token_mask, int32_t* out_slot_to_unique,
+                        int32_t* out_unique_count, hipStream_t stream)
+{
+    int rc = check_common(2, E, k, scoring, renorm);
+    if (rc == ROUTER_OK) rc = check_hidden(H);
+    if (rc == ROUTER_OK) rc = check_projection(x, w);
+    if (rc != ROUTER_OK) return rc;
+    if (!out_inds || !out_weights || !out_unique_ids || !out_token_mask || !out_slot_to_unique ||
+        !out_unique_count)
+        return ROUTER_ERR_INVALID_ARGUMENT;
+    return run_fused(x, w, bias, 2, H, E, k, scoring, renorm, out_inds, out_weights,
+                     opt_out_logits, out_unique_ids, out_token_mask, out_slot_to_unique,
+                     out_unique_count, stream);
+}
+
+int router_topk_from_logits(const float* logits, const float* bias, int64_t M, int E, int k,
+                            int scoring, int renorm, int32_t* out_inds, float* out_weights,
+                            hipStream_t stream)
+{
+    const int rc = check_common(M, E, k, scoring, renorm);
+    if (rc != ROUTER_OK) return rc;
+    if (M == 0) return ROUTER_OK;
+    if (!logits || !out_inds || !out_weights) return ROUTER_ERR_INVALID_ARGUMENT;
+    gpt::TopkLaunch a{};
+    a.logits = logits;
+    a.bias = bias;
+    a.M = M;
+    a.E = E;
+    a.k = k;
+    a.scoring = scoring;
+    a.renorm = renorm;
+    a.vector_rows = (E % 4 == 0) && aligned16(logits);
+    a.inds = out_inds;
+    a.weights = out_weights;
+    return gpt::launch_topk(a, stream) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+const char* router_strerror(int code)
+{
+    switch (code) {
+    case ROUTER_OK: return "ok";
+    case ROUTER_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ROUTER_ERR_UNSUPPORTED: return "shape outside the supported limits";
+    case ROUTER_ERR_MISALIGNED: return "x or w is not 16-byte aligned";
+    case ROUTER_ERR_HIP: return "HIP runtime error";
+    case ROUTER_ERR_NO_WORKSPACE: return "workspace allocation failed";
+    default: return "unknown router error";
+    }
+}
+
+}  // extern "C"

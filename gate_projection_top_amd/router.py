@@ -1,0 +1,206 @@
+"""Thin Python binding of librouter (include/router.h).
+
+Argument marshalling only: shapes and dtypes are checked, outputs are
+allocated with torch on the input's device, and the C entry point of the same
+name is called on the current HIP stream.  Every step of the router runs in
+librouter's HIP kernels; there is no CPU or PyTorch fallback.  If the library
+is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librouter.so")
+
+SOFTMAX = 0
+SQRT_SOFTPLUS = 1
+
+OK = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_UNSUPPORTED = 2
+ERR_MISALIGNED = 3
+ERR_HIP = 4
+ERR_NO_WORKSPACE = 5
+
+EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_topk_from_logits",
+           "router_strerror")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class RouterError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librouter.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; build it with `python -m gate_projection_top_amd.build` "
+            "(or __graft_entry__.build()) — there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.router_init.argtypes = [i32]
+    lib.router_init.restype = i32
+    lib.router_fwd.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.router_fwd.restype = i32
+    lib.router_fwd_m2_table.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
+    lib.router_fwd_m2_table.restype = i32
+    lib.router_topk_from_logits.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, P]
+    lib.router_topk_from_logits.restype = i32
+    lib.router_strerror.argtypes = [i32]
+    lib.router_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().router_strerror(int(code)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(rc: int, where: str):
+    if rc != OK:
+        raise RouterError(rc, where)
+
+
+def _check_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def init(device: Optional[int] = None):
+    """Allocate the per-device workspace now (required before graph capture)."""
+    dev = torch.cuda.current_device() if device is None else int(device)
+    _check(load().router_init(dev), "router_init")
+
+
+def _outputs(M: int, k: int, E: int, device, out_inds, out_weights, want_logits, logits_out):
+    inds = out_inds if out_inds is not None else torch.empty((M, k), dtype=torch.int32, device=device)
+    wts = out_weights if out_weights is not None else torch.empty((M, k), dtype=torch.float32, device=device)
+    _check_tensor(inds, "out_inds", torch.int32, 2)
+    _check_tensor(wts, "out_weights", torch.float32, 2)
+    if tuple(inds.shape) != (M, k) or tuple(wts.shape) != (M, k):
+        raise ValueError("out_inds/out_weights must be [M, k]")
+    logits = logits_out
+    if logits is None and want_logits:
+        logits = torch.empty((M, E), dtype=torch.float32, device=device)
+    if logits is not None:
+        _check_tensor(logits, "logits_out", torch.float32, 2)
+        if tuple(logits.shape) != (M, E):
+            raise ValueError("logits_out must be [M, E]")
+    return inds, wts, logits
+
+
+def _check_bias(bias, E):
+    if bias is not None:
+        _check_tensor(bias, "bias", torch.float32, 1)
+        if bias.shape[0] != E:
+            raise ValueError("bias must be [E]")
+
+
+def router_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+               scoring: int = SOFTMAX, renorm: bool = True, *, return_logits: bool = False,
+               out_inds=None, out_weights=None, logits_out=None):
+    """Fused router.  x: bf16 [M,H]; w: bf16 [E,H]; bias: fp32 [E] or None.
+
+    Returns (inds int32 [M,k], weights fp32 [M,k]) or, with return_logits /
+    logits_out, (inds, weights, logits fp32 [M,E]).
+    """
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    _check_tensor(w, "w", torch.bfloat16, 2)
+    M, H = x.shape
+    E = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("x and w disagree on H")
+    _check_bias(bias, E)
+    inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
+    with torch.cuda.device(x.device):
+        rc = load().router_fwd(_ptr(x), _ptr(w), _ptr(bias), M, H, E, int(k), int(scoring),
+                               int(bool(renorm)), _ptr(inds), _ptr(wts), _ptr(logits),
+                               _stream(x.device))
+    _check(rc, "router_fwd")
+    return (inds, wts, logits) if logits is not None else (inds, wts)
+
+
+def router_fwd_m2_table(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                        scoring: int = SOFTMAX, renorm: bool = True, *, return_logits: bool = False,
+                        out=None):
+    """Two-token router plus the unique-route table, one launch.
+
+    Returns a dict with inds, weights, unique_ids, token_mask, slot_to_unique,
+    unique_count (and logits when return_logits).  `out` may supply any of
+    these tensors preallocated.
+    """
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    _check_tensor(w, "w", torch.bfloat16, 2)
+    M, H = x.shape
+    E = w.shape[0]
+    if M != 2:
+        raise ValueError("router_fwd_m2_table needs exactly two tokens")
+    if w.shape[1] != H:
+        raise ValueError("x and w disagree on H")
+    _check_bias(bias, E)
+    out = dict(out or {})
+    inds, wts, logits = _outputs(2, k, E, x.device, out.get("inds"), out.get("weights"),
+                                 return_logits, out.get("logits"))
+    tab = {}
+    for name, n in (("unique_ids", 2 * k), ("token_mask", 2 * k), ("slot_to_unique", 2 * k),
+                    ("unique_count", 1)):
+        t = out.get(name)
+        if t is None:
+            t = torch.empty(n, dtype=torch.int32, device=x.device)
+        _check_tensor(t, name, torch.int32, 1)
+        if t.shape[0] != n:
+            raise ValueError(f"{name} must have {n} entries")
+        tab[name] = t
+    with torch.cuda.device(x.device):
+        rc = load().router_fwd_m2_table(
+            _ptr(x), _ptr(w), _ptr(bias), H, E, int(k), int(scoring), int(bool(renorm)),
+            _ptr(inds), _ptr(wts), _ptr(logits), _ptr(tab["unique_ids"]), _ptr(tab["token_mask"]),
+            _ptr(tab["slot_to_unique"]), _ptr(tab["unique_count"]), _stream(x.device))
+    _check(rc, "router_fwd_m2_table")
+    res = {"inds": inds, "weights": wts, **tab}
+    if logits is not None:
+        res["logits"] = logits
+    return res
+
+
+def router_topk_from_logits(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                            scoring: int = SOFTMAX, renorm: bool = True, *, out_inds=None,
+                            out_weights=None):
+    """Scoring + top-k + weights on fp32 logits [M,E] already on the GPU."""
+    _check_tensor(logits, "logits", torch.float32, 2)
+    M, E = logits.shape
+    _check_bias(bias, E)
+    inds, wts, _ = _outputs(M, k, E, logits.device, out_inds, out_weights, False, None)
+    with torch.cuda.device(logits.device):
+        rc = load().router_topk_from_logits(_ptr(logits), _ptr(bias), M, E, int(k), int(scoring),
+                                            int(bool(renorm)), _ptr(inds), _ptr(wts),
+                                            _stream(logits.device))
+    _check(rc, "router_topk_from_logits")
+    return inds, wts

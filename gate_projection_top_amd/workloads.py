@@ -264,3 +264,32 @@ def adversarial_logits(M: int, seed: int = 0, E: int = 256, k: int = 8,
                 chain.append(np.nextafter(chain[-1], np.float32(-np.inf), dtype=np.float32))
             logits[r, rng.permutation(members)] = np.array(chain, dtype=np.float32)
     return LogitsCase(logits, None, k, SOFTMAX, True, kind, name=f"adv-logits/M{M}/seed{seed}")
+
+
+# --------------------------------------------------------------------------
+# Device-side pools for timing (same distributions, generated on the GPU so
+# that half-gigabyte pools do not take seconds of host time)
+# --------------------------------------------------------------------------
+def torch_gaussian_bf16(shape, std: float, seed: int, device):
+    """bf16 tensor ~ N(0, std^2) drawn on `device` with a seeded torch generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def torch_rms_normalised_bf16(shape, seed: int, device, eps: float = 1e-6):
+    """Unit-RMS rows (last dim) of N(0,1) draws, rounded to bf16, on `device`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    x = x / torch.sqrt((x * x).mean(dim=-1, keepdim=True) + eps)
+    return x.to(torch.bfloat16)
+
+
+def torch_uniform_f32(n: int, lo: float, hi: float, seed: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.rand(n, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo

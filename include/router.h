@@ -1,0 +1,144 @@
+/*
+ * librouter — fused MoE router for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes plain pointers and sizes; device pointers
+ * are owned by the caller and are never freed or retained by the library.
+ * All calls are asynchronous on `stream`: they enqueue HIP kernels and
+ * return without synchronising.  After router_init() on a device no call
+ * allocates memory, so calls may be captured into a HIP graph.
+ *
+ * What is computed (pages on the fused MoE router):
+ *   - qwisp issue #145 "Observation" and "Change": the gate matvec
+ *     postNorm[H] -> gateLogits[E] and the top-8 producing inds/scores, fused
+ *     into one kernel whose E logits stay on chip;
+ *   - qwisp issue #145 "Bit-exactness": the tie order of the selection is
+ *     part of the contract — keys descending, equal keys to the lower expert
+ *     index, results emitted in that order;
+ *   - dense_router_decode commit notes, "DenseRouterDecodeKernel": scoring by
+ *     sqrt(softplus(logit)) with the stable softplus, selection on score plus
+ *     a per-expert bias, unbiased winners' scores renormalised; the BF16 GEMM
+ *     with FP32 accumulation and the row-level top-k epilogue;
+ *   - b70 lab MTP1 M=2 note, "Unique-route router screen": the optional M=2
+ *     unique-route table produced inside the router launch.
+ *
+ * Precise definition (shared by every entry point):
+ *   logit[t,e]  = sum_i x[t,i]*w[e,i], bf16 operands, fp32 accumulation
+ *                 (order of the fp32 sum is the kernel's, fixed per call shape
+ *                 and identical for every expert);
+ *   scores      = softmax over the row (p_e), or s_e = sqrt(max(l,0) +
+ *                 log1p(exp(-|l|))); computed in double from the fp32 logit;
+ *   key[e]      = logit[e] when bias == NULL (both scorings are increasing in
+ *                 the logit, so this is the exact score order);
+ *               = fl32( fl32(score[e]) + bias[e] ) otherwise;
+ *                 -0 and +0 are the same key;
+ *   inds[t,:]   = the first k experts in (key descending, index ascending)
+ *                 order, in that order;
+ *   weights     = renorm: u_j / sum_{winners} u, with u = exp(l - max l)
+ *                 (softmax) or s (sqrt-softplus), sum in rank order, in double,
+ *                 rounded once to fp32;
+ *                 no renorm: the full-row probability p_j (softmax) or s_j;
+ *                 the bias never enters a weight.
+ *
+ * Layouts: row-major, innermost dimension contiguous.
+ *   x        bf16 [M, H]    (16-byte aligned; H % 8 == 0)
+ *   w        bf16 [E, H]    (W_gate, one row per expert; 16-byte aligned)
+ *   bias     fp32 [E]       or NULL
+ *   logits   fp32 [M, E]
+ *   inds     int32 [M, k]
+ *   weights  fp32 [M, k]
+ *
+ * Limits: 1 <= E <= 256, 1 <= k <= min(E, 16), H >= 8, H % 8 == 0, M >= 0
+ * (M == 0 is a no-op).  Inputs must not alias outputs.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued;
+ * on any error nothing is launched and no output byte changes.  The return
+ * value is ROUTER_OK or one of the codes below; router_strerror() names it.
+ *
+ * Concurrency: router_fwd and router_fwd_m2_table use a per-device
+ * workspace (partial sums and arrival counters).  Calls on one device must be
+ * ordered (same stream, or externally synchronised); overlapping calls on
+ * one device race on that workspace.  router_topk_from_logits uses none.
+ */
+#ifndef GATE_PROJECTION_TOP_ROUTER_H
+#define GATE_PROJECTION_TOP_ROUTER_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROUTER_MAX_E 256
+#define ROUTER_MAX_K 16
+/* router_fwd runs the split-H decode kernel up to this many tokens and the
+ * MFMA GEMM-with-epilogue prefill kernel above it. */
+#define ROUTER_DECODE_MAX_M 64
+
+typedef enum {
+    ROUTER_SCORING_SOFTMAX = 0,
+    ROUTER_SCORING_SQRT_SOFTPLUS = 1
+} router_scoring_t;
+
+enum {
+    ROUTER_OK = 0,
+    ROUTER_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad enum, M < 0 */
+    ROUTER_ERR_UNSUPPORTED = 2,      /* shape outside the limits above */
+    ROUTER_ERR_MISALIGNED = 3,       /* x or w not 16-byte aligned */
+    ROUTER_ERR_HIP = 4,              /* a HIP runtime call failed */
+    ROUTER_ERR_NO_WORKSPACE = 5      /* workspace could not be allocated */
+};
+
+/* Allocates the per-device workspace for `device` (or the current device
+ * when device < 0) and zeroes its counters.  Idempotent and thread-safe.
+ * Call it before capturing router_fwd into a graph; router_fwd calls it
+ * itself on first use otherwise.  The workspace lives until process exit. */
+int router_init(int device);
+
+/* Fused router (gate projection + scoring + top-k + renorm in one launch).
+ * Decode (M <= ROUTER_DECODE_MAX_M): experts and H are split across
+ * workgroups; the last workgroup to arrive holds the E logits of each row in
+ * LDS and runs the selection.  Prefill (larger M): one MFMA GEMM whose
+ * epilogue does the selection from LDS.  Logits reach HBM only when
+ * opt_out_logits is non-NULL, and writing them never changes inds/weights.
+ *   x, w, bias, inds, weights, opt_out_logits: device pointers (see layouts);
+ *   scoring: router_scoring_t; renorm: 0 or 1. */
+int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
+               int scoring, int renorm, int32_t* out_inds, float* out_weights,
+               float* opt_out_logits, hipStream_t stream);
+
+/* router_fwd for exactly two tokens that also emits the unique-route table
+ * in the same launch (b70 lab MTP1 note, "Unique-route router screen"):
+ *   out_unique_ids      int32 [2k]: distinct experts in order of first
+ *                       appearance over the slots (token 0 ranks 0..k-1,
+ *                       then token 1); unused tail entries are -1;
+ *   out_token_mask      int32 [2k]: bit t set iff token t selected that
+ *                       unique expert; unused tail entries are 0;
+ *   out_slot_to_unique  int32 [2k]: for slot s = t*k + j, the position of
+ *                       inds[t,j] in out_unique_ids;
+ *   out_unique_count    int32 [1]:  number of distinct experts (k..2k).
+ * inds/weights are bit-identical to router_fwd's on the same inputs. */
+int router_fwd_m2_table(const void* x, const void* w, const float* bias, int H, int E, int k,
+                        int scoring, int renorm, int32_t* out_inds, float* out_weights,
+                        float* opt_out_logits, int32_t* out_unique_ids,
+                        int32_t* out_token_mask, int32_t* out_slot_to_unique,
+                        int32_t* out_unique_count, hipStream_t stream);
+
+/* Scoring, selection and weights on logits already in HBM (the standalone
+ * logits-to-top-k of the unfused pair; dense_router_decode notes, "Current
+ * working path").  One wavefront per row; uses the same device routine as
+ * the fused kernels, so fused and unfused results are bit-identical.
+ *   logits: fp32 [M, E] device pointer (16-byte aligned rows are read as
+ *   vectors when E % 4 == 0, otherwise element by element). */
+int router_topk_from_logits(const float* logits, const float* bias, int64_t M, int E, int k,
+                            int scoring, int renorm, int32_t* out_inds, float* out_weights,
+                            hipStream_t stream);
+
+/* Static, human-readable name of a return code. */
+const char* router_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

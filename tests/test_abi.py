@@ -1,0 +1,110 @@
+"""librouter loads and exports every entry point include/router.h declares,
+and argument validation rejects bad calls before touching the GPU (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gate_projection_top_amd import router as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "router.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//.*", "", text)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(router_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(R.LIB_PATH):
+        from gate_projection_top_amd import build
+        build.build()
+    return R.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(R.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert getattr(lib, name) is not None
+
+
+def test_strerror_names_every_code(lib):
+    for code in range(0, 6):
+        assert R.strerror(code) and "unknown" not in R.strerror(code)
+    assert "unknown" in R.strerror(99)
+
+
+FAKE = ctypes.c_void_p(0x1000)        # never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(0x1008)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scoring=7), R.ERR_INVALID_ARGUMENT),
+    (dict(renorm=2), R.ERR_INVALID_ARGUMENT),
+    (dict(M=-1), R.ERR_INVALID_ARGUMENT),
+    (dict(E=0), R.ERR_INVALID_ARGUMENT),
+    (dict(k=0), R.ERR_INVALID_ARGUMENT),
+    (dict(k=9, E=8), R.ERR_INVALID_ARGUMENT),
+    (dict(E=257), R.ERR_UNSUPPORTED),
+    (dict(k=17), R.ERR_UNSUPPORTED),
+    (dict(H=0), R.ERR_INVALID_ARGUMENT),
+    (dict(H=4100), R.ERR_UNSUPPORTED),
+    (dict(x=None), R.ERR_INVALID_ARGUMENT),
+    (dict(w=None), R.ERR_INVALID_ARGUMENT),
+    (dict(inds=None), R.ERR_INVALID_ARGUMENT),
+    (dict(weights=None), R.ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE_ODD), R.ERR_MISALIGNED),
+    (dict(w=FAKE_ODD), R.ERR_MISALIGNED),
+])
+def test_router_fwd_rejects(lib, kw, code):
+    a = dict(x=FAKE, w=FAKE, bias=None, M=4, H=4096, E=256, k=8, scoring=0, renorm=1,
+             inds=FAKE, weights=FAKE, logits=None)
+    a.update(kw)
+    rc = lib.router_fwd(a["x"], a["w"], a["bias"], a["M"], a["H"], a["E"], a["k"], a["scoring"],
+                        a["renorm"], a["inds"], a["weights"], a["logits"], None)
+    assert rc == code, (kw, rc)
+
+
+def test_router_fwd_empty_batch_is_ok_without_pointers(lib):
+    assert lib.router_fwd(None, None, None, 0, 4096, 256, 8, 0, 1, None, None, None, None) == R.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=17), R.ERR_UNSUPPORTED),
+    (dict(ids=None), R.ERR_INVALID_ARGUMENT),
+    (dict(mask=None), R.ERR_INVALID_ARGUMENT),
+    (dict(s2u=None), R.ERR_INVALID_ARGUMENT),
+    (dict(count=None), R.ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE_ODD), R.ERR_MISALIGNED),
+    (dict(H=12), R.ERR_UNSUPPORTED),
+])
+def test_m2_table_rejects(lib, kw, code):
+    a = dict(x=FAKE, w=FAKE, H=4096, E=256, k=6, ids=FAKE, mask=FAKE, s2u=FAKE, count=FAKE)
+    a.update(kw)
+    rc = lib.router_fwd_m2_table(a["x"], a["w"], None, a["H"], a["E"], a["k"], 1, 1, FAKE, FAKE,
+                                 None, a["ids"], a["mask"], a["s2u"], a["count"], None)
+    assert rc == code, (kw, rc)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), R.ERR_INVALID_ARGUMENT),
+    (dict(E=300), R.ERR_UNSUPPORTED),
+    (dict(k=20), R.ERR_UNSUPPORTED),
+    (dict(M=-5), R.ERR_INVALID_ARGUMENT),
+    (dict(scoring=-1), R.ERR_INVALID_ARGUMENT),
+])
+def test_topk_rejects(lib, kw, code):
+    a = dict(logits=FAKE, M=16, E=256, k=8, scoring=0)
+    a.update(kw)
+    rc = lib.router_topk_from_logits(a["logits"], None, a["M"], a["E"], a["k"], a["scoring"], 1,
+                                     FAKE, FAKE, None)
+    assert rc == code, (kw, rc)

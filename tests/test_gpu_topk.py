@@ -1,0 +1,97 @@
+"""router_topk_from_logits vs the oracle, rule (a): bit-exact indices, weights within 2 ulp.
+
+Workload: fp32 logits ~ N(0, 2) over E=256, k=8, with rows engineered around
+rank 8 (exact ties, one-ulp chains in both index orders, all-equal rows)
+and the variants the API allows (bias, sqrt-softplus, no renorm, small and
+ragged E, unaligned rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.compare import check_topk
+from gate_projection_top_amd import router as R
+from gate_projection_top_amd import workloads as W
+from gpu_util import DEV, f32_dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+@pytest.mark.parametrize("M", [1, 2, 8, 4096])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_adversarial_rows(orc, M, seed):
+    case = W.adversarial_logits(M, seed=seed)
+    say(f"topk adversarial M={M} seed={seed}")
+    gi, gw = R.router_topk_from_logits(f32_dev(case.logits), None, 8, W.SOFTMAX, True)
+    torch.cuda.synchronize()
+    ri, rw = orc.topk_from_logits(case.logits, None, 8, W.SOFTMAX, True)
+    check_topk(host(gi), host(gw), ri, rw, what=case.name)
+
+
+@pytest.mark.parametrize("scoring", [W.SOFTMAX, W.SQRT_SOFTPLUS])
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_scoring_variants(orc, scoring, renorm, with_bias):
+    case = W.adversarial_logits(512, seed=7)
+    rng = np.random.default_rng(3)
+    bias = rng.uniform(-0.05, 0.05, 256).astype(np.float32) if with_bias else None
+    say(f"topk variant scoring={scoring} renorm={renorm} bias={with_bias}")
+    gi, gw = R.router_topk_from_logits(f32_dev(case.logits), f32_dev(bias), 8, scoring, renorm)
+    torch.cuda.synchronize()
+    ri, rw = orc.topk_from_logits(case.logits, bias, 8, scoring, renorm)
+    check_topk(host(gi), host(gw), ri, rw, what=f"variant s{scoring} r{renorm} b{with_bias}")
+
+
+@pytest.mark.parametrize("E,k", [(16, 2), (16, 16), (100, 7), (255, 16), (256, 1), (256, 16),
+                                 (1, 1), (3, 2), (64, 8)])
+def test_shapes(orc, E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    logits = (rng.standard_normal((77, E)) * 1.4).astype(np.float32)
+    logits[::5, :] = np.float32(0.3)                          # all-equal rows
+    logits[1::7, : E // 2] = np.float32(1.0)                  # big tie block
+    logits[2::9] = np.where(rng.random((logits[2::9].shape)) < 0.5, np.float32(-0.0), np.float32(0.0))
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    for b in (None, bias):
+        say(f"topk shape E={E} k={k} bias={b is not None}")
+        gi, gw = R.router_topk_from_logits(f32_dev(logits), f32_dev(b), k, W.SQRT_SOFTPLUS, True)
+        torch.cuda.synchronize()
+        ri, rw = orc.topk_from_logits(logits, b, k, W.SQRT_SOFTPLUS, True)
+        check_topk(host(gi), host(gw), ri, rw, what=f"E{E}k{k}")
+
+
+def test_unaligned_rows_take_scalar_path(orc):
+    """Rows that start off a 16-byte boundary are read element by element."""
+    case = W.adversarial_logits(33, seed=5)
+    buf = torch.zeros(33 * 256 + 1, dtype=torch.float32, device=DEV)
+    buf[1:] = f32_dev(case.logits).reshape(-1)
+    view = buf[1:].view(33, 256)
+    assert view.data_ptr() % 16 != 0
+    say("topk unaligned")
+    gi, gw = R.router_topk_from_logits(view, None, 8, W.SOFTMAX, True)
+    torch.cuda.synchronize()
+    ri, rw = orc.topk_from_logits(case.logits, None, 8, W.SOFTMAX, True)
+    check_topk(host(gi), host(gw), ri, rw, what="unaligned")
+
+
+def test_empty_is_noop():
+    logits = torch.empty((0, 256), dtype=torch.float32, device=DEV)
+    gi, gw = R.router_topk_from_logits(logits, None, 8)
+    assert gi.shape == (0, 8) and gw.shape == (0, 8)
+
+
+def test_permutation_and_no_duplicates():
+    """Every row's indices are distinct experts in range (the selection-sort swap lesson)."""
+    rng = np.random.default_rng(9)
+    logits = rng.choice(np.array([0.0, 1.0, 2.0], np.float32), size=(1000, 256))
+    gi, _ = R.router_topk_from_logits(f32_dev(logits), None, 16)
+    torch.cuda.synchronize()
+    gi = host(gi)
+    assert gi.min() >= 0 and gi.max() < 256
+    for r in range(gi.shape[0]):
+        assert len(set(gi[r].tolist())) == 16
