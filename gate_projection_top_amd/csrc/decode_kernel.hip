@@ -11,10 +11,10 @@
 //   grid = R row blocks x B expert blocks x S H-splits, 4 waves each.
 //   Phase 1 (every workgroup): the 16x16 (tokens x experts) partial dot
 //     products over its H-split, one bf16 MFMA 16x16x32 per 32-wide k-step,
-//     the four waves' partials summed in LDS in a fixed order, stored to the
-//     workspace; then a release fence and an agent-scope arrival count per
-//     row block.
-//   Phase 2 (the last workgroup of a row block): acquire, sum the S partials
+//     the four waves' partials summed in LDS in a fixed order and published
+//     with device-coherent stores; then an agent-scope arrival count per row
+//     block.
+//   Phase 2 (the last workgroup of a row block): sum the S partials
 //     of each logit in split order into an LDS row tile (the only place the
 //     logits live unless the caller asks for them), route each row with the
 //     shared route_row(), and at M=2 emit the unique-route table.  It resets
@@ -33,6 +33,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kChunk = 4;  // k-steps loaded per wave before its MFMAs
+constexpr int kItemsPerThread = 4;  // logits gathered per thread per batch in phase 2
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -89,41 +90,72 @@ __global__ __launch_bounds__(kThreads) void decode_router_kernel(DecodeLaunch a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][lane & 15] = acc[i];
     __syncthreads();
-    {
-        const int rr = tid >> 4, cc = tid & 15;
-        const float sum = ((red[0][rr][cc] + red[1][rr][cc]) + red[2][rr][cc]) + red[3][rr][cc];
-        const int row = r * kDecodeTile + rr;
-        const int e = b * kDecodeTile + cc;
-        if (row < a.M && e < a.E) a.partials[((int64_t)s * a.M + row) * a.E + e] = sum;
-    }
 
-    // ---- hand-off: the last workgroup of this row block continues
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t arrivals = (uint32_t)(B * a.S);
-        const uint32_t prev = __hip_atomic_fetch_add(&a.counters[r], 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (prev == arrivals - 1u);
+    // ---- hand-off.  Wave 0 alone publishes the workgroup's 16x16 partials
+    // with device-coherent (agent-scope) stores, waits until they have
+    // completed, then takes a ticket on the row block's arrival counter.  The
+    // workgroup that draws the last ticket reads every partial back with
+    // device-coherent loads.  No cache-wide writeback or invalidate is needed
+    // because the published data never sits in a non-coherent cache line.
+    if (wave == 0) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int idx = h * kWave + lane;
+            const int rr = idx >> 4, cc = idx & 15;
+            const float sum = ((red[0][rr][cc] + red[1][rr][cc]) + red[2][rr][cc]) + red[3][rr][cc];
+            const int row = r * kDecodeTile + rr;
+            const int e = b * kDecodeTile + cc;
+            if (row < a.M && e < a.E)
+                __hip_atomic_store(&a.partials[((int64_t)s * a.M + row) * a.E + e], sum,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // every partial store has completed
+        if (lane == 0) {
+            const uint32_t arrivals = (uint32_t)(B * a.S);
+            const uint32_t prev = __hip_atomic_fetch_add(&a.counters[r], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            is_last = (prev == arrivals - 1u);
+        }
     }
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
     if (tid == 0) __hip_atomic_store(&a.counters[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- phase 2: full logits of the row block into LDS, then route rows
+    // All of a thread's partial loads are issued before any is consumed (one
+    // memory round trip per batch instead of one per split); the sum itself
+    // runs in split order.
     const int t0 = r * kDecodeTile;
     const int nrows = min(kDecodeTile, a.M - t0);
     const int items = nrows * a.E;
     const int64_t split_stride = (int64_t)a.M * a.E;
-    for (int it = tid; it < items; it += kThreads) {
-        const int t = it / a.E;
-        const int e = it - t * a.E;
-        const float* p = a.partials + (int64_t)(t0 + t) * a.E + e;
-        float sum = p[0];
-        for (int q = 1; q < a.S; ++q) sum += p[q * split_stride];
-        lrow[t][e] = sum;
-        if (a.logits_out) a.logits_out[(int64_t)(t0 + t) * a.E + e] = sum;
+    const float* pbase = a.partials + (int64_t)t0 * a.E;
+    for (int base = tid; base < items; base += kThreads * kItemsPerThread) {
+        float part[kItemsPerThread][kDecodeMaxSplits];
+#pragma unroll
+        for (int u = 0; u < kItemsPerThread; ++u) {
+            const int it = base + u * kThreads;
+#pragma unroll
+            for (int q = 0; q < kDecodeMaxSplits; ++q)
+                part[u][q] = (it < items && q < a.S)
+                                 ? __hip_atomic_load(pbase + q * split_stride + it, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kItemsPerThread; ++u) {
+            const int it = base + u * kThreads;
+            if (it < items) {
+                float sum = part[u][0];
+#pragma unroll
+                for (int q = 1; q < kDecodeMaxSplits; ++q)
+                    if (q < a.S) sum += part[u][q];
+                const int t = it / a.E;
+                const int e = it - t * a.E;
+                lrow[t][e] = sum;
+                if (a.logits_out) a.logits_out[(int64_t)(t0 + t) * a.E + e] = sum;
+            }
+        }
     }
     __syncthreads();
 

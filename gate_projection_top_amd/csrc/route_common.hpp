@@ -31,9 +31,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // cross-lane primitives (full wavefront active)
 // ---------------------------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
-// row_ror:4 = 0x124, row_ror:8 = 0x128.  After these four steps every lane
-// holds the reduction over its 16-lane row; the four rows are then combined
-// through scalar registers in a fixed order.
+// row_ror:4 = 0x124, row_ror:8 = 0x128 (after these four steps every lane
+// holds the reduction over its 16-lane row), row_bcast:15 = 0x142 and
+// row_bcast:31 = 0x143 (carry a row's result into the rows above it).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
@@ -62,15 +62,19 @@ __device__ __forceinline__ double dpp_f64(double v)
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// Wave-wide max: butterfly inside each 16-lane row, then DPP row_bcast:15
+// (rows 1 and 3 take lane 15 of the row below) and row_bcast:31 (rows 2 and 3
+// take lane 31), which leaves the maximum of all 64 lanes in lane 63; one
+// readlane makes it wave-uniform.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     v = max(v, dpp_u32<0xB1>(v));
     v = max(v, dpp_u32<0x4E>(v));
     v = max(v, dpp_u32<0x124>(v));
     v = max(v, dpp_u32<0x128>(v));
-    const uint32_t a = readlane_u32(v, 0), b = readlane_u32(v, 16);
-    const uint32_t c = readlane_u32(v, 32), d = readlane_u32(v, 48);
-    return max(max(a, b), max(c, d));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+    return readlane_u32(v, 63);
 }
 
 __device__ __forceinline__ float wave_max_f32(float f)
@@ -80,9 +84,11 @@ __device__ __forceinline__ float wave_max_f32(float f)
     v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x4E>(v))));
     v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x124>(v))));
     v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x128>(v))));
-    const float a = __uint_as_float(readlane_u32(v, 0)), b = __uint_as_float(readlane_u32(v, 16));
-    const float c = __uint_as_float(readlane_u32(v, 32)), d = __uint_as_float(readlane_u32(v, 48));
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
+                                                      (int)v, (int)v, 0x142, 0xA, 0xF, false))));
+    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
+                                                      (int)v, (int)v, 0x143, 0xC, 0xF, false))));
+    return __uint_as_float(readlane_u32(v, 63));
 }
 
 // Sum over the wavefront in a fixed association: the 16-lane row sums are
@@ -112,6 +118,12 @@ __device__ __forceinline__ uint32_t order_code(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_code (a folded -0 comes back as +0).
+__device__ __forceinline__ float order_value(uint32_t c)
+{
+    return __uint_as_float((c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c);
+}
+
 // sqrt(softplus(l)) with the stable softplus max(l,0) + log1p(exp(-|l|))
 // (dense_router_decode notes, "Numerically stable softplus"), in double.
 __device__ __forceinline__ double sqrt_softplus(float l)
@@ -133,6 +145,19 @@ struct RowResult {
     float w;    // lane j < k: its weight
 };
 
+// Compare-exchange of two (code, slot) entries so that the first one is the
+// earlier in selection order: larger code, or equal code and lower slot.
+__device__ __forceinline__ void order_pair(uint32_t& ca, int& ia, uint32_t& cb, int& ib)
+{
+    const bool swap = cb > ca || (cb == ca && ib < ia);
+    const uint32_t c = swap ? cb : ca;
+    const int i = swap ? ib : ia;
+    cb = swap ? ca : cb;
+    ib = swap ? ia : ib;
+    ca = c;
+    ia = i;
+}
+
 // Route one row.  v[j]: logit of expert 4*lane+j (ignored when >= E);
 // bv[j]: its selection bias (used only when s.has_bias).
 __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
@@ -144,21 +169,20 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
     for (int j = 0; j < kPerLane; ++j) valid[j] = (lane * kPerLane + j) < s.E;
 
     const bool softmax = s.scoring == kSoftmax;
-    float mx = -__builtin_inff();
-    if (softmax) {
-#pragma unroll
-        for (int j = 0; j < kPerLane; ++j)
-            if (valid[j]) mx = fmaxf(mx, v[j]);
-        mx = wave_max_f32(mx);
-    }
-
     // Scores for every expert are needed only when they form the key or when
     // a softmax weight is the full-row probability.
     const bool need_all = s.has_bias || (softmax && !s.renorm);
+
+    float mx = 0.0f;  // softmax shift: the row's largest logit
     double Z = 1.0;
     double sc[kPerLane] = {0.0, 0.0, 0.0, 0.0};
     if (need_all) {
         if (softmax) {
+            float m = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j)
+                if (valid[j]) m = fmaxf(m, v[j]);
+            mx = wave_max_f32(m);
             double z[kPerLane];
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
@@ -172,7 +196,9 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
         }
     }
 
-    uint32_t code[kPerLane];
+    // Selection codes, then each lane's four entries in selection order.
+    uint32_t c[kPerLane];
+    int slot[kPerLane];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
         float key = v[j];
@@ -180,36 +206,53 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
             const float s32 = (float)sc[j];
             key = s32 + bv[j];
         }
-        code[j] = valid[j] ? order_code(key) : 0u;
+        c[j] = valid[j] ? order_code(key) : 0u;
+        slot[j] = j;
+    }
+    order_pair(c[0], slot[0], c[1], slot[1]);
+    order_pair(c[2], slot[2], c[3], slot[3]);
+    order_pair(c[0], slot[0], c[2], slot[2]);
+    order_pair(c[1], slot[1], c[3], slot[3]);
+    order_pair(c[1], slot[1], c[2], slot[2]);
+
+    // k rounds: the wave-wide largest head wins; among equal heads the lowest
+    // lane, whose head is its lowest-slot entry of that code, i.e. the lowest
+    // expert index.  The winning lane pops its head.
+    int my_idx = 0;
+    uint32_t my_code = 0u;
+    for (int it = 0; it < s.k; ++it) {
+        const uint32_t top = wave_max_u32(c[0]);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(c[0] == top);
+        const int L = (int)__builtin_ctzll(hit);
+        const int wslot = __builtin_amdgcn_readlane(slot[0], L);
+        if (lane == it) {
+            my_idx = L * kPerLane + wslot;
+            my_code = top;
+        }
+        const bool pop = lane == L;
+        c[0] = pop ? c[1] : c[0];
+        slot[0] = pop ? slot[1] : slot[0];
+        c[1] = pop ? c[2] : c[1];
+        slot[1] = pop ? slot[2] : slot[1];
+        c[2] = pop ? c[3] : c[2];
+        slot[2] = pop ? slot[3] : slot[2];
+        c[3] = pop ? 0u : c[3];
     }
 
-    // k rounds of wave arg-max.  The winner is the largest code; among equal
-    // codes the lowest lane, and inside a lane the lowest slot (strict >
-    // below), i.e. the lowest expert index.
-    int my_idx = 0;
-    float my_logit = 0.0f;
-    for (int it = 0; it < s.k; ++it) {
-        uint32_t best = code[0];
-        int bj = 0;
-        float bl = v[0];
-#pragma unroll
-        for (int j = 1; j < kPerLane; ++j) {
-            const bool gt = code[j] > best;
-            best = gt ? code[j] : best;
-            bj = gt ? j : bj;
-            bl = gt ? v[j] : bl;
-        }
-        const uint32_t top = wave_max_u32(best);
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(best == top);
-        const int L = (int)__builtin_ctzll(hit);
-        const int wj = __builtin_amdgcn_readlane(bj, L);
-        const float wl = __uint_as_float(readlane_u32(__float_as_uint(bl), L));
-#pragma unroll
-        for (int j = 0; j < kPerLane; ++j) code[j] = (lane == L && j == wj) ? 0u : code[j];
-        if (lane == it) {
-            my_idx = L * kPerLane + wj;
-            my_logit = wl;
-        }
+    // Winner logits: the key itself without a bias; otherwise fetched from the
+    // lane that holds the expert.
+    float my_logit;
+    if (!s.has_bias) {
+        my_logit = order_value(my_code);
+        if (softmax && !need_all) mx = order_value(readlane_u32(my_code, 0));  // rank 0 holds the max
+    } else {
+        const int src = (my_idx >> 2) << 2;  // byte address of the owning lane
+        const float f0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[0])));
+        const float f1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[1])));
+        const float f2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[2])));
+        const float f3 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[3])));
+        const int j = my_idx & 3;
+        my_logit = j == 0 ? f0 : (j == 1 ? f1 : (j == 2 ? f2 : f3));
     }
 
     // Weights from the unbiased scores; the bias never enters here.
