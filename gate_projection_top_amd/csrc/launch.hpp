@@ -44,16 +44,28 @@ struct PrefillLaunch {
     int32_t* inds;
     float* weights;
     float* logits_out;      // optional
+    float* partials;        // workspace [tile][S][128][256] (S > 1 only)
+    uint32_t* counters;     // workspace [tile][kPrefillCountersPerTile], zero between calls
+    int S;                  // K splits per 128-row tile
+    int k_per_split;        // H elements per split (multiple of 64)
+    uint32_t spin_ticks;    // bounded wait for sibling splits (100 MHz realtime ticks)
 };
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+int prefill_splits(int64_t M);
 
 // Decode geometry shared by the host (workspace sizing) and the launcher.
 constexpr int kDecodeTile = 16;        // rows per row block, experts per expert block
 constexpr int kDecodeMaxSplits = 16;   // H splits
 constexpr int kDecodeMaxM = 64;
 constexpr int kDecodeMaxRowBlocks = kDecodeMaxM / kDecodeTile;
+
+// Prefill geometry: 128-row tiles; K split S ways while tiles * S <= 256.
+constexpr int kPrefillTileRows = 128;
+constexpr int kPrefillMaxPairs = 256;          // (tile, split) pairs with published partials
+constexpr int kPrefillCountersPerTile = 8;     // arrive, done, abandoned[4], pad
+constexpr int kPrefillMaxSplitTiles = kPrefillMaxPairs / 2;
 
 }  // namespace gpt

@@ -3,6 +3,7 @@
 // the router happens here; every step runs in the HIP kernels.
 #include "router.h"
 
+#include <atomic>
 #include <mutex>
 
 #include "launch.hpp"
@@ -10,16 +11,22 @@
 namespace {
 
 struct DeviceWorkspace {
-    float* partials = nullptr;     // decode H-split partial logits [S][M][E]
-    uint32_t* counters = nullptr;  // decode arrival counters, one per row block
+    float* partials = nullptr;          // decode H-split partial logits [S][M][E]
+    uint32_t* counters = nullptr;       // decode arrival counters, one per row block
+    float* pf_partials = nullptr;       // prefill split partials [tile][S][128][256]
+    uint32_t* pf_counters = nullptr;    // prefill per-tile counters
 };
 
 constexpr int kMaxDevices = 64;
 constexpr size_t kPartialFloats =
     (size_t)gpt::kDecodeMaxSplits * gpt::kDecodeMaxM * ROUTER_MAX_E;  // 1 MiB
 constexpr int kCounters = 64;
+constexpr size_t kPfPartialFloats =
+    (size_t)gpt::kPrefillMaxPairs * gpt::kPrefillTileRows * ROUTER_MAX_E;  // 32 MiB
+constexpr size_t kPfCounters = (size_t)gpt::kPrefillMaxSplitTiles * gpt::kPrefillCountersPerTile;
 
 DeviceWorkspace g_ws[kMaxDevices];
+std::atomic<uint32_t> g_spin_ticks{20000};  // 200 us at the 100 MHz realtime clock
 std::mutex g_ws_mutex;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -34,22 +41,25 @@ int init_device(int dev)
     if (hipGetDevice(&prev) != hipSuccess) return ROUTER_ERR_HIP;
     if (prev != dev && hipSetDevice(dev) != hipSuccess) return ROUTER_ERR_HIP;
 
-    float* partials = nullptr;
-    uint32_t* counters = nullptr;
-    hipError_t e = hipMalloc((void**)&partials, kPartialFloats * sizeof(float));
-    if (e == hipSuccess) e = hipMalloc((void**)&counters, kCounters * sizeof(uint32_t));
-    if (e == hipSuccess) e = hipMemset(counters, 0, kCounters * sizeof(uint32_t));
+    DeviceWorkspace ws;
+    hipError_t e = hipMalloc((void**)&ws.partials, kPartialFloats * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&ws.counters, kCounters * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_partials, kPfPartialFloats * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_counters, kPfCounters * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ws.counters, 0, kCounters * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ws.pf_counters, 0, kPfCounters * sizeof(uint32_t));
     // The counters must read zero before any stream (blocking or not) runs a
-    // decode kernel; init is rare, so a device-wide wait is acceptable here.
+    // kernel; init is rare, so a device-wide wait is acceptable here.
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (prev != dev) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
-        if (partials) (void)hipFree(partials);
-        if (counters) (void)hipFree(counters);
+        if (ws.partials) (void)hipFree(ws.partials);
+        if (ws.counters) (void)hipFree(ws.counters);
+        if (ws.pf_partials) (void)hipFree(ws.pf_partials);
+        if (ws.pf_counters) (void)hipFree(ws.pf_counters);
         return ROUTER_ERR_NO_WORKSPACE;
     }
-    g_ws[dev].partials = partials;
-    g_ws[dev].counters = counters;
+    g_ws[dev] = ws;
     return ROUTER_OK;
 }
 
@@ -110,10 +120,10 @@ int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H,
               hipStream_t stream)
 {
     hipError_t e;
+    DeviceWorkspace ws;
+    const int rc = current_workspace(&ws);
+    if (rc != ROUTER_OK) return rc;
     if (M <= ROUTER_DECODE_MAX_M) {
-        DeviceWorkspace ws;
-        const int rc = current_workspace(&ws);
-        if (rc != ROUTER_OK) return rc;
         gpt::DecodeLaunch a{};
         a.x = static_cast<const uint16_t*>(x);
         a.w = static_cast<const uint16_t*>(w);
@@ -149,6 +159,12 @@ int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H,
         a.inds = inds;
         a.weights = weights;
         a.logits_out = logits;
+        a.partials = ws.pf_partials;
+        a.counters = ws.pf_counters;
+        a.S = gpt::prefill_splits(M);
+        const int k_steps = (H + 63) / 64;
+        a.k_per_split = ((k_steps + a.S - 1) / a.S) * 64;
+        a.spin_ticks = g_spin_ticks.load(std::memory_order_relaxed);
         e = gpt::launch_prefill(a, stream);
     }
     return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
@@ -178,6 +194,8 @@ int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H
     if (rc != ROUTER_OK) return rc;
     if (!out_inds || !out_weights) return ROUTER_ERR_INVALID_ARGUMENT;
     if (M > 0x7fffffffLL / 256) return ROUTER_ERR_UNSUPPORTED;
+    // 32-bit byte offsets inside one 128-row tile of X and inside W
+    if ((int64_t)H * 2 * 256 > 0x7fff0000LL) return ROUTER_ERR_UNSUPPORTED;
     return run_fused(x, w, bias, M, H, E, k, scoring, renorm, out_inds, out_weights,
                      opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
 }
@@ -220,6 +238,14 @@ int router_topk_from_logits(const float* logits, const float* bias, int64_t M, i
     a.inds = out_inds;
     a.weights = out_weights;
     return gpt::launch_topk(a, stream) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+int router_set_exchange_timeout_us(int microseconds)
+{
+    if (microseconds < 0) return ROUTER_ERR_INVALID_ARGUMENT;
+    const uint64_t ticks = (uint64_t)microseconds * 100u;
+    g_spin_ticks.store(ticks > 0xffffffffu ? 0xffffffffu : (uint32_t)ticks, std::memory_order_relaxed);
+    return ROUTER_OK;
 }
 
 const char* router_strerror(int code)

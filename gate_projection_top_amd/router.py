@@ -27,7 +27,7 @@ ERR_HIP = 4
 ERR_NO_WORKSPACE = 5
 
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_topk_from_logits",
-           "router_strerror")
+           "router_set_exchange_timeout_us", "router_strerror")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -57,6 +57,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_fwd_m2_table.restype = i32
     lib.router_topk_from_logits.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, P]
     lib.router_topk_from_logits.restype = i32
+    lib.router_set_exchange_timeout_us.argtypes = [i32]
+    lib.router_set_exchange_timeout_us.restype = i32
     lib.router_strerror.argtypes = [i32]
     lib.router_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -97,6 +99,11 @@ def init(device: Optional[int] = None):
     """Allocate the per-device workspace now (required before graph capture)."""
     dev = torch.cuda.current_device() if device is None else int(device)
     _check(load().router_init(dev), "router_init")
+
+
+def set_exchange_timeout_us(microseconds: int):
+    """Bounded wait of a prefill K split for its siblings (0 forces the hand-over path)."""
+    _check(load().router_set_exchange_timeout_us(int(microseconds)), "router_set_exchange_timeout_us")
 
 
 def _outputs(M: int, k: int, E: int, device, out_inds, out_weights, want_logits, logits_out):

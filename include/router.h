@@ -134,6 +134,15 @@ int router_topk_from_logits(const float* logits, const float* bias, int64_t M, i
                             int scoring, int renorm, int32_t* out_inds, float* out_weights,
                             hipStream_t stream);
 
+/* Bounded wait, in microseconds, that a prefill K-split workgroup spends
+ * waiting for its sibling splits before it hands its rows to whichever split
+ * finishes last (default 200).  Results do not depend on it: both paths sum
+ * the same partials in the same order.  0 makes every split that is not the
+ * last to arrive hand over at once (used by the tests to exercise that path).
+ * Process-wide; applies to calls enqueued after it returns.  Negative values
+ * are rejected with ROUTER_ERR_INVALID_ARGUMENT. */
+int router_set_exchange_timeout_us(int microseconds);
+
 /* Static, human-readable name of a return code. */
 const char* router_strerror(int code);
 

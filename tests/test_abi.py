@@ -74,6 +74,11 @@ def test_router_fwd_rejects(lib, kw, code):
     assert rc == code, (kw, rc)
 
 
+def test_exchange_timeout_validation(lib):
+    assert lib.router_set_exchange_timeout_us(-1) == R.ERR_INVALID_ARGUMENT
+    assert lib.router_set_exchange_timeout_us(200) == R.OK
+
+
 def test_router_fwd_empty_batch_is_ok_without_pointers(lib):
     assert lib.router_fwd(None, None, None, 0, 4096, 256, 8, 0, 1, None, None, None, None) == R.OK
 

@@ -101,7 +101,7 @@ def test_m2_table_extremes(orc):
                           ("unique_ids", "token_mask", "slot_to_unique", "unique_count")})
 
 
-@pytest.mark.parametrize("M", [65, 100, 333])
+@pytest.mark.parametrize("M", [65, 100, 333, 1000])
 @pytest.mark.parametrize("scoring,with_bias", [(W.SOFTMAX, True), (W.SOFTMAX, False),
                                                (W.SQRT_SOFTPLUS, True)])
 def test_prefill_ragged(orc, M, scoring, with_bias):
@@ -112,6 +112,34 @@ def test_prefill_ragged(orc, M, scoring, with_bias):
     say(f"router prefill M={M} scoring={scoring} bias={with_bias}")
     gi, gw, gl = run_fwd(case)
     check_router(orc, case, gi, gw, gl)
+
+
+@pytest.mark.parametrize("M,H", [(10000, 256), (20000, 128)])
+def test_prefill_two_and_one_splits(orc, M, H):
+    """10000 rows = 79 tiles (two K splits); 20000 rows = 157 tiles (no split)."""
+    case = W.prefill_case(M=M, H=H, seed=M)
+    say(f"router prefill M={M} H={H}")
+    gi, gw, gl = run_fwd(case)
+    check_router(orc, case, gi, gw, gl)
+
+
+@pytest.mark.parametrize("M", [200, 8192])
+def test_prefill_handover_path_matches(orc, M):
+    """Zero exchange wait: every split but the last hands its rows over; results unchanged."""
+    case = W.prefill_case(M=M, H=1024 if M < 8192 else 7168, seed=77)
+    x, w, b = bf16_dev(case.x), bf16_dev(case.w), f32_dev(case.bias)
+    say(f"prefill hand-over M={M}")
+    ref = R.router_fwd(x, w, b, case.k, case.scoring, case.renorm, return_logits=True)
+    try:
+        R.set_exchange_timeout_us(0)
+        got = R.router_fwd(x, w, b, case.k, case.scoring, case.renorm, return_logits=True)
+        torch.cuda.synchronize()
+    finally:
+        R.set_exchange_timeout_us(200)
+    for a, g in zip(ref, got):
+        assert torch.equal(a.view(torch.int32), g.view(torch.int32))
+    if M < 8192:
+        check_router(orc, case, host(got[0]), host(got[1]), host(got[2]))
 
 
 @pytest.mark.slow
