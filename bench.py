@@ -5,23 +5,28 @@ Headline (the latency point of the router's own metric): router_fwd at
 M=1 token, H=7168, E=256, k=8, softmax, no bias, renorm.  One step = one
 token through 40 MoE layers = 40 router calls, each with its own gate matrix
 and activation.  Gate matrices rotate through a 160-matrix pool (587 MB, more
-than twice the 256 MB Infinity Cache) so that W_gate comes from HBM; the 40
-calls of a step are captured in a HIP graph and replayed.  `value` is
-microseconds per router call (lower is better).
+than twice the 256 MB Infinity Cache) so that W_gate comes from HBM.  The 40
+calls of a step are captured in a HIP graph and replayed; `value` is
+microseconds per router call (lower is better), from the wall clock around the
+timed replays.
 
 Also reported (same JSON line):
   roofline      the decode kernel: algorithmic bytes per launch over its mean
-                duration from per-launch HIP events on its stream, vs 8 TB/s;
+                duration (a HIP event pair on the launching stream around the
+                timed replays, divided by the launch count), vs 8 TB/s; traffic
+                from the committed rocprofv3 counter summary when the kernel
+                sources still match it, else null;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   extras        cache-hot cycle, verify widths M=2/8 at H=4096, the biased M=2
                 table on/off delta, the standalone top-k at M=4096, and the
-                8192-token prefill (tokens/s and fraction of bf16 MFMA peak).
+                8192-token prefill (tokens/s, fraction of bf16 MFMA and HBM peak).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,10 +35,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 LAYERS = 40
 POOL = 160
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_M1_H7168_traffic.txt")
+KERNEL_SOURCES = ["route_common.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
 
 
 def log(msg):
@@ -45,22 +52,82 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--section", choices=["all", "decode", "prefill", "topk"], default="all",
+                    help="restrict to one workload (for counter-collection runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
 
-def event_times_ms(torch, fn, n, stream):
-    """Per-launch durations (ms) from an event pair recorded around each launch on `stream`."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    for i in range(n):
-        starts[i].record(stream)
-        fn(i)
-        ends[i].record(stream)
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gate_projection_top_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """Bytes per decode launch from the committed counter summary, if it still applies."""
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_sources_sha256_16") != kernel_source_digest():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class GraphTimer:
+    """A HIP graph of calls (replayed for the wall-clock `value`)."""
+
+    def __init__(self, torch, calls):
+        for c in calls:  # eager warm-up (allocates nothing inside capture)
+            c()
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for c in calls:
+                c()
+
+    def replay(self):
+        self.graph.replay()
+
+
+def timed_replays(torch, graphs, steps, warmup):
+    """Time `steps` replays (round-robin over graphs) after warm-up.
+
+    Returns (wall seconds, event milliseconds): the wall clock around the
+    replay loop, and a HIP event pair recorded on the replaying stream at its
+    two ends (GPU time of the back-to-back launches, host launch latency
+    excluded).
+    """
+    for s in range(warmup):
+        graphs[s % len(graphs)].replay()
     torch.cuda.synchronize()
-    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        graphs[s % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, start.elapsed_time(end)
+
+
+def graph_call_us(torch, calls, steps, warmup):
+    """Mean GPU microseconds per call: `calls` captured once, replayed `steps` times."""
+    g = GraphTimer(torch, calls)
+    _, ms = timed_replays(torch, [g], steps, warmup)
+    return ms * 1e3 / (steps * len(calls))
 
 
 def main():
@@ -79,83 +146,25 @@ def main():
     torch.cuda.set_device(dev)
     R.load()
     R.init(0)
-    stream = torch.cuda.current_stream(dev)
 
-    # ------------------------------------------------------------------ headline
-    H, E, k = 7168, 256, 8
-    log(f"generating pools: W {POOL}x{E}x{H} bf16, X {LAYERS}x1x{H}")
-    wpool = W.torch_gaussian_bf16((POOL, E, H), 1.0 / H ** 0.5, seed=1, device=dev)
-    xpool = W.torch_rms_normalised_bf16((LAYERS, 1, H), seed=2, device=dev)
-    inds = torch.empty((LAYERS, 1, k), dtype=torch.int32, device=dev)
-    wts = torch.empty((LAYERS, 1, k), dtype=torch.float32, device=dev)
-
-    def call(layer, widx):
-        R.router_fwd(xpool[layer], wpool[widx], None, k, W.SOFTMAX, True,
-                     out_inds=inds[layer], out_weights=wts[layer])
-
-    groups = POOL // LAYERS
-    for g in range(groups):              # eager warm-up (also initialises everything)
-        for l in range(LAYERS):
-            call(l, g * LAYERS + l)
-    torch.cuda.synchronize()
-
-    graphs = []
-    for g in range(groups):
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for l in range(LAYERS):
-                call(l, g * LAYERS + l)
-        graphs.append(gr)
-    torch.cuda.synchronize()
-
-    for s in range(args.warmup):
-        graphs[s % groups].replay()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps x {LAYERS} calls (cold W pool, graph replay)")
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        graphs[s % groups].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    us_per_call = ms_per_step * 1e3 / LAYERS
-
-    # per-launch kernel durations with HIP events (eager, same stream, cold pool)
-    n_ev = args.steps * LAYERS
-    ev = event_times_ms(torch, lambda i: call(i % LAYERS, i % POOL), n_ev, stream)
-    kern_us = 1e3 * sum(ev) / len(ev)
-    bytes_per_launch = E * H * 2 + H * 2 + k * 8  # W + x + (inds, weights)
-    achieved_gbs = bytes_per_launch / (kern_us * 1e-6) / 1e9
-
-    extras = {"decode_M1_H7168_event_us_per_launch": round(kern_us, 3)}
-
-    # cache-hot cycle: the same 40 gate matrices every step (MALL-resident)
-    for _ in range(args.warmup):
-        graphs[0].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graphs[0].replay()
-    torch.cuda.synchronize()
-    extras["decode_M1_H7168_hot_us_per_call"] = round((time.perf_counter() - t0) * 1e6 / (args.steps * LAYERS), 3)
-    del graphs
-
-    if not args.no_extras:
-        extras.update(run_extras(torch, R, W, dev, stream, args))
-
-    # ------------------------------------------------------------- CPU baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(W, args.cpu_seconds)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration_mib} MiB device-to-device copy")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": "router µs/call at M=1,H=7168,E=256,k=8; tokens/s at M=8192; % HBM/MFMA peak",
-        "value": round(us_per_call, 3),
+        "value": None,
         "unit": "µs/call",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": None,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -165,56 +174,86 @@ def main():
             "workload": "decode router M=1 H=7168 E=256 k=8 softmax renorm, no bias; "
                         "one step = 40 layers x 1 call, distinct W_gate per call from a "
                         "160-matrix (587 MB) pool, HIP-graph replay",
-            "M": 1, "H": H, "E": E, "k": k, "calls_per_step": LAYERS,
+            "M": 1, "H": 7168, "E": 256, "k": 8, "calls_per_step": LAYERS,
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "decode_router_kernel",
-            "achieved": round(achieved_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "bytes_per_launch": bytes_per_launch,
-            "launch_us": round(kern_us, 3),
-        },
-        "cpu_baseline": cpu,
-        "extras": extras,
+        "roofline": None,
+        "cpu_baseline": None,
+        "extras": {},
     }
+
+    if args.section in ("all", "decode"):
+        decode_headline(torch, R, W, dev, args, out)
+    if args.section in ("all",):
+        out["extras"].update(decode_extras(torch, R, W, dev, args))
+    if args.section in ("all", "topk"):
+        out["extras"].update(topk_extras(torch, R, W, dev, args))
+    if args.section in ("all", "prefill"):
+        out["extras"].update(prefill_extras(torch, R, W, dev, args))
+    if args.section == "all" and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def run_extras(torch, R, W, dev, stream, args):
+def decode_headline(torch, R, W, dev, args, out):
+    H, E, k = 7168, 256, 8
+    log(f"generating pools: W {POOL}x{E}x{H} bf16, X {LAYERS}x1x{H}")
+    wpool = W.torch_gaussian_bf16((POOL, E, H), 1.0 / H ** 0.5, seed=1, device=dev)
+    xpool = W.torch_rms_normalised_bf16((LAYERS, 1, H), seed=2, device=dev)
+    inds = torch.empty((LAYERS, 1, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((LAYERS, 1, k), dtype=torch.float32, device=dev)
+
+    def call(layer, widx):
+        return lambda: R.router_fwd(xpool[layer], wpool[widx], None, k, W.SOFTMAX, True,
+                                    out_inds=inds[layer], out_weights=wts[layer])
+
+    groups = POOL // LAYERS
+    step_calls = [[call(l, g * LAYERS + l) for l in range(LAYERS)] for g in range(groups)]
+    clean = [GraphTimer(torch, c) for c in step_calls]
+
+    log(f"timing {args.steps} steps x {LAYERS} calls (cold W pool, graph replay)")
+    wall, ev_ms = timed_replays(torch, clean, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    out["value"] = round(ms_per_step * 1e3 / LAYERS, 3)
+    out["ms_per_step"] = round(ms_per_step, 4)
+
+    n_launch = args.steps * LAYERS
+    kern_us = ev_ms * 1e3 / n_launch
+    bytes_per_launch = E * H * 2 + H * 2 + k * 8  # W + x + (inds, weights)
+    achieved = bytes_per_launch / (kern_us * 1e-6) / 1e9
+    traffic = committed_traffic()
+    out["roofline"] = {
+        "bound": "hbm",
+        "kernel": "decode_router_kernel",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "bytes_per_launch": bytes_per_launch,
+        "launch_us": round(kern_us, 3),
+        "launches_timed": n_launch,
+        "launch_timing": "HIP event pair on the launching stream around the timed replays "
+                         "(back-to-back launches) / launch count",
+    }
+    # cache-hot cycle: the same 40 gate matrices every step (Infinity-Cache resident)
+    hot, _ = timed_replays(torch, clean[:1], args.steps, args.warmup)
+    out["extras"]["decode_M1_H7168_hot_us_per_call"] = round(hot * 1e6 / (args.steps * LAYERS), 3)
+    out["extras"]["decode_kernel_sources_sha256_16"] = kernel_source_digest()
+    del clean, wpool
+
+
+def decode_extras(torch, R, W, dev, args):
     ex = {}
-    reps = max(args.steps, 10)
-
-    def graph_us(fn, n_calls):
-        fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e6 / (reps * n_calls)
-
-    # verify widths at H=4096 (40-layer hot cycle)
     H, E = 4096, 256
     wl = W.torch_gaussian_bf16((LAYERS, E, H), 1.0 / H ** 0.5, seed=3, device=dev)
     for M in (1, 2, 8):
         x = W.torch_rms_normalised_bf16((LAYERS, M, H), seed=4 + M, device=dev)
         oi = torch.empty((LAYERS, M, 8), dtype=torch.int32, device=dev)
         ow = torch.empty((LAYERS, M, 8), dtype=torch.float32, device=dev)
-
-        def step(x=x, oi=oi, ow=ow):
-            for l in range(LAYERS):
-                R.router_fwd(x[l], wl[l], None, 8, W.SOFTMAX, True, out_inds=oi[l], out_weights=ow[l])
-        ex[f"decode_M{M}_H4096_hot_us_per_call"] = round(graph_us(step, LAYERS), 3)
+        calls = [(lambda l=l, x=x, oi=oi, ow=ow: R.router_fwd(x[l], wl[l], None, 8, W.SOFTMAX, True,
+                                                               out_inds=oi[l], out_weights=ow[l]))
+                 for l in range(LAYERS)]
+        ex[f"decode_M{M}_H4096_hot_us_per_call"] = round(graph_call_us(torch, calls, args.steps, args.warmup), 3)
     log("verify widths done")
 
     # biased M=2 with and without the unique-route table (k=6)
@@ -225,61 +264,76 @@ def run_extras(torch, R, W, dev, stream, args):
     tabs = [{n: torch.empty(12 if n != "unique_count" else 1, dtype=torch.int32, device=dev)
              for n in ("unique_ids", "token_mask", "slot_to_unique", "unique_count")}
             for _ in range(LAYERS)]
-
-    def step_off():
-        for l in range(LAYERS):
-            R.router_fwd(x2[l], wl[l], bias, 6, W.SQRT_SOFTPLUS, True, out_inds=oi[l], out_weights=ow[l])
-
-    def step_on():
-        for l in range(LAYERS):
-            R.router_fwd_m2_table(x2[l], wl[l], bias, 6, W.SQRT_SOFTPLUS, True,
-                                  out=dict(inds=oi[l], weights=ow[l], **tabs[l]))
-    off = graph_us(step_off, LAYERS)
-    on = graph_us(step_on, LAYERS)
-    ex["biased_M2_k6_table_off_us_per_call"] = round(off, 3)
-    ex["biased_M2_k6_table_on_us_per_call"] = round(on, 3)
-    ex["table_overhead_us_per_call"] = round(on - off, 3)
+    off = [(lambda l=l: R.router_fwd(x2[l], wl[l], bias, 6, W.SQRT_SOFTPLUS, True,
+                                     out_inds=oi[l], out_weights=ow[l])) for l in range(LAYERS)]
+    on = [(lambda l=l: R.router_fwd_m2_table(x2[l], wl[l], bias, 6, W.SQRT_SOFTPLUS, True,
+                                             out=dict(inds=oi[l], weights=ow[l], **tabs[l])))
+          for l in range(LAYERS)]
+    t_off = graph_call_us(torch, off, args.steps, args.warmup)
+    t_on = graph_call_us(torch, on, args.steps, args.warmup)
+    ex["biased_M2_k6_table_off_us_per_call"] = round(t_off, 3)
+    ex["biased_M2_k6_table_on_us_per_call"] = round(t_on, 3)
+    ex["table_overhead_us_per_call"] = round(t_on - t_off, 3)
     ex["table_overhead_context_b70_us_per_layer"] = 3.132
-    del wl
-    log("table on/off done")
+    for M in (16, 64):
+        xm = W.torch_gaussian_bf16((LAYERS, M, H), 1.0, seed=20 + M, device=dev)
+        oim = torch.empty((LAYERS, M, 6), dtype=torch.int32, device=dev)
+        owm = torch.empty((LAYERS, M, 6), dtype=torch.float32, device=dev)
+        calls = [(lambda l=l, xm=xm, oim=oim, owm=owm: R.router_fwd(
+            xm[l], wl[l], bias, 6, W.SQRT_SOFTPLUS, True, out_inds=oim[l], out_weights=owm[l]))
+            for l in range(LAYERS)]
+        ex[f"biased_M{M}_k6_us_per_call"] = round(graph_call_us(torch, calls, args.steps, args.warmup), 3)
+    log("biased router done")
+    return ex
 
-    # standalone top-k at M=4096
+
+def topk_extras(torch, R, W, dev, args):
+    ex = {}
     lg = torch.randn((4, 4096, 256), device=dev, dtype=torch.float32) * 2 ** 0.5
-    ti = torch.empty((4096, 8), dtype=torch.int32, device=dev)
-    tw = torch.empty((4096, 8), dtype=torch.float32, device=dev)
-    evt = event_times_ms(torch, lambda i: R.router_topk_from_logits(lg[i % 4], None, 8, out_inds=ti, out_weights=tw),
-                         reps, stream)
-    t_us = 1e3 * sum(evt) / len(evt)
-    ex["topk_M4096_us_per_call"] = round(t_us, 3)
+    ti = torch.empty((4, 4096, 8), dtype=torch.int32, device=dev)
+    tw = torch.empty((4, 4096, 8), dtype=torch.float32, device=dev)
+    calls = [(lambda i=i: R.router_topk_from_logits(lg[i], None, 8, out_inds=ti[i], out_weights=tw[i]))
+             for i in range(4)]
+    t_us = graph_call_us(torch, calls, max(args.steps // 2, 2), 2)
+    ex["topk_M4096_event_us_per_call"] = round(t_us, 3)
     ex["topk_M4096_GBs"] = round((4096 * 256 * 4 + 4096 * 64) / (t_us * 1e-6) / 1e9, 1)
-    del lg
     log("top-k done")
+    return ex
 
-    # prefill M=8192, H=7168 (4 rotating X buffers: 470 MB, cold)
-    M, H = 8192, 7168
-    xs = W.torch_gaussian_bf16((4, M, H), 1.0, seed=11, device=dev)
+
+def prefill_extras(torch, R, W, dev, args):
+    ex = {}
+    M, H, E = 8192, 7168, 256
+    xs = W.torch_gaussian_bf16((4, M, H), 1.0, seed=11, device=dev)   # 470 MB: cold X
     wp = W.torch_gaussian_bf16((E, H), 1.0 / H ** 0.5, seed=12, device=dev)
     bp = W.torch_uniform_f32(E, -0.02, 0.02, seed=13, device=dev)
     pi = torch.empty((M, 8), dtype=torch.int32, device=dev)
     pw = torch.empty((M, 8), dtype=torch.float32, device=dev)
-    for i in range(args.warmup):
-        R.router_fwd(xs[i % 4], wp, bp, 8, W.SOFTMAX, True, out_inds=pi, out_weights=pw)
-    evp = event_times_ms(torch, lambda i: R.router_fwd(xs[i % 4], wp, bp, 8, W.SOFTMAX, True,
-                                                       out_inds=pi, out_weights=pw), reps, stream)
-    p_us = 1e3 * sum(evp) / len(evp)
+    calls = [(lambda i=i: R.router_fwd(xs[i], wp, bp, 8, W.SOFTMAX, True, out_inds=pi, out_weights=pw))
+             for i in range(4)]
+    p_us = graph_call_us(torch, calls, max(args.steps // 2, 2), 2)
     flops = 2.0 * M * E * H
-    ex["prefill_M8192_H7168_us_per_call"] = round(p_us, 2)
+    tflops = flops / (p_us * 1e-6) / 1e12
+    ex["prefill_M8192_H7168_event_us_per_call"] = round(p_us, 2)
     ex["prefill_M8192_tokens_per_s"] = round(M / (p_us * 1e-6), 0)
-    ex["prefill_mfma_tflops"] = round(flops / (p_us * 1e-6) / 1e12, 1)
-    ex["prefill_mfma_frac"] = round(flops / (p_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-    ex["prefill_hbm_frac"] = round((M * H * 2 + E * H * 2 + M * 64) / (p_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    ex["prefill_mfma_tflops"] = round(tflops, 1)
+    ex["prefill_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
+    ex["prefill_hbm_frac"] = round((M * H * 2 + E * H * 2 + E * 4 + M * 64) / (p_us * 1e-6) / 1e9
+                                   / HBM_PEAK_GBS, 4)
+    # context: the vendor GEMM (hipBLASLt through torch) on the same projection, logits only
+    xf = xs[0]
+    wpt = wp.t().contiguous()  # [H, E]: no transposed view reaches the library GEMM
+    try:
+        mm_us = graph_call_us(torch, [lambda: torch.mm(xf, wpt)] * 4, max(args.steps // 2, 2), 2)
+        ex["context_torch_mm_bf16_logits_only_us"] = round(mm_us, 2)
+    except RuntimeError as exc:  # library GEMM not capturable
+        log(f"torch.mm context skipped: {exc}")
     log("prefill done")
     return ex
 
 
 def cpu_baseline(W, seconds):
     """The oracle (as written, single thread) on M=1 H=7168 router calls for ~`seconds`."""
-    import numpy as np
     import oracle
 
     orc = oracle.get()
