@@ -40,7 +40,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 LAYERS = 40
 POOL = 160
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_M1_H7168_traffic.txt")
-KERNEL_SOURCES = ["route_common.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
+KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
 
 
 def log(msg):

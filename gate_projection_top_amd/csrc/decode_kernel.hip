@@ -5,24 +5,34 @@
 // The page leaves open how a matvec spread over many workgroups meets a top-k
 // that needs the whole logit row in one place (serialise the matvec into one
 // threadgroup, or reduce across threadgroups).  Here: reduce across
-// workgroups with a last-arriver hand-off, because one CU cannot pull the
-// 2-3.5 MiB gate matrix from HBM fast enough on its own.
+// workgroups, because one CU cannot pull the 2-3.5 MiB gate matrix from HBM
+// fast enough on its own.
 //
-//   grid = R row blocks x B expert blocks x S H-splits, 4 waves each.
+//   grid = R row blocks x B expert blocks x S H-splits; each workgroup has
+//   kDecodeWaves load waves and one control wave.
+//   Start: the control wave draws an arrival ticket on the row block's
+//     counter.  The workgroup that draws the last ticket is the row block's
+//     finisher; every other workgroup of the block has started by then, and
+//     none of them ever waits, so the finisher's wait below always ends.
+//     The ticket's round trip overlaps the loads of phase 1.
 //   Phase 1 (every workgroup): the 16x16 (tokens x experts) partial dot
 //     products over its H-split, one bf16 MFMA 16x16x32 per 32-wide k-step,
-//     the four waves' partials summed in LDS in a fixed order and published
-//     with device-coherent stores; then an agent-scope arrival count per row
-//     block.
-//   Phase 2 (the last workgroup of a row block): sum the S partials
-//     of each logit in split order into an LDS row tile (the only place the
-//     logits live unless the caller asks for them), route each row with the
-//     shared route_row(), and at M=2 emit the unique-route table.  It resets
-//     the counter, so the kernel is replayable inside a HIP graph.
+//     every wave's loads issued before its first MFMA; the waves' partials
+//     summed in LDS in wave order and published with device-coherent 16-byte
+//     stores.  Non-finishers are then done: no wait for the stores.
+//   Phase 2 (finisher): every partial slot holds a signalling-NaN sentinel
+//     between launches, and arithmetic never produces that bit pattern, so
+//     a slot holding anything else has been published.  Each wave takes rows
+//     of the block; lane L polls the S partials of experts 4L..4L+3 (the
+//     routing layout itself) until none is the sentinel, resets those slots
+//     to the sentinel, adds the partials in split order and routes the row
+//     with route_row(); at M=2 the unique-route table follows.  The finisher
+//     also resets the counter, so the kernel replays inside a HIP graph.
 //
 // Every logit is accumulated in the same order regardless of its expert
 // index, so two experts with identical gate rows get bitwise-equal logits and
 // the tie goes to the lower index, as the contract requires.
+#include "coherent.hpp"
 #include "launch.hpp"
 #include "route_common.hpp"
 
@@ -30,17 +40,29 @@ namespace gpt {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kLoadWaves = kDecodeWaves;
+constexpr int kWaves = kLoadWaves + 1;  // + the control wave
 constexpr int kThreads = kWaves * kWave;
-constexpr int kChunk = 4;  // k-steps loaded per wave before its MFMAs
-constexpr int kItemsPerThread = 4;  // logits gathered per thread per batch in phase 2
+constexpr int kChunk = 8;  // k-steps whose loads a wave issues before its MFMAs
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ float not_sentinel(float v)
+{
+    // a quiet NaN stands in for the (never produced) sentinel pattern
+    return __float_as_uint(v) == kDecodeSentinel ? __uint_as_float(0x7fc00000u) : v;
+}
+
+__device__ __forceinline__ bool published(f32x4 v)
+{
+    // bitwise, not short-circuit: one compare per value, no branches
+    return (__float_as_uint(v[0]) != kDecodeSentinel) & (__float_as_uint(v[1]) != kDecodeSentinel) &
+           (__float_as_uint(v[2]) != kDecodeSentinel) & (__float_as_uint(v[3]) != kDecodeSentinel);
+}
+
 __global__ __launch_bounds__(kThreads) void decode_router_kernel(DecodeLaunch a)
 {
-    __shared__ float red[kWaves][kDecodeTile][kDecodeTile + 1];
-    __shared__ float lrow[kDecodeTile][kMaxE];
+    __shared__ float red[kLoadWaves][kDecodeTile][kDecodeTile + 1];
     __shared__ int32_t slots[2 * kMaxK];
     __shared__ int is_last;
 
@@ -55,125 +77,135 @@ __global__ __launch_bounds__(kThreads) void decode_router_kernel(DecodeLaunch a)
     const int b = bid % B;
     const int r = bid / B;
 
-    // ---- phase 1: partial logits of 16 tokens x 16 experts over one H-split
-    const int arow = r * kDecodeTile + (lane & 15);  // MFMA A row  = token
-    const int bcol = b * kDecodeTile + (lane & 15);  // MFMA B col  = expert
-    const int kq = (lane >> 4) * 8;                  // this lane's 8 of the 32 k
-    const bool arow_ok = arow < a.M;
-    const bool bcol_ok = bcol < a.E;
-    const uint16_t* xp = a.x + (int64_t)(arow_ok ? arow : 0) * a.H + kq;
-    const uint16_t* wp = a.w + (int64_t)(bcol_ok ? bcol : 0) * a.H + kq;
-
-    const int KS = (a.H + 31) >> 5;
-    const int ks0 = s * a.ks_per_split;
-    const int ks1 = min(KS, ks0 + a.ks_per_split);
-    const bf16x8 zero = __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0});
-
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int base = ks0 + wave; base < ks1; base += kWaves * kChunk) {
-        bf16x8 av[kChunk], bv[kChunk];
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int ks = base + c * kWaves;
-            const int k0 = ks * 32;
-            const bool in = ks < ks1 && (k0 + kq) < a.H;
-            av[c] = (in && arow_ok) ? load_bf16x8(xp + k0) : zero;
-            bv[c] = (in && bcol_ok) ? load_bf16x8(wp + k0) : zero;
-        }
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c)
-            if (base + c * kWaves < ks1)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv[c], acc, 0, 0, 0);
-    }
-
-    // MFMA 16x16 result layout: lane holds rows 4*(lane/16)+i, column lane%16.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][lane & 15] = acc[i];
-    __syncthreads();
-
-    // ---- hand-off.  Wave 0 alone publishes the workgroup's 16x16 partials
-    // with device-coherent (agent-scope) stores, waits until they have
-    // completed, then takes a ticket on the row block's arrival counter.  The
-    // workgroup that draws the last ticket reads every partial back with
-    // device-coherent loads.  No cache-wide writeback or invalidate is needed
-    // because the published data never sits in a non-coherent cache line.
-    if (wave == 0) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int idx = h * kWave + lane;
-            const int rr = idx >> 4, cc = idx & 15;
-            const float sum = ((red[0][rr][cc] + red[1][rr][cc]) + red[2][rr][cc]) + red[3][rr][cc];
-            const int row = r * kDecodeTile + rr;
-            const int e = b * kDecodeTile + cc;
-            if (row < a.M && e < a.E)
-                __hip_atomic_store(&a.partials[((int64_t)s * a.M + row) * a.E + e], sum,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // every partial store has completed
+    if (wave == kLoadWaves) {
+        // ---- control wave: the arrival ticket (its wait stalls no load wave)
         if (lane == 0) {
-            const uint32_t arrivals = (uint32_t)(B * a.S);
             const uint32_t prev = __hip_atomic_fetch_add(&a.counters[r], 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            is_last = (prev == arrivals - 1u);
+            is_last = prev == (uint32_t)(B * a.S) - 1u;
         }
+    } else {
+        // ---- phase 1: partial logits of 16 tokens x 16 experts over one H-split
+        const int arow = r * kDecodeTile + (lane & 15);  // MFMA A row  = token
+        const int bcol = b * kDecodeTile + (lane & 15);  // MFMA B col  = expert
+        const int kq = (lane >> 4) * 8;                  // this lane's 8 of the 32 k
+        const bool arow_ok = arow < a.M;
+        const bool bcol_ok = bcol < a.E;
+        const uint16_t* xp = a.x + (int64_t)(arow_ok ? arow : 0) * a.H + kq;
+        const uint16_t* wp = a.w + (int64_t)(bcol_ok ? bcol : 0) * a.H + kq;
+
+        const int KS = (a.H + 31) >> 5;
+        const int ks0 = s * a.ks_per_split;
+        const int ks1 = min(KS, ks0 + a.ks_per_split);
+        const bf16x8 zero = __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0});
+
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int base = ks0 + wave; base < ks1; base += kLoadWaves * kChunk) {
+            bf16x8 av[kChunk], bv[kChunk];
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const int ks = base + c * kLoadWaves;
+                const int k0 = ks * 32;
+                const bool in = ks < ks1 && (k0 + kq) < a.H;
+                av[c] = (in && arow_ok) ? load_bf16x8(xp + k0) : zero;
+                bv[c] = (in && bcol_ok) ? load_bf16x8(wp + k0) : zero;
+            }
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c)
+                if (base + c * kLoadWaves < ks1)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv[c], acc, 0, 0, 0);
+        }
+        // MFMA 16x16 result layout: lane holds rows 4*(lane/16)+i, column lane%16.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][lane & 15] = acc[i];
     }
     __syncthreads();
-    if (!is_last) return;
+
+    // ---- publish: wave 0 sums the load waves' partials (wave order) and
+    // stores them device-coherently (lane l: token row l/4, experts
+    // 4(l%4)..+3 of the block).  Layout [S][M][256] fp32.
+    const int qstride = a.M * kMaxE * 4;  // bytes per split
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(a.partials, 0, a.S * qstride, 0x00020000);
+    if (wave == 0) {
+        const int rr = lane >> 2, cc = (lane & 3) * 4;
+        f32x4 sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v = red[0][rr][cc + j];
+#pragma unroll
+            for (int w = 1; w < kLoadWaves; ++w) v += red[w][rr][cc + j];
+            sum[j] = not_sentinel(v);
+        }
+        const int row = r * kDecodeTile + rr;
+        if (row < a.M) publish4(prs, s * qstride + (row * kMaxE + b * kDecodeTile + cc) * 4, sum);
+    }
+    if (!is_last) return;  // written by the control wave before the barrier
     if (tid == 0) __hip_atomic_store(&a.counters[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // ---- phase 2: full logits of the row block into LDS, then route rows
-    // All of a thread's partial loads are issued before any is consumed (one
-    // memory round trip per batch instead of one per split); the sum itself
-    // runs in split order.
+    // ---- phase 2 (finisher): one wave per row; lane L owns experts 4L..4L+3.
     const int t0 = r * kDecodeTile;
     const int nrows = min(kDecodeTile, a.M - t0);
-    const int items = nrows * a.E;
-    const int64_t split_stride = (int64_t)a.M * a.E;
-    const float* pbase = a.partials + (int64_t)t0 * a.E;
-    for (int base = tid; base < items; base += kThreads * kItemsPerThread) {
-        float part[kItemsPerThread][kDecodeMaxSplits];
+    const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};
+    const bool mine = lane < 4 * B;  // the lane's expert group lies in a published block
+    const f32x4 sentinel4 = __builtin_bit_cast(f32x4, u32x4{kDecodeSentinel, kDecodeSentinel,
+                                                            kDecodeSentinel, kDecodeSentinel});
+    // bias beyond E reads as 0 (out-of-range buffer loads return zero)
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
+
+    for (int t = wave; t < nrows; t += kWaves) {
+        const int off = ((t0 + t) * kMaxE + lane * kPerLane) * 4;
+        // Splits q >= S lie past the end of the buffer range: their loads
+        // return zeros and their stores are dropped, so no branch on S.
+        // The wait ends once the publishers' stores land; the time limit is
+        // only a guard so that no wave can spin forever: a row that hits it
+        // is reported as index -1 with a NaN weight.
+        f32x4 part[kDecodeMaxSplits];
+        const uint64_t t_poll = __builtin_amdgcn_s_memrealtime();
+        bool gave_up = false;
+        for (;;) {
+            asm volatile("" ::: "memory");  // re-read every pass: the loads stay in the loop
 #pragma unroll
-        for (int u = 0; u < kItemsPerThread; ++u) {
-            const int it = base + u * kThreads;
+            for (int q = 0; q < kDecodeMaxSplits; ++q) part[q] = fetch4(prs, off + q * qstride);
+            bool ok = true;
 #pragma unroll
-            for (int q = 0; q < kDecodeMaxSplits; ++q)
-                part[u][q] = (it < items && q < a.S)
-                                 ? __hip_atomic_load(pbase + q * split_stride + it, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)
-                                 : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kItemsPerThread; ++u) {
-            const int it = base + u * kThreads;
-            if (it < items) {
-                float sum = part[u][0];
-#pragma unroll
-                for (int q = 1; q < kDecodeMaxSplits; ++q)
-                    if (q < a.S) sum += part[u][q];
-                const int t = it / a.E;
-                const int e = it - t * a.E;
-                lrow[t][e] = sum;
-                if (a.logits_out) a.logits_out[(int64_t)(t0 + t) * a.E + e] = sum;
+            for (int q = 0; q < kDecodeMaxSplits; ++q) ok &= published(part[q]);
+            if (__builtin_amdgcn_ballot_w64(mine && !ok) == 0) break;
+            if (__builtin_amdgcn_s_memrealtime() - t_poll > kDecodePollLimitTicks) {
+                gave_up = true;
+                break;
             }
         }
-    }
-    __syncthreads();
-
-    const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};
-    float bv[kPerLane] = {0.f, 0.f, 0.f, 0.f};
-    if (a.bias) {
-#pragma unroll
-        for (int j = 0; j < kPerLane; ++j) {
-            const int e = lane * kPerLane + j;
-            if (e < a.E) bv[j] = a.bias[e];
+        if (gave_up) {
+            if (lane < a.k) {
+                const int64_t o = (int64_t)(t0 + t) * a.k + lane;
+                a.inds[o] = -1;
+                a.weights[o] = __builtin_nanf("");
+                if (a.table_ids) slots[t * a.k + lane] = -1;
+            }
+            continue;
         }
-    }
-    for (int t = wave; t < nrows; t += kWaves) {
+        if (mine) {
+#pragma unroll
+            for (int q = 0; q < kDecodeMaxSplits; ++q) publish4(prs, off + q * qstride, sentinel4);
+        }
+        float bv[kPerLane];
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j)
+            bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  brs, (lane * kPerLane + j) * 4, 0, 0));
+        f32x4 sum = part[0];
+#pragma unroll
+        for (int q = 1; q < kDecodeMaxSplits; ++q) sum += part[q];
         float v[kPerLane];
 #pragma unroll
-        for (int j = 0; j < kPerLane; ++j) {
-            const int e = lane * kPerLane + j;
-            v[j] = e < a.E ? lrow[t][e] : 0.f;
+        for (int j = 0; j < kPerLane; ++j) v[j] = (lane * kPerLane + j < a.E) ? sum[j] : 0.f;
+        if (a.logits_out) {
+            float* lo = a.logits_out + (int64_t)(t0 + t) * a.E + lane * kPerLane;
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j)
+                if (lane * kPerLane + j < a.E) lo[j] = v[j];
         }
         const RowResult res = route_row(v, bv, spec);
         if (lane < a.k) {

@@ -29,7 +29,7 @@ struct DecodeLaunch {
     int32_t* table_mask;
     int32_t* table_s2u;
     int32_t* table_count;
-    float* partials;        // workspace [S][M][E]
+    float* partials;        // workspace [S][M][256], every slot kDecodeSentinel between calls
     uint32_t* counters;     // workspace [R], zero between calls
     int S;                  // H splits
     int ks_per_split;       // 32-wide k-steps per split
@@ -61,6 +61,17 @@ constexpr int kDecodeTile = 16;        // rows per row block, experts per expert
 constexpr int kDecodeMaxSplits = 16;   // H splits
 constexpr int kDecodeMaxM = 64;
 constexpr int kDecodeMaxRowBlocks = kDecodeMaxM / kDecodeTile;
+constexpr int kDecodeWaves = 8;                // load waves per workgroup (plus one control wave)
+// Empty decode partial slot: a signalling NaN, a pattern no arithmetic
+// result has (NaN results are quiet).
+constexpr uint32_t kDecodeSentinel = 0x7f800001u;
+// Guard on the finisher's wait for published partials (100 MHz realtime
+// clock): 100 ms, orders of magnitude above any real wait.
+constexpr uint64_t kDecodePollLimitTicks = 10000000u;
+// Workgroups a decode launch aims for.  Fewer than one per CU: every
+// workgroup's loads still fit in one round trip to HBM, and fewer arrivals
+// queue on the row block's counter.
+constexpr int kDecodeTargetWorkgroups = 128;
 
 // Prefill geometry: 128-row tiles; K split S ways while tiles * S <= 256.
 constexpr int kPrefillTileRows = 128;

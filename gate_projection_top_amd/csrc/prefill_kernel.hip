@@ -28,6 +28,7 @@
 // whichever path produces it.
 #include "launch.hpp"
 #include "route_common.hpp"
+#include "coherent.hpp"
 
 namespace gpt {
 
@@ -49,7 +50,6 @@ constexpr int kTileBytes = kBM * kTileStride * 4;
 constexpr int kRingBytes = kNStage * kStageBytes;
 constexpr int kLdsBytes = kRingBytes > kTileBytes ? kRingBytes : kTileBytes;
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // ---------------------------------------------------------------------------
@@ -110,24 +110,6 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// ---------------------------------------------------------------------------
-// split exchange: 128-bit device-coherent (sc1) stores and loads
-// ---------------------------------------------------------------------------
-constexpr int kCoherent = 16;  // buffer cache-policy bit: device scope
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
-}
-__device__ __forceinline__ void publish4(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCoherent);
-}
-__device__ __forceinline__ f32x4 fetch4(__amdgpu_buffer_rsrc_t r, int byte_off)
-{
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
 }
 
 // Byte offset of the published partial of split s, tile-local row r, column
@@ -293,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
     uint32_t* arrive = p.counters + tile * kPrefillCountersPerTile;
     uint32_t* done = arrive + 1;
     uint32_t* abandoned = arrive + 2;  // one flag per split
-    const __amdgpu_buffer_rsrc_t prs = partial_rsrc(p.partials);
+    const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(p.partials);
     constexpr int kVecPerRow = kBN / 4;  // 64 float4 per row
 
     // publish the rows owned by the other splits

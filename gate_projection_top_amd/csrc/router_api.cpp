@@ -11,7 +11,7 @@
 namespace {
 
 struct DeviceWorkspace {
-    float* partials = nullptr;          // decode H-split partial logits [S][M][E]
+    float* partials = nullptr;          // decode H-split partial logits [S][M][256], sentinel-filled
     uint32_t* counters = nullptr;       // decode arrival counters, one per row block
     float* pf_partials = nullptr;       // prefill split partials [tile][S][128][256]
     uint32_t* pf_counters = nullptr;    // prefill per-tile counters
@@ -46,6 +46,8 @@ int init_device(int dev)
     if (e == hipSuccess) e = hipMalloc((void**)&ws.counters, kCounters * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_partials, kPfPartialFloats * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_counters, kPfCounters * sizeof(uint32_t));
+    if (e == hipSuccess)
+        e = hipMemsetD32((hipDeviceptr_t)ws.partials, (int)gpt::kDecodeSentinel, kPartialFloats);
     if (e == hipSuccess) e = hipMemset(ws.counters, 0, kCounters * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(ws.pf_counters, 0, kPfCounters * sizeof(uint32_t));
     // The counters must read zero before any stream (blocking or not) runs a
@@ -97,15 +99,15 @@ int check_projection(const void* x, const void* w)
     return ROUTER_OK;
 }
 
-// Decode split choice: aim for >= 256 workgroups (one per CU) with at least
-// one k-step per wave in every split.
+// Decode split choice: about kDecodeTargetWorkgroups workgroups, with at
+// least one 32-wide k-step per wave in every split.
 void decode_splits(int M, int H, int E, int* S_out, int* ks_per_split_out)
 {
     const int R = (M + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int B = (E + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int KS = (H + 31) / 32;
-    int S = (256 + R * B - 1) / (R * B);
-    const int by_work = KS / 4 > 1 ? KS / 4 : 1;
+    int S = (gpt::kDecodeTargetWorkgroups + R * B - 1) / (R * B);
+    const int by_work = KS / gpt::kDecodeWaves > 1 ? KS / gpt::kDecodeWaves : 1;
     if (S > by_work) S = by_work;
     if (S > gpt::kDecodeMaxSplits) S = gpt::kDecodeMaxSplits;
     if (S < 1) S = 1;
