@@ -40,10 +40,8 @@ namespace gpt {
 
 namespace {
 
-constexpr int kLoadWaves = kDecodeWaves;
-constexpr int kWaves = kLoadWaves + 1;  // + the control wave
-constexpr int kThreads = kWaves * kWave;
-constexpr int kChunk = 8;  // k-steps whose loads a wave issues before its MFMAs
+constexpr int kChunk = 8;      // k-steps whose loads a wave issues before its MFMAs
+constexpr int kPollGap = 16;   // s_sleep units (64 clocks) between the two polls in flight
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -60,8 +58,44 @@ __device__ __forceinline__ bool published(f32x4 v)
            (__float_as_uint(v[2]) != kDecodeSentinel) & (__float_as_uint(v[3]) != kDecodeSentinel);
 }
 
-__global__ __launch_bounds__(kThreads) void decode_router_kernel(DecodeLaunch a)
+// One poll: every split's slot of this lane's four experts.  Splits q >= S
+// lie past the end of the buffer range, so their loads return zeros without
+// touching memory.  The empty asm keeps the loads from being hoisted out of
+// the polling loop.
+template <int kMaxS>
+__device__ __forceinline__ void poll_issue(f32x4 (&p)[kMaxS], __amdgpu_buffer_rsrc_t prs, int off,
+                                           int qstride)
 {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < kMaxS; ++q) p[q] = fetch4(prs, off + q * qstride);
+}
+
+// True when no lane that owns published slots still sees the sentinel.
+template <int kMaxS>
+__device__ __forceinline__ bool poll_ready(const f32x4 (&p)[kMaxS], bool mine)
+{
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < kMaxS; ++q) ok &= published(p[q]);
+    return __builtin_amdgcn_ballot_w64(mine && !ok) == 0;
+}
+
+// The logit: partials added in split order (zeros past S change nothing).
+template <int kMaxS>
+__device__ __forceinline__ f32x4 poll_sum(const f32x4 (&p)[kMaxS])
+{
+    f32x4 sum = p[0];
+#pragma unroll
+    for (int q = 1; q < kMaxS; ++q) sum += p[q];
+    return sum;
+}
+
+template <int kLoadWaves, int kMaxS>
+__global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel(DecodeLaunch a)
+{
+    constexpr int kWaves = kLoadWaves + 1;  // + the control wave
+
     __shared__ float red[kLoadWaves][kDecodeTile][kDecodeTile + 1];
     __shared__ int32_t slots[2 * kMaxK];
     __shared__ int is_last;
@@ -78,11 +112,26 @@ __global__ __launch_bounds__(kThreads) void decode_router_kernel(DecodeLaunch a)
     const int r = bid / B;
 
     if (wave == kLoadWaves) {
-        // ---- control wave: the arrival ticket (its wait stalls no load wave)
+        // ---- control wave: the arrival ticket, in two levels so that no
+        // counter sees more than max(S, B) arrivals: the last of an expert
+        // block's S workgroups goes on to the row block's counter, and the
+        // last of those B is the finisher.  The control wave's waits stall no
+        // load wave.  Each counter is reset by the workgroup that drew its
+        // last ticket, when every ticket on it has been drawn.
         if (lane == 0) {
-            const uint32_t prev = __hip_atomic_fetch_add(&a.counters[r], 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            is_last = prev == (uint32_t)(B * a.S) - 1u;
+            uint32_t* block_ctr = a.counters + kDecodeCounterStride * (r * kDecodeMaxBlocks + b);
+            uint32_t* row_ctr = a.counters + kDecodeCounterStride * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + r);
+            int last = 0;
+            if (__hip_atomic_fetch_add(block_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)a.S - 1u) {
+                __hip_atomic_store(block_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (__hip_atomic_fetch_add(row_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (uint32_t)B - 1u) {
+                    __hip_atomic_store(row_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    last = 1;
+                }
+            }
+            is_last = last;
         }
     } else {
         // ---- phase 1: partial logits of 16 tokens x 16 experts over one H-split
@@ -141,7 +190,6 @@ __global__ __launch_bounds__(kThreads) void decode_router_kernel(DecodeLaunch a)
         if (row < a.M) publish4(prs, s * qstride + (row * kMaxE + b * kDecodeTile + cc) * 4, sum);
     }
     if (!is_last) return;  // written by the control wave before the barrier
-    if (tid == 0) __hip_atomic_store(&a.counters[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- phase 2 (finisher): one wave per row; lane L owns experts 4L..4L+3.
     const int t0 = r * kDecodeTile;
@@ -154,60 +202,101 @@ __global__ __launch_bounds__(kThreads) void decode_router_kernel(DecodeLaunch a)
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
 
-    for (int t = wave; t < nrows; t += kWaves) {
-        const int off = ((t0 + t) * kMaxE + lane * kPerLane) * 4;
-        // Splits q >= S lie past the end of the buffer range: their loads
-        // return zeros and their stores are dropped, so no branch on S.
-        // The wait ends once the publishers' stores land; the time limit is
-        // only a guard so that no wave can spin forever: a row that hits it
-        // is reported as index -1 with a NaN weight.
-        f32x4 part[kDecodeMaxSplits];
-        const uint64_t t_poll = __builtin_amdgcn_s_memrealtime();
-        bool gave_up = false;
-        for (;;) {
-            asm volatile("" ::: "memory");  // re-read every pass: the loads stay in the loop
-#pragma unroll
-            for (int q = 0; q < kDecodeMaxSplits; ++q) part[q] = fetch4(prs, off + q * qstride);
-            bool ok = true;
-#pragma unroll
-            for (int q = 0; q < kDecodeMaxSplits; ++q) ok &= published(part[q]);
-            if (__builtin_amdgcn_ballot_w64(mine && !ok) == 0) break;
-            if (__builtin_amdgcn_s_memrealtime() - t_poll > kDecodePollLimitTicks) {
-                gave_up = true;
-                break;
-            }
-        }
-        if (gave_up) {
-            if (lane < a.k) {
-                const int64_t o = (int64_t)(t0 + t) * a.k + lane;
-                a.inds[o] = -1;
-                a.weights[o] = __builtin_nanf("");
-                if (a.table_ids) slots[t * a.k + lane] = -1;
-            }
-            continue;
-        }
-        if (mine) {
-#pragma unroll
-            for (int q = 0; q < kDecodeMaxSplits; ++q) publish4(prs, off + q * qstride, sentinel4);
-        }
-        float bv[kPerLane];
-#pragma unroll
-        for (int j = 0; j < kPerLane; ++j)
-            bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  brs, (lane * kPerLane + j) * 4, 0, 0));
-        f32x4 sum = part[0];
-#pragma unroll
-        for (int q = 1; q < kDecodeMaxSplits; ++q) sum += part[q];
+    // The first wave with no row of its own takes one pass over a dummy row
+    // through the same code: the finisher runs on a different CU from call
+    // to call, so its routing code is usually not in that CU's instruction
+    // cache, and this wave, running ahead, fetches it while the row waves
+    // are still polling.  (One wave only: dummy passes share SIMDs with the
+    // real rows.)
+    const int my_rows = wave < nrows ? (nrows - wave + kWaves - 1) / kWaves : 0;
+    const int passes = my_rows > 0 ? my_rows : (wave == nrows ? 1 : 0);
+    for (int it = 0; it < passes; ++it) {
+        const int t = wave + it * kWaves;
+        const bool real = t < nrows;  // wave-uniform
         float v[kPerLane];
+        float bv[kPerLane] = {0.f, 0.f, 0.f, 0.f};
+        if (real) {
+            const int off = ((t0 + t) * kMaxE + lane * kPerLane) * 4;
+            // Splits q >= S lie past the end of the buffer range: their loads
+            // return zeros and their stores are dropped, so no branch on S.
+            // The wait ends once the publishers' stores land; the time limit is
+            // only a guard so that no wave can spin forever: a row that hits it
+            // is reported as index -1 with a NaN weight.
+            f32x4 sum;
+            const uint64_t t_poll = __builtin_amdgcn_s_memrealtime();
+            bool gave_up = false;
+            if constexpr (kMaxS <= 8) {
+                // Two polls stay in flight, half a round trip apart, so a
+                // partial that lands is seen about a quarter round trip
+                // sooner on average.  (At 16 splits the second poll's
+                // registers would spill.)
+                f32x4 p0[kMaxS], p1[kMaxS];
+                poll_issue<kMaxS>(p0, prs, off, qstride);
+                __builtin_amdgcn_s_sleep(kPollGap);
+                for (;;) {
+                    poll_issue<kMaxS>(p1, prs, off, qstride);
+                    if (poll_ready<kMaxS>(p0, mine)) {
+                        sum = poll_sum<kMaxS>(p0);
+                        break;
+                    }
+                    poll_issue<kMaxS>(p0, prs, off, qstride);
+                    if (poll_ready<kMaxS>(p1, mine)) {
+                        sum = poll_sum<kMaxS>(p1);
+                        break;
+                    }
+                    if (__builtin_amdgcn_s_memrealtime() - t_poll > kDecodePollLimitTicks) {
+                        gave_up = true;
+                        break;
+                    }
+                }
+            } else {
+                f32x4 p0[kMaxS];
+                for (;;) {
+                    poll_issue<kMaxS>(p0, prs, off, qstride);
+                    if (poll_ready<kMaxS>(p0, mine)) {
+                        sum = poll_sum<kMaxS>(p0);
+                        break;
+                    }
+                    if (__builtin_amdgcn_s_memrealtime() - t_poll > kDecodePollLimitTicks) {
+                        gave_up = true;
+                        break;
+                    }
+                }
+            }
+            if (gave_up) {
+                if (lane < a.k) {
+                    const int64_t o = (int64_t)(t0 + t) * a.k + lane;
+                    a.inds[o] = -1;
+                    a.weights[o] = __builtin_nanf("");
+                    if (a.table_ids) slots[t * a.k + lane] = -1;
+                }
+                continue;
+            }
+            if (mine) {
 #pragma unroll
-        for (int j = 0; j < kPerLane; ++j) v[j] = (lane * kPerLane + j < a.E) ? sum[j] : 0.f;
-        if (a.logits_out) {
-            float* lo = a.logits_out + (int64_t)(t0 + t) * a.E + lane * kPerLane;
+                for (int q = 0; q < kMaxS; ++q) publish4(prs, off + q * qstride, sentinel4);
+            }
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
-                if (lane * kPerLane + j < a.E) lo[j] = v[j];
+                bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      brs, (lane * kPerLane + j) * 4, 0, 0));
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) v[j] = (lane * kPerLane + j < a.E) ? sum[j] : 0.f;
+            if (a.logits_out) {
+                float* lo = a.logits_out + (int64_t)(t0 + t) * a.E + lane * kPerLane;
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j)
+                    if (lane * kPerLane + j < a.E) lo[j] = v[j];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) v[j] = 0.0625f * (float)(lane * kPerLane + j);
         }
         const RowResult res = route_row(v, bv, spec);
+        if (!real) {
+            asm volatile("; dummy row %0 %1" :: "v"(res.idx), "v"(res.w));  // keep the pass
+            continue;
+        }
         if (lane < a.k) {
             const int64_t o = (int64_t)(t0 + t) * a.k + lane;
             a.inds[o] = res.idx;
@@ -230,7 +319,15 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream)
     const int R = (a.M + kDecodeTile - 1) / kDecodeTile;
     const int B = (a.E + kDecodeTile - 1) / kDecodeTile;
     const int grid = R * B * a.S;
-    hipLaunchKernelGGL(decode_router_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+    if (a.load_waves == kDecodeNarrow.load_waves && a.S <= kDecodeNarrow.max_splits) {
+        hipLaunchKernelGGL((decode_router_kernel<kDecodeNarrow.load_waves, kDecodeNarrow.max_splits>),
+                           dim3(grid), dim3((kDecodeNarrow.load_waves + 1) * kWave), 0, stream, a);
+    } else if (a.load_waves == kDecodeWide.load_waves && a.S <= kDecodeWide.max_splits) {
+        hipLaunchKernelGGL((decode_router_kernel<kDecodeWide.load_waves, kDecodeWide.max_splits>),
+                           dim3(grid), dim3((kDecodeWide.load_waves + 1) * kWave), 0, stream, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

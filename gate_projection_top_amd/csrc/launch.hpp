@@ -30,9 +30,10 @@ struct DecodeLaunch {
     int32_t* table_s2u;
     int32_t* table_count;
     float* partials;        // workspace [S][M][256], every slot kDecodeSentinel between calls
-    uint32_t* counters;     // workspace [R], zero between calls
+    uint32_t* counters;     // workspace, kDecodeCounters words, zero between calls
     int S;                  // H splits
     int ks_per_split;       // 32-wide k-steps per split
+    int load_waves;         // geometry: 4 (kDecodeNarrow) or 8 (kDecodeWide)
 };
 
 struct PrefillLaunch {
@@ -58,20 +59,40 @@ int prefill_splits(int64_t M);
 
 // Decode geometry shared by the host (workspace sizing) and the launcher.
 constexpr int kDecodeTile = 16;        // rows per row block, experts per expert block
-constexpr int kDecodeMaxSplits = 16;   // H splits
+constexpr int kDecodeMaxSplits = 16;   // H splits (either geometry)
 constexpr int kDecodeMaxM = 64;
 constexpr int kDecodeMaxRowBlocks = kDecodeMaxM / kDecodeTile;
-constexpr int kDecodeWaves = 8;                // load waves per workgroup (plus one control wave)
+constexpr int kDecodeMaxBlocks = 256 / kDecodeTile;  // expert blocks at E = 256
+// Arrival counters, one 64-byte line apart: per (row block, expert block),
+// then per row block.
+constexpr int kDecodeCounterStride = 16;
+constexpr int kDecodeCounters =
+    kDecodeCounterStride * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + kDecodeMaxRowBlocks);
 // Empty decode partial slot: a signalling NaN, a pattern no arithmetic
 // result has (NaN results are quiet).
 constexpr uint32_t kDecodeSentinel = 0x7f800001u;
 // Guard on the finisher's wait for published partials (100 MHz realtime
 // clock): 100 ms, orders of magnitude above any real wait.
 constexpr uint64_t kDecodePollLimitTicks = 10000000u;
-// Workgroups a decode launch aims for.  Fewer than one per CU: every
-// workgroup's loads still fit in one round trip to HBM, and fewer arrivals
-// queue on the row block's counter.
-constexpr int kDecodeTargetWorkgroups = 128;
+
+// Two decode geometries.  A row block with at most kDecodeNarrowMaxRows
+// tokens takes about 256 workgroups of 4 load waves: more CUs pull W (each
+// CU keeps only so many misses in flight) and the finisher has few rows to
+// route.  More rows take about 128 workgroups of 8 load waves, so the
+// finisher has enough waves to route 16 rows.  Each workgroup also has one
+// control wave.
+struct DecodeGeometry {
+    int load_waves;
+    int target_workgroups;
+    int max_splits;
+};
+constexpr DecodeGeometry kDecodeNarrow{4, 256, 16};
+constexpr DecodeGeometry kDecodeWide{8, 128, 8};
+constexpr int kDecodeNarrowMaxRows = 4;
+inline DecodeGeometry decode_geometry(int M)
+{
+    return M <= kDecodeNarrowMaxRows ? kDecodeNarrow : kDecodeWide;
+}
 
 // Prefill geometry: 128-row tiles; K split S ways while tiles * S <= 256.
 constexpr int kPrefillTileRows = 128;

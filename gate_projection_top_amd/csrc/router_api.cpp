@@ -12,7 +12,7 @@ namespace {
 
 struct DeviceWorkspace {
     float* partials = nullptr;          // decode H-split partial logits [S][M][256], sentinel-filled
-    uint32_t* counters = nullptr;       // decode arrival counters, one per row block
+    uint32_t* counters = nullptr;       // decode arrival counters (two levels)
     float* pf_partials = nullptr;       // prefill split partials [tile][S][128][256]
     uint32_t* pf_counters = nullptr;    // prefill per-tile counters
 };
@@ -20,7 +20,7 @@ struct DeviceWorkspace {
 constexpr int kMaxDevices = 64;
 constexpr size_t kPartialFloats =
     (size_t)gpt::kDecodeMaxSplits * gpt::kDecodeMaxM * ROUTER_MAX_E;  // 1 MiB
-constexpr int kCounters = 64;
+constexpr int kCounters = gpt::kDecodeCounters;
 constexpr size_t kPfPartialFloats =
     (size_t)gpt::kPrefillMaxPairs * gpt::kPrefillTileRows * ROUTER_MAX_E;  // 32 MiB
 constexpr size_t kPfCounters = (size_t)gpt::kPrefillMaxSplitTiles * gpt::kPrefillCountersPerTile;
@@ -99,21 +99,23 @@ int check_projection(const void* x, const void* w)
     return ROUTER_OK;
 }
 
-// Decode split choice: about kDecodeTargetWorkgroups workgroups, with at
-// least one 32-wide k-step per wave in every split.
-void decode_splits(int M, int H, int E, int* S_out, int* ks_per_split_out)
+// Decode split choice: about the geometry's target workgroup count, with at
+// least one 32-wide k-step per load wave in every split.
+void decode_splits(int M, int H, int E, int* S_out, int* ks_per_split_out, int* load_waves_out)
 {
+    const gpt::DecodeGeometry g = gpt::decode_geometry(M);
     const int R = (M + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int B = (E + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int KS = (H + 31) / 32;
-    int S = (gpt::kDecodeTargetWorkgroups + R * B - 1) / (R * B);
-    const int by_work = KS / gpt::kDecodeWaves > 1 ? KS / gpt::kDecodeWaves : 1;
+    int S = (g.target_workgroups + R * B - 1) / (R * B);
+    const int by_work = KS / g.load_waves > 1 ? KS / g.load_waves : 1;
     if (S > by_work) S = by_work;
-    if (S > gpt::kDecodeMaxSplits) S = gpt::kDecodeMaxSplits;
+    if (S > g.max_splits) S = g.max_splits;
     if (S < 1) S = 1;
     const int per = (KS + S - 1) / S;
     *ks_per_split_out = per;
     *S_out = (KS + per - 1) / per;
+    *load_waves_out = g.load_waves;
 }
 
 int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
@@ -145,7 +147,7 @@ int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H,
         a.table_count = t_count;
         a.partials = ws.partials;
         a.counters = ws.counters;
-        decode_splits((int)M, H, E, &a.S, &a.ks_per_split);
+        decode_splits((int)M, H, E, &a.S, &a.ks_per_split, &a.load_waves);
         e = gpt::launch_decode(a, stream);
     } else {
         gpt::PrefillLaunch a{};
