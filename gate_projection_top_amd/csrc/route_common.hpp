@@ -62,33 +62,28 @@ __device__ __forceinline__ double dpp_f64(double v)
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// One butterfly step of an unsigned max: the DPP source lane's value, with 0
+// (the identity of max) where the pattern leaves a lane unwritten, so the
+// compiler folds the move into a single v_max_u32_dpp.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t max_step_u32(uint32_t v)
+{
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false));
+}
+
 // Wave-wide max: butterfly inside each 16-lane row, then DPP row_bcast:15
 // (rows 1 and 3 take lane 15 of the row below) and row_bcast:31 (rows 2 and 3
 // take lane 31), which leaves the maximum of all 64 lanes in lane 63; one
 // readlane makes it wave-uniform.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    v = max(v, dpp_u32<0xB1>(v));
-    v = max(v, dpp_u32<0x4E>(v));
-    v = max(v, dpp_u32<0x124>(v));
-    v = max(v, dpp_u32<0x128>(v));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+    v = max_step_u32<0xB1>(v);
+    v = max_step_u32<0x4E>(v);
+    v = max_step_u32<0x124>(v);
+    v = max_step_u32<0x128>(v);
+    v = max_step_u32<0x142, 0xA>(v);
+    v = max_step_u32<0x143, 0xC>(v);
     return readlane_u32(v, 63);
-}
-
-__device__ __forceinline__ float wave_max_f32(float f)
-{
-    uint32_t v = __float_as_uint(f);
-    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0xB1>(v))));
-    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x4E>(v))));
-    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x124>(v))));
-    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp_u32<0x128>(v))));
-    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
-                                                      (int)v, (int)v, 0x142, 0xA, 0xF, false))));
-    v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(
-                                                      (int)v, (int)v, 0x143, 0xC, 0xF, false))));
-    return __uint_as_float(readlane_u32(v, 63));
 }
 
 // Sum over the wavefront in a fixed association: the 16-lane row sums are
@@ -178,11 +173,13 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
     double sc[kPerLane] = {0.0, 0.0, 0.0, 0.0};
     if (need_all) {
         if (softmax) {
-            float m = -__builtin_inff();
+            // the row max through order codes (a max of -0 comes back as
+            // +0, which shifts every exponent by exactly the same zero)
+            uint32_t m = 0u;
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
-                if (valid[j]) m = fmaxf(m, v[j]);
-            mx = wave_max_f32(m);
+                if (valid[j]) m = max(m, order_code(v[j]));
+            mx = order_value(wave_max_u32(m));
             double z[kPerLane];
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
@@ -214,6 +211,9 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
     order_pair(c[0], slot[0], c[2], slot[2]);
     order_pair(c[1], slot[1], c[3], slot[3]);
     order_pair(c[1], slot[1], c[2], slot[2]);
+    // the four slots in selection order, two bits each, head in the low bits
+    uint32_t slots = (uint32_t)slot[0] | ((uint32_t)slot[1] << 2) | ((uint32_t)slot[2] << 4) |
+                     ((uint32_t)slot[3] << 6);
 
     // k rounds: the wave-wide largest head wins; among equal heads the lowest
     // lane, whose head is its lowest-slot entry of that code, i.e. the lowest
@@ -224,19 +224,17 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
         const uint32_t top = wave_max_u32(c[0]);
         const uint64_t hit = __builtin_amdgcn_ballot_w64(c[0] == top);
         const int L = (int)__builtin_ctzll(hit);
-        const int wslot = __builtin_amdgcn_readlane(slot[0], L);
+        const int wslot = (int)(readlane_u32(slots, L) & 3u);
         if (lane == it) {
             my_idx = L * kPerLane + wslot;
             my_code = top;
         }
         const bool pop = lane == L;
         c[0] = pop ? c[1] : c[0];
-        slot[0] = pop ? slot[1] : slot[0];
         c[1] = pop ? c[2] : c[1];
-        slot[1] = pop ? slot[2] : slot[1];
         c[2] = pop ? c[3] : c[2];
-        slot[2] = pop ? slot[3] : slot[2];
         c[3] = pop ? 0u : c[3];
+        slots = pop ? slots >> 2 : slots;
     }
 
     // Winner logits: the key itself without a bias; otherwise fetched from the
