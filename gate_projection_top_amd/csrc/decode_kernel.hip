@@ -48,14 +48,14 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float not_sentinel(float v)
 {
     // a quiet NaN stands in for the (never produced) sentinel pattern
-    return __float_as_uint(v) == kDecodeSentinel ? __uint_as_float(0x7fc00000u) : v;
+    return __float_as_uint(v) == kPartialSentinel ? __uint_as_float(0x7fc00000u) : v;
 }
 
 __device__ __forceinline__ bool published(f32x4 v)
 {
     // bitwise, not short-circuit: one compare per value, no branches
-    return (__float_as_uint(v[0]) != kDecodeSentinel) & (__float_as_uint(v[1]) != kDecodeSentinel) &
-           (__float_as_uint(v[2]) != kDecodeSentinel) & (__float_as_uint(v[3]) != kDecodeSentinel);
+    return (__float_as_uint(v[0]) != kPartialSentinel) & (__float_as_uint(v[1]) != kPartialSentinel) &
+           (__float_as_uint(v[2]) != kPartialSentinel) & (__float_as_uint(v[3]) != kPartialSentinel);
 }
 
 // One poll: every split's slot of this lane's four experts.  Splits q >= S
@@ -196,8 +196,8 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     const int nrows = min(kDecodeTile, a.M - t0);
     const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};
     const bool mine = lane < 4 * B;  // the lane's expert group lies in a published block
-    const f32x4 sentinel4 = __builtin_bit_cast(f32x4, u32x4{kDecodeSentinel, kDecodeSentinel,
-                                                            kDecodeSentinel, kDecodeSentinel});
+    const f32x4 sentinel4 = __builtin_bit_cast(f32x4, u32x4{kPartialSentinel, kPartialSentinel,
+                                                            kPartialSentinel, kPartialSentinel});
     // bias beyond E reads as 0 (out-of-range buffer loads return zero)
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);

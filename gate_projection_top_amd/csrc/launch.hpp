@@ -29,7 +29,7 @@ struct DecodeLaunch {
     int32_t* table_mask;
     int32_t* table_s2u;
     int32_t* table_count;
-    float* partials;        // workspace [S][M][256], every slot kDecodeSentinel between calls
+    float* partials;        // workspace [S][M][256], every slot kPartialSentinel between calls
     uint32_t* counters;     // workspace, kDecodeCounters words, zero between calls
     int S;                  // H splits
     int ks_per_split;       // 32-wide k-steps per split
@@ -70,7 +70,7 @@ constexpr int kDecodeCounters =
     kDecodeCounterStride * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + kDecodeMaxRowBlocks);
 // Empty decode partial slot: a signalling NaN, a pattern no arithmetic
 // result has (NaN results are quiet).
-constexpr uint32_t kDecodeSentinel = 0x7f800001u;
+constexpr uint32_t kPartialSentinel = 0x7f800001u;
 // Guard on the finisher's wait for published partials (100 MHz realtime
 // clock): 100 ms, orders of magnitude above any real wait.
 constexpr uint64_t kDecodePollLimitTicks = 10000000u;

@@ -155,8 +155,15 @@ __device__ __forceinline__ void order_pair(uint32_t& ca, int& ia, uint32_t& cb, 
 
 // Route one row.  v[j]: logit of expert 4*lane+j (ignored when >= E);
 // bv[j]: its selection bias (used only when s.has_bias).
-__device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
-                                               const float (&bv)[kPerLane], const RowSpec& s)
+// Routes N rows at once, in lockstep: every step below runs for each row in
+// turn, so the N rows' dependency chains (DPP reductions, readlanes, f64
+// arithmetic) interleave and a wave issues instructions while one row waits.
+// kNeedAll: scores for every expert are needed (they form the key, or a
+// softmax weight is the full-row probability); the two cases compile apart.
+template <int N, bool kNeedAll>
+__device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
+                                                const float (&bv)[kPerLane], const RowSpec& s,
+                                                RowResult (&out)[N])
 {
     const int lane = threadIdx.x & (kWave - 1);
     bool valid[kPerLane];
@@ -164,14 +171,193 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
     for (int j = 0; j < kPerLane; ++j) valid[j] = (lane * kPerLane + j) < s.E;
 
     const bool softmax = s.scoring == kSoftmax;
-    // Scores for every expert are needed only when they form the key or when
-    // a softmax weight is the full-row probability.
-    const bool need_all = s.has_bias || (softmax && !s.renorm);
+    constexpr bool need_all = kNeedAll;
+
+    float mx[N];                 // softmax shift: the row's largest logit
+    double Z[N];
+    double sc[N][kPerLane];      // scores: the key's first term
+    double un[N][kPerLane];      // unbiased scores: the weights' terms
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        mx[n] = 0.0f;
+        Z[n] = 1.0;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) sc[n][j] = un[n][j] = 0.0;
+    }
+    if constexpr (need_all) {
+        if (softmax) {
+            // the row max through order codes (a max of -0 comes back as
+            // +0, which shifts every exponent by exactly the same zero)
+            uint32_t m[N];
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                m[n] = 0u;
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j)
+                    if (valid[j]) m[n] = max(m[n], order_code(v[n][j]));
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) mx[n] = order_value(wave_max_u32(m[n]));
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j)
+                    un[n][j] = valid[j] ? exp((double)v[n][j] - (double)mx[n]) : 0.0;
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+                Z[n] = wave_sum_f64(((un[n][0] + un[n][1]) + un[n][2]) + un[n][3]);
+            // z * (1/Z): within an ulp of z / Z in double, so its rounding
+            // to fp32 (all the key keeps) agrees but for ~1e-8 of values
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const double rZ = 1.0 / Z[n];
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j) sc[n][j] = un[n][j] * rZ;
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j) {
+                    sc[n][j] = valid[j] ? sqrt_softplus(v[n][j]) : 0.0;
+                    un[n][j] = sc[n][j];
+                }
+        }
+    }
+
+    // Selection codes, then each lane's four entries in selection order.
+    uint32_t c[N][kPerLane];
+    uint32_t slots[N];  // the four slots in selection order, two bits each, head lowest
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        int slot[kPerLane];
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            float key = v[n][j];
+            if (s.has_bias) {
+                const float s32 = (float)sc[n][j];
+                key = s32 + bv[j];
+            }
+            c[n][j] = valid[j] ? order_code(key) : 0u;
+            slot[j] = j;
+        }
+        order_pair(c[n][0], slot[0], c[n][1], slot[1]);
+        order_pair(c[n][2], slot[2], c[n][3], slot[3]);
+        order_pair(c[n][0], slot[0], c[n][2], slot[2]);
+        order_pair(c[n][1], slot[1], c[n][3], slot[3]);
+        order_pair(c[n][1], slot[1], c[n][2], slot[2]);
+        slots[n] = (uint32_t)slot[0] | ((uint32_t)slot[1] << 2) | ((uint32_t)slot[2] << 4) |
+                   ((uint32_t)slot[3] << 6);
+    }
+
+    // k rounds: the wave-wide largest head wins; among equal heads the lowest
+    // lane, whose head is its lowest-slot entry of that code, i.e. the lowest
+    // expert index.  The winning lane pops its head.
+    int my_idx[N];
+    uint32_t my_code[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        my_idx[n] = 0;
+        my_code[n] = 0u;
+    }
+    for (int it = 0; it < s.k; ++it) {
+        uint32_t top[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) top[n] = wave_max_u32(c[n][0]);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(c[n][0] == top[n]);
+            const int L = (int)__builtin_ctzll(hit);
+            const int wslot = (int)(readlane_u32(slots[n], L) & 3u);
+            if (lane == it) {
+                my_idx[n] = L * kPerLane + wslot;
+                my_code[n] = top[n];
+            }
+            const bool pop = lane == L;
+            c[n][0] = pop ? c[n][1] : c[n][0];
+            c[n][1] = pop ? c[n][2] : c[n][1];
+            c[n][2] = pop ? c[n][3] : c[n][2];
+            c[n][3] = pop ? 0u : c[n][3];
+            slots[n] = pop ? slots[n] >> 2 : slots[n];
+        }
+    }
+
+    // The winners' unbiased scores.  When every score was computed above,
+    // fetch the winner's from the lane that holds it; otherwise compute it
+    // from the winner's logit (the key itself, since there is no bias).
+    double u[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        u[n] = 0.0;
+        if constexpr (need_all) {
+            const int src = (my_idx[n] >> 2) << 2;  // byte address of the owning lane
+            const int j = my_idx[n] & 3;
+            double got[kPerLane];
+#pragma unroll
+            for (int q = 0; q < kPerLane; ++q) {
+                const uint64_t bits = __builtin_bit_cast(uint64_t, un[n][q]);
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)bits);
+                const uint32_t hi =
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(bits >> 32));
+                got[q] = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+            }
+            u[n] = j == 0 ? got[0] : (j == 1 ? got[1] : (j == 2 ? got[2] : got[3]));
+            if (lane >= s.k) u[n] = 0.0;
+        } else {
+            if (softmax) mx[n] = order_value(readlane_u32(my_code[n], 0));  // rank 0 holds the max
+            if (lane < s.k) {
+                const float my_logit = order_value(my_code[n]);
+                u[n] = softmax ? exp((double)my_logit - (double)mx[n]) : sqrt_softplus(my_logit);
+            }
+        }
+    }
+    // The bias never enters the weights.
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        float w;
+        if (s.renorm) {
+            double total = 0.0;
+            for (int j = 0; j < s.k; ++j) total += readlane_f64(u[n], j);
+            w = (float)(u[n] / total);
+        } else {
+            w = softmax ? (float)(u[n] / Z[n]) : (float)u[n];
+        }
+        out[n] = RowResult{my_idx[n], w};
+    }
+}
+
+// N rows in lockstep (same spec); rows n carry logits v[n] and get out[n].
+template <int N>
+__device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const float (&bv)[kPerLane],
+                                           const RowSpec& s, RowResult (&out)[N])
+{
+    const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
+    if (need_all)
+        route_rows_impl<N, true>(v, bv, s, out);
+    else
+        route_rows_impl<N, false>(v, bv, s, out);
+}
+
+// One row: the same steps as route_rows, written for a single row (the
+// generic form costs the single-row decode path ~0.3 us of latency).  The
+// two give bit-identical results on identical inputs.
+template <bool kNeedAll>
+__device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
+                                                    const float (&bv)[kPerLane], const RowSpec& s)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    bool valid[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) valid[j] = (lane * kPerLane + j) < s.E;
+
+    const bool softmax = s.scoring == kSoftmax;
+    constexpr bool need_all = kNeedAll;
 
     float mx = 0.0f;  // softmax shift: the row's largest logit
     double Z = 1.0;
-    double sc[kPerLane] = {0.0, 0.0, 0.0, 0.0};
-    if (need_all) {
+    double sc[kPerLane] = {0.0, 0.0, 0.0, 0.0};  // scores: the key's first term
+    double un[kPerLane] = {0.0, 0.0, 0.0, 0.0};  // unbiased scores: the weights' terms
+    if constexpr (need_all) {
         if (softmax) {
             // the row max through order codes (a max of -0 comes back as
             // +0, which shifts every exponent by exactly the same zero)
@@ -180,16 +366,20 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
             for (int j = 0; j < kPerLane; ++j)
                 if (valid[j]) m = max(m, order_code(v[j]));
             mx = order_value(wave_max_u32(m));
-            double z[kPerLane];
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
-                z[j] = valid[j] ? exp((double)v[j] - (double)mx) : 0.0;
-            Z = wave_sum_f64(((z[0] + z[1]) + z[2]) + z[3]);
+                un[j] = valid[j] ? exp((double)v[j] - (double)mx) : 0.0;
+            Z = wave_sum_f64(((un[0] + un[1]) + un[2]) + un[3]);
+            // z * (1/Z): within an ulp of z / Z in double, so its rounding
+            // to fp32 (all the key keeps) agrees but for ~1e-8 of values
+            const double rZ = 1.0 / Z;
 #pragma unroll
-            for (int j = 0; j < kPerLane; ++j) sc[j] = z[j] / Z;
+            for (int j = 0; j < kPerLane; ++j) sc[j] = un[j] * rZ;
         } else {
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j) sc[j] = valid[j] ? sqrt_softplus(v[j]) : 0.0;
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) un[j] = sc[j];
         }
     }
 
@@ -237,25 +427,31 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
         slots = pop ? slots >> 2 : slots;
     }
 
-    // Winner logits: the key itself without a bias; otherwise fetched from the
-    // lane that holds the expert.
-    float my_logit;
-    if (!s.has_bias) {
-        my_logit = order_value(my_code);
-        if (softmax && !need_all) mx = order_value(readlane_u32(my_code, 0));  // rank 0 holds the max
-    } else {
-        const int src = (my_idx >> 2) << 2;  // byte address of the owning lane
-        const float f0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[0])));
-        const float f1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[1])));
-        const float f2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[2])));
-        const float f3 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v[3])));
-        const int j = my_idx & 3;
-        my_logit = j == 0 ? f0 : (j == 1 ? f1 : (j == 2 ? f2 : f3));
-    }
-
-    // Weights from the unbiased scores; the bias never enters here.
+    // The winners' unbiased scores.  When every score was computed above,
+    // fetch the winner's from the lane that holds it; otherwise compute it
+    // from the winner's logit (the key itself, since there is no bias).
     double u = 0.0;
-    if (lane < s.k) u = softmax ? exp((double)my_logit - (double)mx) : sqrt_softplus(my_logit);
+    if constexpr (need_all) {
+        const int src = (my_idx >> 2) << 2;  // byte address of the owning lane
+        const int j = my_idx & 3;
+        double got[kPerLane];
+#pragma unroll
+        for (int q = 0; q < kPerLane; ++q) {
+            const uint64_t bits = __builtin_bit_cast(uint64_t, un[q]);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)bits);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(bits >> 32));
+            got[q] = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+        }
+        u = j == 0 ? got[0] : (j == 1 ? got[1] : (j == 2 ? got[2] : got[3]));
+        if (lane >= s.k) u = 0.0;
+    } else {
+        if (softmax) mx = order_value(readlane_u32(my_code, 0));  // rank 0 holds the max
+        if (lane < s.k) {
+            const float my_logit = order_value(my_code);
+            u = softmax ? exp((double)my_logit - (double)mx) : sqrt_softplus(my_logit);
+        }
+    }
+    // The bias never enters the weights.
     float w;
     if (s.renorm) {
         double total = 0.0;
@@ -265,6 +461,13 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
         w = softmax ? (float)(u / Z) : (float)u;
     }
     return RowResult{my_idx, w};
+}
+
+__device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
+                                               const float (&bv)[kPerLane], const RowSpec& s)
+{
+    const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
+    return need_all ? route_row_impl<true>(v, bv, s) : route_row_impl<false>(v, bv, s);
 }
 
 // ---------------------------------------------------------------------------

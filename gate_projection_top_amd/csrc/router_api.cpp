@@ -47,7 +47,7 @@ int init_device(int dev)
     if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_partials, kPfPartialFloats * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_counters, kPfCounters * sizeof(uint32_t));
     if (e == hipSuccess)
-        e = hipMemsetD32((hipDeviceptr_t)ws.partials, (int)gpt::kDecodeSentinel, kPartialFloats);
+        e = hipMemsetD32((hipDeviceptr_t)ws.partials, (int)gpt::kPartialSentinel, kPartialFloats);
     if (e == hipSuccess) e = hipMemset(ws.counters, 0, kCounters * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(ws.pf_counters, 0, kPfCounters * sizeof(uint32_t));
     // The counters must read zero before any stream (blocking or not) runs a
