@@ -208,6 +208,19 @@ def prefill_case(M: int = 8192, H: int = 7168, seed: int = 0, E: int = 256, k: i
     return RouterCase(x, w, bias, k, SOFTMAX, True, name=f"prefill/M{M}/H{H}/seed{seed}")
 
 
+def shape_case(M: int, H: int, E: int, k: int, scoring: int, with_bias: bool, renorm: bool,
+               seed: int = 0) -> RouterCase:
+    """Any shape within the limits: X ~ N(0,1), W ~ N(0,1/H) in bf16, and a
+    U(-0.05,0.05) selection bias when asked for (edge-case and sweep tests)."""
+    rng = _rng(seed, 8)
+    x = gaussian_bf16(rng, (M, H), 1.0)
+    w = gaussian_bf16(rng, (E, H), 1.0 / np.sqrt(H))
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32) if with_bias else None
+    name = (f"shape/M{M}/H{H}/E{E}/k{k}/{'sm' if scoring == SOFTMAX else 'ssp'}"
+            f"/{'bias' if with_bias else 'nobias'}/{'renorm' if renorm else 'raw'}/seed{seed}")
+    return RouterCase(x, w, bias, k, scoring, renorm, name=name)
+
+
 def metric_case(seed: int = 0) -> RouterCase:
     """Single-token decode at H=7168 (the latency headline shape)."""
     c = decode_case(1, H=7168, seed=seed)
