@@ -33,7 +33,7 @@ struct DecodeLaunch {
     uint32_t* counters;     // workspace, kDecodeCounters words, zero between calls
     int S;                  // H splits
     int ks_per_split;       // 32-wide k-steps per split
-    int load_waves;         // geometry: 4 (kDecodeNarrow) or 8 (kDecodeWide)
+    int load_waves;         // geometry: kDecodeNarrow.load_waves or kDecodeWide.load_waves
 };
 
 struct PrefillLaunch {
@@ -76,17 +76,18 @@ constexpr uint32_t kPartialSentinel = 0x7f800001u;
 constexpr uint64_t kDecodePollLimitTicks = 10000000u;
 
 // Two decode geometries.  A row block with at most kDecodeNarrowMaxRows
-// tokens takes about 256 workgroups of 4 load waves: more CUs pull W (each
-// CU keeps only so many misses in flight) and the finisher has few rows to
-// route.  More rows take about 128 workgroups of 8 load waves, so the
-// finisher has enough waves to route 16 rows.  Each workgroup also has one
-// control wave.
+// tokens takes about 256 workgroups of 3 load waves: more CUs pull W (each
+// CU keeps only so many misses in flight), fewer waves to dispatch, and the
+// finisher has few rows to route.  More rows take about 128 workgroups of 8
+// load waves, so the finisher has enough waves to route 16 rows.  Each
+// workgroup also has one control wave (which routes a row too).  Sweeps of
+// 2/3/4 and 4/8/16 load waves and 64/128/256 workgroups chose these.
 struct DecodeGeometry {
     int load_waves;
     int target_workgroups;
     int max_splits;
 };
-constexpr DecodeGeometry kDecodeNarrow{4, 256, 16};
+constexpr DecodeGeometry kDecodeNarrow{3, 256, 16};
 constexpr DecodeGeometry kDecodeWide{8, 128, 8};
 constexpr int kDecodeNarrowMaxRows = 4;
 inline DecodeGeometry decode_geometry(int M)
