@@ -98,6 +98,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
 
     __shared__ float red[kLoadWaves][kDecodeTile][kDecodeTile + 1];
     __shared__ int32_t slots[2 * kMaxK];
+    __shared__ int polled[kDecodeTile];  // finisher: 1 = row's partials read, 2 = row gave up
     __shared__ int is_last;
 
     const int tid = threadIdx.x;
@@ -111,6 +112,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     const int b = bid % B;
     const int r = bid / B;
 
+    if (tid < kDecodeTile) polled[tid] = 0;
     if (wave == kLoadWaves) {
         // ---- control wave: the arrival ticket, in two levels so that no
         // counter sees more than max(S, B) arrivals: the last of an expert
@@ -207,9 +209,28 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     // to call, so its routing code is usually not in that CU's instruction
     // cache, and this wave, running ahead, fetches it while the row waves
     // are still polling.  (One wave only: dummy passes share SIMDs with the
-    // real rows.)
+    // real rows.)  The next free wave, if there is one, puts the sentinel
+    // back into each row's slots once the row's wave has read them, so the
+    // row waves go straight from their poll to routing.
     const int my_rows = wave < nrows ? (nrows - wave + kWaves - 1) / kWaves : 0;
     const int passes = my_rows > 0 ? my_rows : (wave == nrows ? 1 : 0);
+    const bool has_helper = nrows + 1 < kWaves;
+    if (has_helper && wave == nrows + 1) {
+        const uint64_t t_wait = __builtin_amdgcn_s_memrealtime();
+        for (int t = 0; t < nrows; ++t) {
+            int st;
+            // the row waves' own poll limit bounds this wait; the doubled
+            // limit here is only a guard
+            while ((st = __hip_atomic_load(&polled[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0 &&
+                   __builtin_amdgcn_s_memrealtime() - t_wait < 2 * kDecodePollLimitTicks)
+                __builtin_amdgcn_s_sleep(1);
+            if (st == 1 && mine) {
+                const int off = ((t0 + t) * kMaxE + lane * kPerLane) * 4;
+#pragma unroll
+                for (int q = 0; q < kMaxS; ++q) publish4(prs, off + q * qstride, sentinel4);
+            }
+        }
+    }
     for (int it = 0; it < passes; ++it) {
         const int t = wave + it * kWaves;
         const bool real = t < nrows;  // wave-uniform
@@ -264,6 +285,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                 }
             }
             if (gave_up) {
+                if (lane == 0) __hip_atomic_store(&polled[t], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 if (lane < a.k) {
                     const int64_t o = (int64_t)(t0 + t) * a.k + lane;
                     a.inds[o] = -1;
@@ -272,7 +294,9 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                 }
                 continue;
             }
-            if (mine) {
+            if (has_helper) {
+                if (lane == 0) __hip_atomic_store(&polled[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else if (mine) {
 #pragma unroll
                 for (int q = 0; q < kMaxS; ++q) publish4(prs, off + q * qstride, sentinel4);
             }
@@ -292,7 +316,9 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j) v[j] = 0.0625f * (float)(lane * kPerLane + j);
         }
-        const RowResult res = route_row(v, bv, spec);
+        // a routing wave has a SIMD to itself in the narrow geometry; the
+        // wide one puts two or three waves on each SIMD
+        const RowResult res = route_row<kLoadWaves + 1 <= 4 ? kRoundsLane : kRoundsScalar>(v, bv, spec);
         if (!real) {
             asm volatile("; dummy row %0 %1" :: "v"(res.idx), "v"(res.w));  // keep the pass
             continue;

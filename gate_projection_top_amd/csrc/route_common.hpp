@@ -31,9 +31,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // cross-lane primitives (full wavefront active)
 // ---------------------------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
-// row_ror:4 = 0x124, row_ror:8 = 0x128 (after these four steps every lane
-// holds the reduction over its 16-lane row), row_bcast:15 = 0x142 and
-// row_bcast:31 = 0x143 (carry a row's result into the rows above it).
+// row_ror:4 = 0x124, row_ror:8 = 0x128, row_mirror = 0x140 and
+// row_half_mirror = 0x141 (each moves data only inside a 16-lane row);
+// row_bcast:15 = 0x142 and row_bcast:31 = 0x143 carry a row's value into
+// the rows above it.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
@@ -62,28 +63,46 @@ __device__ __forceinline__ double dpp_f64(double v)
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// One butterfly step of an unsigned max: the DPP source lane's value, with 0
-// (the identity of max) where the pattern leaves a lane unwritten, so the
-// compiler folds the move into a single v_max_u32_dpp.
-template <int CTRL, int ROW_MASK = 0xF>
+// One butterfly step of an unsigned max against the DPP source lane's value;
+// the old value 0 (the identity of max) lets the compiler fold the move into
+// a single v_max_u32_dpp.
+template <int CTRL>
 __device__ __forceinline__ uint32_t max_step_u32(uint32_t v)
 {
-    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false));
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
 }
 
-// Wave-wide max: butterfly inside each 16-lane row, then DPP row_bcast:15
-// (rows 1 and 3 take lane 15 of the row below) and row_bcast:31 (rows 2 and 3
-// take lane 31), which leaves the maximum of all 64 lanes in lane 63; one
-// readlane makes it wave-uniform.
+// Wave-wide max in a scalar register: the butterfly inside each 16-lane row,
+// then DPP row_bcast:15 (rows 1 and 3 take lane 15 of the row below) and
+// row_bcast:31 (rows 2 and 3 take lane 31), which leaves the maximum of all
+// 64 lanes in lane 63, and one readlane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     v = max_step_u32<0xB1>(v);
     v = max_step_u32<0x4E>(v);
     v = max_step_u32<0x124>(v);
     v = max_step_u32<0x128>(v);
-    v = max_step_u32<0x142, 0xA>(v);
-    v = max_step_u32<0x143, 0xC>(v);
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
     return readlane_u32(v, 63);
+}
+
+// Wave-wide max delivered to every lane: the butterfly inside each 16-lane
+// row (quad_perm xor 1 and xor 2, row_half_mirror, then row_mirror and
+// row_ror:8 into two registers, which both end with the row max), then
+// gfx950's permlane16 and permlane32 swaps across rows.  Every lane can then
+// compare against the max without a readlane into a scalar register.
+__device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v)
+{
+    v = max_step_u32<0xB1>(v);
+    v = max_step_u32<0x4E>(v);
+    v = max_step_u32<0x141>(v);
+    const uint32_t a = max_step_u32<0x140>(v);
+    const uint32_t b = max_step_u32<0x128>(v);
+    const auto p = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    const uint32_t x = max((uint32_t)p[0], (uint32_t)p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)q[0], (uint32_t)q[1]);
 }
 
 // Sum over the wavefront in a fixed association: the 16-lane row sums are
@@ -153,6 +172,140 @@ __device__ __forceinline__ void order_pair(uint32_t& ca, int& ia, uint32_t& cb, 
     ia = i;
 }
 
+// One selection round's pop: the lane whose head equals the round's maximum
+// and that no lower lane matches.  mask: the lanes whose head equals it.
+__device__ __forceinline__ bool round_pop(uint32_t head, uint32_t top, uint64_t& mask)
+{
+    const bool eq = head == top;
+    mask = __builtin_amdgcn_ballot_w64(eq);
+    const uint32_t below =
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    return (eq ? below : 1u) == 0u;
+}
+
+// After the rounds: rank `lane` went to the lowest lane L of that round's
+// mask.  L's pops follow its selection order, so the position of the rank in
+// L's list of won ranks (`wins`, rank + 1 in 5-bit fields, pop order) picks
+// the slot out of L's selection order (`order`, 2-bit slots).
+__device__ __forceinline__ int round_winner(uint64_t my_mask, uint32_t wins, uint32_t order)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t lo = (uint32_t)my_mask, hi = (uint32_t)(my_mask >> 32);
+    const int L = lo ? __builtin_ctz(lo) : (hi ? 32 + __builtin_ctz(hi) : 0);
+    const uint32_t info = (uint32_t)__builtin_amdgcn_ds_bpermute(L << 2, (int)(wins | (order << 20)));
+    const uint32_t want = (uint32_t)lane + 1u;
+    uint32_t w = 0u;
+#pragma unroll
+    for (int q = 1; q < kPerLane; ++q) w = (((info >> (5 * q)) & 31u) == want) ? (uint32_t)q : w;
+    return L * kPerLane + (int)((info >> (20 + 2 * w)) & 3u);
+}
+
+// Sum of u over lanes 0..k-1 (k <= 16; lanes k.. hold +0) as a fixed tree
+// inside the first 16-lane row: partners xor 1, xor 2, then the mirrored
+// quad and the mirrored half.  Each step adds the same two values in both
+// partner lanes, so every lane of the row ends with the same bits.
+__device__ __forceinline__ double rank_sum(double u)
+{
+    u = u + dpp_f64<0xB1>(u);
+    u = u + dpp_f64<0x4E>(u);
+    u = u + dpp_f64<0x141>(u);
+    return u + dpp_f64<0x140>(u);
+}
+
+// Two ways to run the k selection rounds; they give bit-identical results.
+//   kRoundsLane: each round's maximum reaches every lane (wave_max_all_u32),
+//     the pop is decided with vector instructions only, and the winners'
+//     indices are resolved once after the last round.  The shortest chain of
+//     dependent steps per round: for a routing wave with a SIMD to itself.
+//   kRoundsScalar: the maximum and the winning lane pass through scalar
+//     registers (readlane, find-first-set).  Fewer vector instructions per
+//     round: for routing waves that share a SIMD.
+enum RoundStyle : int { kRoundsLane = 0, kRoundsScalar = 1 };
+
+template <RoundStyle kStyle>
+__device__ __forceinline__ uint32_t max_code(uint32_t v)
+{
+    if constexpr (kStyle == kRoundsLane)
+        return wave_max_all_u32(v);
+    else
+        return wave_max_u32(v);
+}
+
+// k rounds over N rows: the wave-wide largest head wins; among equal heads
+// the lowest lane, whose head is its lowest-slot entry of that code, i.e. the
+// lowest expert index.  The winning lane pops its head.  c[n]: the lane's
+// four codes in selection order; order[n]: their slots, two bits each, head
+// in the low bits.  Lane j < k ends with the index and code of rank j.
+template <int N, RoundStyle kStyle>
+__device__ __forceinline__ void select_rounds(uint32_t (&c)[N][kPerLane], const uint32_t (&order)[N],
+                                              int k, int (&my_idx)[N], uint32_t (&my_code)[N])
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if constexpr (kStyle == kRoundsLane) {
+        // lane `it` keeps round it's mask; each lane lists the ranks it won
+        uint64_t my_mask[N];
+        uint32_t wins[N], wshift[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            my_mask[n] = 0u;
+            my_code[n] = 0u;
+            wins[n] = 0u;
+            wshift[n] = 0u;
+        }
+        for (int it = 0; it < k; ++it) {
+            uint32_t top[N];
+#pragma unroll
+            for (int n = 0; n < N; ++n) top[n] = wave_max_all_u32(c[n][0]);
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                uint64_t m;
+                const bool pop = round_pop(c[n][0], top[n], m);
+                c[n][0] = pop ? c[n][1] : c[n][0];
+                c[n][1] = pop ? c[n][2] : c[n][1];
+                c[n][2] = pop ? c[n][3] : c[n][2];
+                c[n][3] = pop ? 0u : c[n][3];
+                wins[n] = pop ? wins[n] | ((uint32_t)(it + 1) << wshift[n]) : wins[n];
+                wshift[n] = pop ? wshift[n] + 5u : wshift[n];
+                if (lane == it) {
+                    my_mask[n] = m;
+                    my_code[n] = top[n];
+                }
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < N; ++n) my_idx[n] = round_winner(my_mask[n], wins[n], order[n]);
+    } else {
+        uint32_t slots[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            slots[n] = order[n];
+            my_idx[n] = 0;
+            my_code[n] = 0u;
+        }
+        for (int it = 0; it < k; ++it) {
+            uint32_t top[N];
+#pragma unroll
+            for (int n = 0; n < N; ++n) top[n] = wave_max_u32(c[n][0]);
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(c[n][0] == top[n]);
+                const int L = (int)__builtin_ctzll(hit);
+                const int wslot = (int)(readlane_u32(slots[n], L) & 3u);
+                if (lane == it) {
+                    my_idx[n] = L * kPerLane + wslot;
+                    my_code[n] = top[n];
+                }
+                const bool pop = lane == L;
+                c[n][0] = pop ? c[n][1] : c[n][0];
+                c[n][1] = pop ? c[n][2] : c[n][1];
+                c[n][2] = pop ? c[n][3] : c[n][2];
+                c[n][3] = pop ? 0u : c[n][3];
+                slots[n] = pop ? slots[n] >> 2 : slots[n];
+            }
+        }
+    }
+}
+
 // Route one row.  v[j]: logit of expert 4*lane+j (ignored when >= E);
 // bv[j]: its selection bias (used only when s.has_bias).
 // Routes N rows at once, in lockstep: every step below runs for each row in
@@ -160,7 +313,7 @@ __device__ __forceinline__ void order_pair(uint32_t& ca, int& ia, uint32_t& cb, 
 // arithmetic) interleave and a wave issues instructions while one row waits.
 // kNeedAll: scores for every expert are needed (they form the key, or a
 // softmax weight is the full-row probability); the two cases compile apart.
-template <int N, bool kNeedAll>
+template <int N, bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
                                                 const float (&bv)[kPerLane], const RowSpec& s,
                                                 RowResult (&out)[N])
@@ -197,7 +350,7 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
                     if (valid[j]) m[n] = max(m[n], order_code(v[n][j]));
             }
 #pragma unroll
-            for (int n = 0; n < N; ++n) mx[n] = order_value(wave_max_u32(m[n]));
+            for (int n = 0; n < N; ++n) mx[n] = order_value(max_code<kStyle>(m[n]));
 #pragma unroll
             for (int n = 0; n < N; ++n)
 #pragma unroll
@@ -250,37 +403,9 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
                    ((uint32_t)slot[3] << 6);
     }
 
-    // k rounds: the wave-wide largest head wins; among equal heads the lowest
-    // lane, whose head is its lowest-slot entry of that code, i.e. the lowest
-    // expert index.  The winning lane pops its head.
     int my_idx[N];
     uint32_t my_code[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        my_idx[n] = 0;
-        my_code[n] = 0u;
-    }
-    for (int it = 0; it < s.k; ++it) {
-        uint32_t top[N];
-#pragma unroll
-        for (int n = 0; n < N; ++n) top[n] = wave_max_u32(c[n][0]);
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(c[n][0] == top[n]);
-            const int L = (int)__builtin_ctzll(hit);
-            const int wslot = (int)(readlane_u32(slots[n], L) & 3u);
-            if (lane == it) {
-                my_idx[n] = L * kPerLane + wslot;
-                my_code[n] = top[n];
-            }
-            const bool pop = lane == L;
-            c[n][0] = pop ? c[n][1] : c[n][0];
-            c[n][1] = pop ? c[n][2] : c[n][1];
-            c[n][2] = pop ? c[n][3] : c[n][2];
-            c[n][3] = pop ? 0u : c[n][3];
-            slots[n] = pop ? slots[n] >> 2 : slots[n];
-        }
-    }
+    select_rounds<N, kStyle>(c, slots, s.k, my_idx, my_code);
 
     // The winners' unbiased scores.  When every score was computed above,
     // fetch the winner's from the lane that holds it; otherwise compute it
@@ -316,9 +441,7 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
     for (int n = 0; n < N; ++n) {
         float w;
         if (s.renorm) {
-            double total = 0.0;
-            for (int j = 0; j < s.k; ++j) total += readlane_f64(u[n], j);
-            w = (float)(u[n] / total);
+            w = (float)(u[n] / rank_sum(u[n]));
         } else {
             w = softmax ? (float)(u[n] / Z[n]) : (float)u[n];
         }
@@ -327,21 +450,21 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
 }
 
 // N rows in lockstep (same spec); rows n carry logits v[n] and get out[n].
-template <int N>
+template <int N, RoundStyle kStyle = kRoundsScalar>
 __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const float (&bv)[kPerLane],
                                            const RowSpec& s, RowResult (&out)[N])
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
     if (need_all)
-        route_rows_impl<N, true>(v, bv, s, out);
+        route_rows_impl<N, true, kStyle>(v, bv, s, out);
     else
-        route_rows_impl<N, false>(v, bv, s, out);
+        route_rows_impl<N, false, kStyle>(v, bv, s, out);
 }
 
 // One row: the same steps as route_rows, written for a single row (the
 // generic form costs the single-row decode path ~0.3 us of latency).  The
 // two give bit-identical results on identical inputs.
-template <bool kNeedAll>
+template <bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
                                                     const float (&bv)[kPerLane], const RowSpec& s)
 {
@@ -365,7 +488,7 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
                 if (valid[j]) m = max(m, order_code(v[j]));
-            mx = order_value(wave_max_u32(m));
+            mx = order_value(max_code<kStyle>(m));
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
                 un[j] = valid[j] ? exp((double)v[j] - (double)mx) : 0.0;
@@ -405,27 +528,13 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     uint32_t slots = (uint32_t)slot[0] | ((uint32_t)slot[1] << 2) | ((uint32_t)slot[2] << 4) |
                      ((uint32_t)slot[3] << 6);
 
-    // k rounds: the wave-wide largest head wins; among equal heads the lowest
-    // lane, whose head is its lowest-slot entry of that code, i.e. the lowest
-    // expert index.  The winning lane pops its head.
-    int my_idx = 0;
-    uint32_t my_code = 0u;
-    for (int it = 0; it < s.k; ++it) {
-        const uint32_t top = wave_max_u32(c[0]);
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(c[0] == top);
-        const int L = (int)__builtin_ctzll(hit);
-        const int wslot = (int)(readlane_u32(slots, L) & 3u);
-        if (lane == it) {
-            my_idx = L * kPerLane + wslot;
-            my_code = top;
-        }
-        const bool pop = lane == L;
-        c[0] = pop ? c[1] : c[0];
-        c[1] = pop ? c[2] : c[1];
-        c[2] = pop ? c[3] : c[2];
-        c[3] = pop ? 0u : c[3];
-        slots = pop ? slots >> 2 : slots;
-    }
+    uint32_t cc[1][kPerLane] = {{c[0], c[1], c[2], c[3]}};
+    const uint32_t ord[1] = {slots};
+    int idx1[1];
+    uint32_t code1[1];
+    select_rounds<1, kStyle>(cc, ord, s.k, idx1, code1);
+    const int my_idx = idx1[0];
+    const uint32_t my_code = code1[0];
 
     // The winners' unbiased scores.  When every score was computed above,
     // fetch the winner's from the lane that holds it; otherwise compute it
@@ -454,20 +563,19 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     // The bias never enters the weights.
     float w;
     if (s.renorm) {
-        double total = 0.0;
-        for (int j = 0; j < s.k; ++j) total += readlane_f64(u, j);
-        w = (float)(u / total);
+        w = (float)(u / rank_sum(u));
     } else {
         w = softmax ? (float)(u / Z) : (float)u;
     }
     return RowResult{my_idx, w};
 }
 
+template <RoundStyle kStyle = kRoundsLane>
 __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
                                                const float (&bv)[kPerLane], const RowSpec& s)
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
-    return need_all ? route_row_impl<true>(v, bv, s) : route_row_impl<false>(v, bv, s);
+    return need_all ? route_row_impl<true, kStyle>(v, bv, s) : route_row_impl<false, kStyle>(v, bv, s);
 }
 
 // ---------------------------------------------------------------------------

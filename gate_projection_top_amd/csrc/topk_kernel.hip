@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_from_logits_kernel(To
                 if (e < a.E) v[j] = r[e];
             }
         }
-        const RowResult res = route_row(v, bv, spec);
+        const RowResult res = route_row<kRoundsScalar>(v, bv, spec);  // several waves per SIMD
         if (lane < a.k) {
             a.inds[row * a.k + lane] = res.idx;
             a.weights[row * a.k + lane] = res.w;
