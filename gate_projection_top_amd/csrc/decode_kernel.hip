@@ -204,6 +204,8 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
 
+    // Rows go to the waves in turn starting at wave 1 (wave 0 has just spent
+    // its time on the publish, and the others reach this point first).
     // The first wave with no row of its own takes one pass over a dummy row
     // through the same code: the finisher runs on a different CU from call
     // to call, so its routing code is usually not in that CU's instruction
@@ -212,10 +214,11 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     // real rows.)  The next free wave, if there is one, puts the sentinel
     // back into each row's slots once the row's wave has read them, so the
     // row waves go straight from their poll to routing.
-    const int my_rows = wave < nrows ? (nrows - wave + kWaves - 1) / kWaves : 0;
-    const int passes = my_rows > 0 ? my_rows : (wave == nrows ? 1 : 0);
+    const int slot_of_wave = (wave + kWaves - 1) % kWaves;  // row t goes to wave (t + 1) % kWaves
+    const int my_rows = slot_of_wave < nrows ? (nrows - slot_of_wave + kWaves - 1) / kWaves : 0;
+    const int passes = my_rows > 0 ? my_rows : (slot_of_wave == nrows ? 1 : 0);
     const bool has_helper = nrows + 1 < kWaves;
-    if (has_helper && wave == nrows + 1) {
+    if (has_helper && slot_of_wave == nrows + 1) {
         const uint64_t t_wait = __builtin_amdgcn_s_memrealtime();
         for (int t = 0; t < nrows; ++t) {
             int st;
@@ -232,7 +235,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         }
     }
     for (int it = 0; it < passes; ++it) {
-        const int t = wave + it * kWaves;
+        const int t = slot_of_wave + it * kWaves;
         const bool real = t < nrows;  // wave-uniform
         float v[kPerLane];
         float bv[kPerLane] = {0.f, 0.f, 0.f, 0.f};
