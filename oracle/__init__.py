@@ -51,10 +51,11 @@ class Oracle:
         lib.oracle_logits.argtypes = [P, P, i64, i64, i64, P, P]
         lib.oracle_topk_from_logits.argtypes = [P, P, i64, i64, ci, ci, ci, P, P]
         lib.oracle_router.argtypes = [P, P, P, i64, i64, i64, ci, ci, ci, P, P, P, P]
+        lib.oracle_route_table.argtypes = [P, ci, ci, P, P, P, P]
         lib.oracle_route_table_m2.argtypes = [P, ci, P, P, P, P]
         lib.oracle_row_scores.argtypes = [P, i64, ci, P, P]
         for f in (lib.oracle_logits, lib.oracle_topk_from_logits, lib.oracle_router,
-                  lib.oracle_route_table_m2, lib.oracle_row_scores):
+                  lib.oracle_route_table, lib.oracle_route_table_m2, lib.oracle_row_scores):
             f.restype = ci
         self.lib = lib
 
@@ -108,6 +109,21 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_router failed: {rc}")
         return inds, wts, lg, ad
+
+    def route_table(self, inds: np.ndarray):
+        """Unique-route table of inds [M, k] (slots token-major)."""
+        inds = np.ascontiguousarray(inds, dtype=np.int32)
+        assert inds.ndim == 2
+        M, k = inds.shape
+        ids = np.empty(M * k, np.int32)
+        mask = np.empty(M * k, np.int32)
+        s2u = np.empty(M * k, np.int32)
+        cnt = np.empty(1, np.int32)
+        rc = self.lib.oracle_route_table(self._ptr(inds), M, k, self._ptr(ids), self._ptr(mask),
+                                         self._ptr(s2u), self._ptr(cnt))
+        if rc:
+            raise ValueError(f"oracle_route_table failed: {rc}")
+        return ids, mask, s2u, int(cnt[0])
 
     def route_table_m2(self, inds: np.ndarray):
         inds = np.ascontiguousarray(inds, dtype=np.int32)

@@ -204,11 +204,12 @@ int oracle_router(const uint16_t* x, const uint16_t* w, const float* bias, int64
     return rc;
 }
 
-int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* token_mask,
-                          int32_t* slot_to_unique, int32_t* count)
+int oracle_route_table(const int32_t* inds, int M, int k, int32_t* ids, int32_t* token_mask,
+                       int32_t* slot_to_unique, int32_t* count)
 {
-    if (k < 1 || !inds || !ids || !token_mask || !slot_to_unique || !count) return ORACLE_EINVAL;
-    int n = 2 * k;
+    if (M < 1 || M > 31 || k < 1 || !inds || !ids || !token_mask || !slot_to_unique || !count)
+        return ORACLE_EINVAL;
+    int n = M * k;
     int u = 0;
     for (int i = 0; i < n; ++i) {
         ids[i] = -1;
@@ -231,4 +232,10 @@ int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* tok
     }
     *count = u;
     return 0;
+}
+
+int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* token_mask,
+                          int32_t* slot_to_unique, int32_t* count)
+{
+    return oracle_route_table(inds, 2, k, ids, token_mask, slot_to_unique, count);
 }

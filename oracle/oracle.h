@@ -49,8 +49,17 @@ int oracle_router(const uint16_t* x, const uint16_t* w, const float* bias, int64
                   int64_t H, int64_t E, int k, int scoring, int renorm, int32_t* inds,
                   float* weights, float* logits_out, double* absdot_out);
 
-/* Unique-route table for two tokens.  inds: [2,k] as produced by the router.
- * ids [2k], token_mask [2k], slot_to_unique [2k], count [1]. */
+/* Unique-route table of M tokens (1 <= M <= 31).  inds: [M,k] as produced by
+ * the router; slots s = t*k + j are walked token-major, then rank.
+ * ids [M*k]: distinct experts in order of first appearance, -1 after count;
+ * token_mask [M*k]: bit t set iff token t selected ids[q], 0 after count;
+ * slot_to_unique [M*k]: position of slot s's expert in ids; count [1].
+ * (The B70 note defines the table for the MTP1 pair, M=2; the same walk
+ * gives it at every verify width.) */
+int oracle_route_table(const int32_t* inds, int M, int k, int32_t* ids, int32_t* token_mask,
+                       int32_t* slot_to_unique, int32_t* count);
+
+/* The M=2 table (oracle_route_table with M=2). */
 int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* token_mask,
                           int32_t* slot_to_unique, int32_t* count);
 

@@ -398,6 +398,56 @@ def pin_table_invariants(o):
         assert sum(bin(int(m)).count("1") for m in mask) == 2 * k
 
 
+def pin_table_verify_widths(o):
+    """Any M: identical tokens share every expert (mask of M ones); disjoint tokens each
+    get k entries with mask 1 << t; hand-worked M=3 overlap; the M=2 entry point agrees."""
+    k = 4
+    base = [17, 3, 250, 64]
+    for M in (1, 3, 8, 16):
+        same = np.array([np.roll(base, t) for t in range(M)], np.int32)
+        ids, mask, s2u, cnt = o.route_table(same)
+        assert cnt == k and list(ids[:k]) == base and np.all(ids[k:] == -1)
+        assert list(mask[:k]) == [(1 << M) - 1] * k and np.all(mask[k:] == 0)
+        assert [base[v] for v in s2u] == list(same.reshape(-1))
+        disjoint = np.array([[t * k + j for j in range(k)] for t in range(M)], np.int32)
+        ids, mask, s2u, cnt = o.route_table(disjoint)
+        assert cnt == M * k and list(ids) == list(range(M * k))
+        assert list(mask) == [1 << (s // k) for s in range(M * k)]
+        assert list(s2u) == list(range(M * k))
+    # token 0 {5, 9}, token 1 {9, 4}, token 2 {4, 5}
+    ids, mask, s2u, cnt = o.route_table(np.array([[5, 9], [9, 4], [4, 5]], np.int32))
+    assert cnt == 3 and list(ids) == [5, 9, 4, -1, -1, -1]
+    assert list(mask) == [0b101, 0b011, 0b110, 0, 0, 0] and list(s2u) == [0, 1, 1, 2, 2, 0]
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        pair = np.stack([rng.choice(256, 6, replace=False) for _ in range(2)]).astype(np.int32)
+        a, b = o.route_table(pair), o.route_table_m2(pair)
+        assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3])) and a[3] == b[3]
+
+
+def pin_table_invariants_any_m(o):
+    """Random M in 1..16 with M*k <= 64: dict.fromkeys order, membership masks, slot map,
+    M*k mask bits in total."""
+    rng = np.random.default_rng(22)
+    for _ in range(300):
+        M = int(rng.integers(1, 17))
+        k = int(rng.integers(1, 64 // M + 1))
+        pool = rng.choice(256, size=int(rng.integers(k, min(256, M * k) + 1)), replace=False)
+        inds = np.stack([rng.choice(pool, size=k, replace=False) for _ in range(M)]).astype(np.int32)
+        ids, mask, s2u, cnt = o.route_table(inds)
+        slots = list(inds.reshape(-1))
+        uniq = list(dict.fromkeys(slots))
+        assert cnt == len(uniq) and list(ids[:cnt]) == uniq
+        assert np.all(ids[cnt:] == -1) and np.all(mask[cnt:] == 0)
+        for s, e in enumerate(slots):
+            assert ids[s2u[s]] == e
+        for q in range(cnt):
+            want = sum(1 << t for t in range(M) if ids[q] in inds[t])
+            assert mask[q] == want
+        assert k <= cnt <= M * k
+        assert sum(bin(int(m)).count("1") for m in mask) == M * k
+
+
 ALL_PINS = [
     pin_logits_small_integers, pin_logits_rational, pin_logits_one_hot, pin_logits_blas,
     pin_softplus_closed_forms, pin_softplus_logaddexp, pin_softmax_closed_forms,
@@ -405,5 +455,6 @@ ALL_PINS = [
     pin_unbiased_key_is_exact_score_order, pin_all_equal_rows,
     pin_bias_orders_equal_scores, pin_bias_flips_but_weights_unbiased, pin_bias_invariance,
     pin_renorm_sums_and_softmax_identity, pin_softmax_no_renorm_is_probability,
-    pin_table_hand_cases, pin_table_invariants,
+    pin_table_hand_cases, pin_table_invariants, pin_table_verify_widths,
+    pin_table_invariants_any_m,
 ]

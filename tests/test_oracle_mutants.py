@@ -43,6 +43,8 @@ MUTANTS = [
     ("table_tail_zero", "ids[i] = -1;", "ids[i] = 0;"),
     ("table_mask_overwrite", "token_mask[pos] |= 1 << token;", "token_mask[pos] = 1 << token;"),
     ("table_slot_map_raw", "slot_to_unique[s] = pos;", "slot_to_unique[s] = s;"),
+    ("table_pair_width_only", "int n = M * k;", "int n = (M > 2 ? 2 : M) * k;"),
+    ("table_mask_two_tokens", "token_mask[pos] |= 1 << token;", "token_mask[pos] |= 1 << (token & 1);"),
 ]
 
 
