@@ -275,6 +275,23 @@ def decode_extras(torch, R, W, dev, args):
     ex["biased_M2_k6_table_on_us_per_call"] = round(t_on, 3)
     ex["table_overhead_us_per_call"] = round(t_on - t_off, 3)
     ex["table_overhead_context_b70_us_per_layer"] = 3.132
+    # the table at the widest verify width (M=8, k=8: 64 slots), decode router
+    x8 = W.torch_rms_normalised_bf16((LAYERS, 8, H), seed=12, device=dev)
+    oi8 = torch.empty((LAYERS, 8, 8), dtype=torch.int32, device=dev)
+    ow8 = torch.empty((LAYERS, 8, 8), dtype=torch.float32, device=dev)
+    tabs8 = [{n: torch.empty(64 if n != "unique_count" else 1, dtype=torch.int32, device=dev)
+              for n in ("unique_ids", "token_mask", "slot_to_unique", "unique_count")}
+             for _ in range(LAYERS)]
+    off8 = [(lambda l=l: R.router_fwd(x8[l], wl[l], None, 8, W.SOFTMAX, True,
+                                      out_inds=oi8[l], out_weights=ow8[l])) for l in range(LAYERS)]
+    on8 = [(lambda l=l: R.router_fwd_route_table(x8[l], wl[l], None, 8, W.SOFTMAX, True,
+                                                 out=dict(inds=oi8[l], weights=ow8[l], **tabs8[l])))
+           for l in range(LAYERS)]
+    t_off8 = graph_call_us(torch, off8, args.steps, args.warmup)
+    t_on8 = graph_call_us(torch, on8, args.steps, args.warmup)
+    ex["table_M8_k8_off_us_per_call"] = round(t_off8, 3)
+    ex["table_M8_k8_on_us_per_call"] = round(t_on8, 3)
+    ex["table_M8_k8_overhead_us_per_call"] = round(t_on8 - t_off8, 3)
     for M in (16, 64):
         xm = W.torch_gaussian_bf16((LAYERS, M, H), 1.0, seed=20 + M, device=dev)
         oim = torch.empty((LAYERS, M, 6), dtype=torch.int32, device=dev)

@@ -26,7 +26,7 @@
 //     of the block; lane L polls the S partials of experts 4L..4L+3 (the
 //     routing layout itself) until none is the sentinel, resets those slots
 //     to the sentinel, adds the partials in split order and routes the row
-//     with route_row(); at M=2 the unique-route table follows.  The finisher
+//     with route_row(); the unique-route table, when asked for, follows.  The finisher
 //     also resets the counter, so the kernel replays inside a HIP graph.
 //
 // Every logit is accumulated in the same order regardless of its expert
@@ -97,7 +97,8 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     constexpr int kWaves = kLoadWaves + 1;  // + the control wave
 
     __shared__ float red[kLoadWaves][kDecodeTile][kDecodeTile + 1];
-    __shared__ int32_t slots[2 * kMaxK];
+    __shared__ int32_t slots[kWave];  // route table: M*k <= 64 slots
+    __shared__ int32_t tab_first[kMaxE + 1], tab_mask[kMaxE + 1];
     __shared__ int polled[kDecodeTile];  // finisher: 1 = row's partials read, 2 = row gave up
     __shared__ int is_last;
 
@@ -330,14 +331,15 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
             const int64_t o = (int64_t)(t0 + t) * a.k + lane;
             a.inds[o] = res.idx;
             a.weights[o] = res.w;
-            if (a.table_ids) slots[t * a.k + lane] = res.idx;  // M == 2: t < 2, k <= 16
+            if (a.table_ids) slots[t * a.k + lane] = res.idx;  // table: M*k <= 64
         }
     }
 
-    if (a.table_ids) {  // M == 2: both rows are in this row block
+    if (a.table_ids) {  // table: M <= 16, so every row is in this row block
         __syncthreads();
         if (wave == 0)
-            emit_route_table_m2(slots, a.k, a.table_ids, a.table_mask, a.table_s2u, a.table_count);
+            emit_route_table(slots, a.M, a.k, tab_first, tab_mask, a.table_ids, a.table_mask,
+                             a.table_s2u, a.table_count);
     }
 }
 

@@ -25,7 +25,7 @@ struct DecodeLaunch {
     int32_t* inds;
     float* weights;
     float* logits_out;      // optional
-    int32_t* table_ids;     // M == 2 table (all four set or all NULL)
+    int32_t* table_ids;     // unique-route table, M*k <= 64 (all four set or all NULL)
     int32_t* table_mask;
     int32_t* table_s2u;
     int32_t* table_count;

@@ -579,40 +579,46 @@ __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
 }
 
 // ---------------------------------------------------------------------------
-// M=2 unique-route table (b70 lab MTP1 note, "Unique-route router screen")
+// unique-route table (b70 lab MTP1 note, "Unique-route router screen", for
+// the MTP1 pair; qwisp issue #145, "Observation", for the other verify widths)
 // ---------------------------------------------------------------------------
-// One wavefront; slot s = t*k + j holds inds[t][j] (2k <= 64 slots).  Stable
-// de-duplication by first appearance, ranks by a prefix count of first
-// appearances, token masks gathered onto each first appearance.
-__device__ __forceinline__ void emit_route_table_m2(const int32_t* slot_ids, int k,
-                                                    int32_t* ids, int32_t* mask,
-                                                    int32_t* slot_to_unique, int32_t* count)
+// One wavefront; slot s = t*k + j holds inds[t][j] for M tokens (M*k <= 64
+// slots).  Per expert, two LDS cells (first_of, mask_of: kMaxE + 1 entries
+// each, the last one shared by any id outside 0..kMaxE-1) collect, with LDS
+// min and or atomics, the expert's first slot and its token mask (bit t =
+// token t); the first appearances, ranked by a prefix count over a ballot,
+// give the unique list in encounter order.
+__device__ __forceinline__ void emit_route_table(const int32_t* slot_ids, int M, int k,
+                                                 int32_t* first_of, int32_t* mask_of,
+                                                 int32_t* ids, int32_t* mask,
+                                                 int32_t* slot_to_unique, int32_t* count)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int n = 2 * k;
+    const int n = M * k;
     const bool active = lane < n;
-    const int id = active ? slot_ids[lane] : -1 - lane;  // inactive lanes never match
-
-    int first = -1;
-    for (int j = 0; j < n; ++j) {
-        const int idj = __builtin_amdgcn_readlane(id, j);
-        if (first < 0 && idj == id) first = j;
+    const int id = active ? slot_ids[lane] : 0;
+    const int cell = (id >= 0 && id < kMaxE) ? id : kMaxE;
+    if (active) {
+        first_of[cell] = kWave;
+        mask_of[cell] = 0;
     }
+    if (active) {
+        __hip_atomic_fetch_min(&first_of[cell], lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_or(&mask_of[cell], 1 << (lane / k), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    const int first = active ? __hip_atomic_load(&first_of[cell], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP)
+                             : -1;
     const uint64_t firsts = __builtin_amdgcn_ballot_w64(active && first == lane);
     const int unique = __builtin_popcountll(firsts);
     const int rank = active ? __builtin_popcountll(firsts & ((1ull << first) - 1ull)) : 0;
-
-    int token_bits = 0;
-    for (int j = 0; j < n; ++j) {
-        const int fj = __builtin_amdgcn_readlane(first, j);
-        if (lane == fj) token_bits |= 1 << (j / k);
-    }
 
     if (active) {
         slot_to_unique[lane] = rank;
         if (first == lane) {
             ids[rank] = id;
-            mask[rank] = token_bits;
+            mask[rank] = __hip_atomic_load(&mask_of[cell], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         if (lane >= unique) {
             ids[lane] = -1;

@@ -204,22 +204,40 @@ int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H
                      opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
+// The table is built by the finisher of the single row block, in one wavefront.
+static_assert(ROUTER_TABLE_MAX_M <= gpt::kDecodeTile, "table rows share one row block");
+static_assert(ROUTER_TABLE_MAX_SLOTS <= 64, "table slots fit one wavefront");
+static_assert(ROUTER_TABLE_MAX_M <= ROUTER_DECODE_MAX_M, "table calls take the decode path");
+
+int router_fwd_route_table(const void* x, const void* w, const float* bias, int M, int H, int E,
+                           int k, int scoring, int renorm, int32_t* out_inds, float* out_weights,
+                           float* opt_out_logits, int32_t* out_unique_ids,
+                           int32_t* out_token_mask, int32_t* out_slot_to_unique,
+                           int32_t* out_unique_count, hipStream_t stream)
+{
+    int rc = check_common(M, E, k, scoring, renorm);
+    if (rc == ROUTER_OK) rc = check_hidden(H);
+    if (rc == ROUTER_OK) rc = check_projection(x, w);
+    if (rc != ROUTER_OK) return rc;
+    if (M < 1) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (M > ROUTER_TABLE_MAX_M || M * k > ROUTER_TABLE_MAX_SLOTS) return ROUTER_ERR_UNSUPPORTED;
+    if (!out_inds || !out_weights || !out_unique_ids || !out_token_mask || !out_slot_to_unique ||
+        !out_unique_count)
+        return ROUTER_ERR_INVALID_ARGUMENT;
+    return run_fused(x, w, bias, M, H, E, k, scoring, renorm, out_inds, out_weights,
+                     opt_out_logits, out_unique_ids, out_token_mask, out_slot_to_unique,
+                     out_unique_count, stream);
+}
+
 int router_fwd_m2_table(const void* x, const void* w, const float* bias, int H, int E, int k,
                         int scoring, int renorm, int32_t* out_inds, float* out_weights,
                         float* opt_out_logits, int32_t* out_unique_ids,
                         int32_t* out_token_mask, int32_t* out_slot_to_unique,
                         int32_t* out_unique_count, hipStream_t stream)
 {
-    int rc = check_common(2, E, k, scoring, renorm);
-    if (rc == ROUTER_OK) rc = check_hidden(H);
-    if (rc == ROUTER_OK) rc = check_projection(x, w);
-    if (rc != ROUTER_OK) return rc;
-    if (!out_inds || !out_weights || !out_unique_ids || !out_token_mask || !out_slot_to_unique ||
-        !out_unique_count)
-        return ROUTER_ERR_INVALID_ARGUMENT;
-    return run_fused(x, w, bias, 2, H, E, k, scoring, renorm, out_inds, out_weights,
-                     opt_out_logits, out_unique_ids, out_token_mask, out_slot_to_unique,
-                     out_unique_count, stream);
+    return router_fwd_route_table(x, w, bias, 2, H, E, k, scoring, renorm, out_inds, out_weights,
+                                  opt_out_logits, out_unique_ids, out_token_mask,
+                                  out_slot_to_unique, out_unique_count, stream);
 }
 
 int router_topk_from_logits(const float* logits, const float* bias, int64_t M, int E, int k,

@@ -26,7 +26,12 @@ ERR_MISALIGNED = 3
 ERR_HIP = 4
 ERR_NO_WORKSPACE = 5
 
-EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_topk_from_logits",
+# router_fwd_route_table limits (ROUTER_TABLE_MAX_M / ROUTER_TABLE_MAX_SLOTS)
+TABLE_MAX_M = 16
+TABLE_MAX_SLOTS = 64
+
+EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
+           "router_topk_from_logits",
            "router_set_exchange_timeout_us", "router_strerror")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -55,6 +60,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_fwd.restype = i32
     lib.router_fwd_m2_table.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
     lib.router_fwd_m2_table.restype = i32
+    lib.router_fwd_route_table.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P,
+                                           P, P]
+    lib.router_fwd_route_table.restype = i32
     lib.router_topk_from_logits.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, P]
     lib.router_topk_from_logits.restype = i32
     lib.router_set_exchange_timeout_us.argtypes = [i32]
@@ -154,10 +162,11 @@ def router_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k
     return (inds, wts, logits) if logits is not None else (inds, wts)
 
 
-def router_fwd_m2_table(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k: int,
-                        scoring: int = SOFTMAX, renorm: bool = True, *, return_logits: bool = False,
-                        out=None):
-    """Two-token router plus the unique-route table, one launch.
+def router_fwd_route_table(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                           scoring: int = SOFTMAX, renorm: bool = True, *, return_logits: bool = False,
+                           out=None):
+    """Router plus the unique-route table of its M tokens, one launch
+    (1 <= M <= TABLE_MAX_M, M*k <= TABLE_MAX_SLOTS).
 
     Returns a dict with inds, weights, unique_ids, token_mask, slot_to_unique,
     unique_count (and logits when return_logits).  `out` may supply any of
@@ -167,8 +176,48 @@ def router_fwd_m2_table(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.T
     _check_tensor(w, "w", torch.bfloat16, 2)
     M, H = x.shape
     E = w.shape[0]
-    if M != 2:
+    if not 1 <= M <= TABLE_MAX_M or M * int(k) > TABLE_MAX_SLOTS:
+        raise ValueError(f"the route table needs 1 <= M <= {TABLE_MAX_M} and M*k <= {TABLE_MAX_SLOTS}")
+    if w.shape[1] != H:
+        raise ValueError("x and w disagree on H")
+    _check_bias(bias, E)
+    out = dict(out or {})
+    inds, wts, logits = _outputs(M, k, E, x.device, out.get("inds"), out.get("weights"),
+                                 return_logits, out.get("logits"))
+    n = M * int(k)
+    tab = {}
+    for name, cnt in (("unique_ids", n), ("token_mask", n), ("slot_to_unique", n),
+                      ("unique_count", 1)):
+        t = out.get(name)
+        if t is None:
+            t = torch.empty(cnt, dtype=torch.int32, device=x.device)
+        _check_tensor(t, name, torch.int32, 1)
+        if t.shape[0] != cnt:
+            raise ValueError(f"{name} must have {cnt} entries")
+        tab[name] = t
+    with torch.cuda.device(x.device):
+        rc = load().router_fwd_route_table(
+            _ptr(x), _ptr(w), _ptr(bias), M, H, E, int(k), int(scoring), int(bool(renorm)),
+            _ptr(inds), _ptr(wts), _ptr(logits), _ptr(tab["unique_ids"]), _ptr(tab["token_mask"]),
+            _ptr(tab["slot_to_unique"]), _ptr(tab["unique_count"]), _stream(x.device))
+    _check(rc, "router_fwd_route_table")
+    res = {"inds": inds, "weights": wts, **tab}
+    if logits is not None:
+        res["logits"] = logits
+    return res
+
+
+def router_fwd_m2_table(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                        scoring: int = SOFTMAX, renorm: bool = True, *, return_logits: bool = False,
+                        out=None):
+    """Two-token router plus the unique-route table, one launch (the MTP1
+    pair; router_fwd_route_table with M = 2)."""
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    if x.shape[0] != 2:
         raise ValueError("router_fwd_m2_table needs exactly two tokens")
+    _check_tensor(w, "w", torch.bfloat16, 2)
+    M, H = x.shape
+    E = w.shape[0]
     if w.shape[1] != H:
         raise ValueError("x and w disagree on H")
     _check_bias(bias, E)

@@ -199,6 +199,38 @@ def biased_case(M: int, seed: int = 0, H: int = 4096, E: int = 256, k: int = 6,
     return RouterCase(x, w, bias, k, SQRT_SOFTPLUS, True, name=f"biased/M{M}/seed{seed}")
 
 
+def verify_table_case(M: int, seed: int = 0, H: int = 4096, E: int = 256, k: int = 8,
+                      biased: bool = False) -> RouterCase:
+    """M tokens at a verify width for the unique-route table: the decode router
+    (softmax, no bias, k=8) or, with biased=True, the sqrt-softplus router with a
+    U(-0.05,0.05) selection bias.  Seeds with seed % 10 < 5 overwrite 1..k gate
+    rows with a scaled copy of sum_t x_t/|x_t|^2, which every token then picks,
+    and (odd seeds among those) 1..3 more rows with the same construction over
+    the first half of the tokens only, so masks cover all-tokens, some-tokens and
+    one-token experts."""
+    rng = _rng(seed, 9)
+    x = gaussian_bf16(rng, (M, H), 1.0)
+    w = gaussian_bf16(rng, (E, H), 1.0 / np.sqrt(H))
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32) if biased else None
+    if seed % 10 < 5:
+        xb = bf16_bits_to_f32(x).astype(np.float64)
+        unit = xb / np.einsum("th,th->t", xb, xb)[:, None]
+        groups = [np.arange(M)]
+        if seed % 2 == 1 and M > 1:
+            groups.append(np.arange((M + 1) // 2))
+        rows = rng.choice(E, size=int(rng.integers(1, k + 1)) + 3, replace=False)
+        at = 0
+        for gi, tok in enumerate(groups):
+            count = int(rng.integers(1, k + 1)) if gi == 0 else int(rng.integers(1, 4))
+            for r in rows[at:at + count]:
+                alpha = 4.0 + 0.25 * rng.standard_normal()
+                w[r] = f32_to_bf16_bits((alpha * unit[tok].sum(axis=0)).astype(np.float32))
+            at += count
+    scoring = SQRT_SOFTPLUS if biased else SOFTMAX
+    kind = "biased" if biased else "softmax"
+    return RouterCase(x, w, bias, k, scoring, True, name=f"table/{kind}/M{M}/k{k}/seed{seed}")
+
+
 def prefill_case(M: int = 8192, H: int = 7168, seed: int = 0, E: int = 256, k: int = 8) -> RouterCase:
     """Prefill router: softmax scores with U(-0.02,0.02) selection-only bias."""
     rng = _rng(seed, 6)

@@ -74,6 +74,10 @@ extern "C" {
 /* router_fwd runs the split-H decode kernel up to this many tokens and the
  * MFMA GEMM-with-epilogue prefill kernel above it. */
 #define ROUTER_DECODE_MAX_M 64
+/* router_fwd_route_table: at most this many tokens, and at most
+ * ROUTER_TABLE_MAX_SLOTS = M*k slots (one wavefront builds the table). */
+#define ROUTER_TABLE_MAX_M 16
+#define ROUTER_TABLE_MAX_SLOTS 64
 
 typedef enum {
     ROUTER_SCORING_SOFTMAX = 0,
@@ -123,6 +127,26 @@ int router_fwd_m2_table(const void* x, const void* w, const float* bias, int H, 
                         float* opt_out_logits, int32_t* out_unique_ids,
                         int32_t* out_token_mask, int32_t* out_slot_to_unique,
                         int32_t* out_unique_count, hipStream_t stream);
+
+/* router_fwd plus the unique-route table at any verify width: the table of
+ * router_fwd_m2_table extended from the MTP1 pair to M tokens (qwisp issue
+ * #145, "Observation": the router runs at every verify width), in the same
+ * launch.  Slots s = t*k + j are walked token-major, then rank:
+ *   out_unique_ids      int32 [M*k]: distinct experts in order of first
+ *                       appearance; unused tail entries are -1;
+ *   out_token_mask      int32 [M*k]: bit t set iff token t selected that
+ *                       unique expert; unused tail entries are 0;
+ *   out_slot_to_unique  int32 [M*k]: position of inds[t,j] in out_unique_ids;
+ *   out_unique_count    int32 [1]:   number of distinct experts (k..M*k).
+ * Limits: 1 <= M <= ROUTER_TABLE_MAX_M and M*k <= ROUTER_TABLE_MAX_SLOTS,
+ * else ROUTER_ERR_UNSUPPORTED (nothing launched); the rest as router_fwd.
+ * inds/weights are bit-identical to router_fwd's on the same inputs; with
+ * M = 2 the call is router_fwd_m2_table. */
+int router_fwd_route_table(const void* x, const void* w, const float* bias, int M, int H, int E,
+                           int k, int scoring, int renorm, int32_t* out_inds, float* out_weights,
+                           float* opt_out_logits, int32_t* out_unique_ids,
+                           int32_t* out_token_mask, int32_t* out_slot_to_unique,
+                           int32_t* out_unique_count, hipStream_t stream);
 
 /* Scoring, selection and weights on logits already in HBM (the standalone
  * logits-to-top-k of the unfused pair; dense_router_decode notes, "Current

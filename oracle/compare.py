@@ -174,9 +174,10 @@ def check_router(orc, case, gpu_inds, gpu_w, gpu_logits, ref=None, rows=None) ->
     return RouterReport(M, n_band, exact_in_band, ratio, max_wrel)
 
 
-def check_table(orc, gpu_inds2, table: dict):
-    """Rule (c): the emitted table equals the oracle's table of the same indices."""
-    ids, mask, s2u, cnt = orc.route_table_m2(np.asarray(gpu_inds2, np.int32))
+def check_table(orc, gpu_inds, table: dict):
+    """Rule (c): the emitted table equals the oracle's table of the same indices
+    (gpu_inds: [M, k])."""
+    ids, mask, s2u, cnt = orc.route_table(np.asarray(gpu_inds, np.int32))
     got = {k: np.asarray(v) for k, v in table.items()}
     assert np.array_equal(got["unique_ids"], ids), (got["unique_ids"], ids)
     assert np.array_equal(got["token_mask"], mask), (got["token_mask"], mask)

@@ -101,6 +101,29 @@ def test_m2_table_rejects(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(M=0), R.ERR_INVALID_ARGUMENT),
+    (dict(M=-1), R.ERR_INVALID_ARGUMENT),
+    (dict(M=17, k=2), R.ERR_UNSUPPORTED),
+    (dict(M=8, k=9), R.ERR_UNSUPPORTED),
+    (dict(M=9, k=8), R.ERR_UNSUPPORTED),
+    (dict(k=17), R.ERR_UNSUPPORTED),
+    (dict(ids=None), R.ERR_INVALID_ARGUMENT),
+    (dict(mask=None), R.ERR_INVALID_ARGUMENT),
+    (dict(s2u=None), R.ERR_INVALID_ARGUMENT),
+    (dict(count=None), R.ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE_ODD), R.ERR_MISALIGNED),
+    (dict(H=12), R.ERR_UNSUPPORTED),
+])
+def test_route_table_rejects(lib, kw, code):
+    a = dict(x=FAKE, w=FAKE, M=8, H=4096, E=256, k=8, ids=FAKE, mask=FAKE, s2u=FAKE, count=FAKE)
+    a.update(kw)
+    rc = lib.router_fwd_route_table(a["x"], a["w"], None, a["M"], a["H"], a["E"], a["k"], 0, 1,
+                                    FAKE, FAKE, None, a["ids"], a["mask"], a["s2u"], a["count"],
+                                    None)
+    assert rc == code, (kw, rc)
+
+
+@pytest.mark.parametrize("kw,code", [
     (dict(logits=None), R.ERR_INVALID_ARGUMENT),
     (dict(E=300), R.ERR_UNSUPPORTED),
     (dict(k=20), R.ERR_UNSUPPORTED),

@@ -1,4 +1,5 @@
-"""router_fwd / router_fwd_m2_table vs the oracle (rules b and c) and self-consistency.
+"""router_fwd / router_fwd_m2_table / router_fwd_route_table vs the oracle (rules b and c) and
+self-consistency.
 
 Workloads (seeded, synthetic): the tiny E=16 router with exact-tie rows, the
 verify-width decode router (M in {1,2,8}, H=4096, unit-RMS activations), the
@@ -99,6 +100,39 @@ def test_m2_table_extremes(orc):
     assert np.all(host(res["token_mask"])[:8] == 3) and np.all(host(res["unique_ids"])[8:] == -1)
     check_table(orc, gi, {k: host(res[k]) for k in
                           ("unique_ids", "token_mask", "slot_to_unique", "unique_count")})
+
+
+TABLE_WIDTHS = [(1, 8, False), (3, 8, False), (4, 8, False), (8, 8, False), (16, 4, False),
+                (3, 6, True), (8, 6, True), (10, 6, True)]
+
+
+@pytest.mark.parametrize("M,k,biased", TABLE_WIDTHS, ids=lambda v: str(v))
+@pytest.mark.parametrize("seed", [0, 1, 3, 5, 8])
+def test_route_table_verify_widths(orc, M, k, biased, seed):
+    """The table at every verify width (M*k <= 64 slots) is the oracle's table of the
+    returned indices, and inds/weights are the bytes router_fwd gives."""
+    case = W.verify_table_case(M, seed=seed, k=k, biased=biased)
+    say(f"route table {case.name}")
+    res = R.router_fwd_route_table(bf16_dev(case.x), bf16_dev(case.w), f32_dev(case.bias), case.k,
+                                   case.scoring, case.renorm, return_logits=True)
+    torch.cuda.synchronize()
+    gi, gw, gl = host(res["inds"]), host(res["weights"]), host(res["logits"])
+    check_router(orc, case, gi, gw, gl)
+    check_table(orc, gi, {k: host(res[k]) for k in
+                          ("unique_ids", "token_mask", "slot_to_unique", "unique_count")})
+    pi, pw, _ = run_fwd(case)
+    assert np.array_equal(pi, gi) and np.array_equal(pw.view(np.uint32), gw.view(np.uint32))
+    if seed % 10 < 5 and M > 1:
+        assert int(host(res["unique_count"])[0]) < M * case.k  # shared experts were forced
+
+
+def test_route_table_m2_matches_general(orc):
+    case = W.biased_case(2, seed=2)
+    args = (bf16_dev(case.x), bf16_dev(case.w), f32_dev(case.bias), case.k, case.scoring, case.renorm)
+    a, b = R.router_fwd_m2_table(*args), R.router_fwd_route_table(*args)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name].view(torch.int32), b[name].view(torch.int32)), name
 
 
 @pytest.mark.parametrize("M", [65, 100, 333, 1000])

@@ -48,6 +48,17 @@ def _shapes():
     out.append(("m2 table", lambda: R.router_fwd_m2_table(x, w, b, case.k, case.scoring,
                                                            case.renorm, out=t), list(t.values())))
 
+    case8 = W.verify_table_case(8, seed=13)
+    x8, w8 = bf16_dev(case8.x), bf16_dev(case8.w)
+    t8 = {n: torch.empty(8 * case8.k if n != "unique_count" else 1, dtype=torch.int32,
+                         device="cuda:0")
+          for n in ("unique_ids", "token_mask", "slot_to_unique", "unique_count")}
+    t8["inds"] = torch.empty((8, case8.k), dtype=torch.int32, device="cuda:0")
+    t8["weights"] = torch.empty((8, case8.k), dtype=torch.float32, device="cuda:0")
+    out.append(("M=8 table", lambda: R.router_fwd_route_table(x8, w8, None, case8.k, case8.scoring,
+                                                              case8.renorm, out=t8),
+                list(t8.values())))
+
     lg = f32_dev(W.adversarial_logits(64, seed=12).logits)
     ti = torch.empty((64, 8), dtype=torch.int32, device="cuda:0")
     tw = torch.empty((64, 8), dtype=torch.float32, device="cuda:0")
