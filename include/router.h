@@ -19,7 +19,8 @@
  *     a per-expert bias, unbiased winners' scores renormalised; the BF16 GEMM
  *     with FP32 accumulation and the row-level top-k epilogue;
  *   - b70 lab MTP1 M=2 note, "Unique-route router screen": the optional M=2
- *     unique-route table produced inside the router launch.
+ *     unique-route table produced inside the router launch (here also at the
+ *     other verify widths of qwisp issue #145, "Observation").
  *
  * Precise definition (shared by every entry point):
  *   logit[t,e]  = sum_i x[t,i]*w[e,i], bf16 operands, fp32 accumulation
