@@ -11,10 +11,12 @@
 //   grid = R row blocks x B expert blocks x S H-splits; each workgroup has
 //   kDecodeWaves load waves and one control wave.
 //   Start: the control wave draws an arrival ticket on the row block's
-//     counter.  The workgroup that draws the last ticket is the row block's
-//     finisher; every other workgroup of the block has started by then, and
-//     none of them ever waits, so the finisher's wait below always ends.
-//     The ticket's round trip overlaps the loads of phase 1.
+//     counter.  The workgroups that draw the last F tickets are the row
+//     block's finishers (F > 1 when the block has more rows than a
+//     workgroup has waves to spare, each finisher taking every F-th row).
+//     No workgroup but a finisher ever waits, and the grid (at most 256
+//     workgroups) is resident at once, so the finishers' waits below always
+//     end.  The ticket's round trip overlaps the loads of phase 1.
 //   Phase 1 (every workgroup): the 16x16 (tokens x experts) partial dot
 //     products over its H-split, one bf16 MFMA 16x16x32 per 32-wide k-step,
 //     every wave's loads issued before its first MFMA; the waves' partials
@@ -100,7 +102,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     __shared__ int32_t slots[kWave];  // route table: M*k <= 64 slots
     __shared__ int32_t tab_first[kMaxE + 1], tab_mask[kMaxE + 1];
     __shared__ int polled[kDecodeTile];  // finisher: 1 = row's partials read, 2 = row gave up
-    __shared__ int is_last;
+    __shared__ int fin_index;  // this workgroup's finisher index, -1: not a finisher
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -113,6 +115,14 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     const int b = bid % B;
     const int r = bid / B;
 
+    // Finishers per row block: the last nfin workgroups to draw a ticket on
+    // the block's row counter each route every nfin-th row, so that no wave
+    // of a finisher routes more than one row.  (The route table needs all
+    // rows in one workgroup: one finisher then.)
+    const int t0 = r * kDecodeTile;
+    const int rows_here = min(kDecodeTile, a.M - t0);
+    const int nfin = a.table_ids ? 1 : min(B, max(1, (rows_here + kWaves - 2) / (kWaves - 1)));
+
     if (tid < kDecodeTile) polled[tid] = 0;
     if (wave == kLoadWaves) {
         // ---- control wave: the arrival ticket, in two levels so that no
@@ -124,17 +134,16 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         if (lane == 0) {
             uint32_t* block_ctr = a.counters + kDecodeCounterStride * (r * kDecodeMaxBlocks + b);
             uint32_t* row_ctr = a.counters + kDecodeCounterStride * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + r);
-            int last = 0;
+            int fin = -1;
             if (__hip_atomic_fetch_add(block_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                 (uint32_t)a.S - 1u) {
                 __hip_atomic_store(block_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (__hip_atomic_fetch_add(row_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    (uint32_t)B - 1u) {
+                const uint32_t rt = __hip_atomic_fetch_add(row_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (rt == (uint32_t)B - 1u)
                     __hip_atomic_store(row_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    last = 1;
-                }
+                if (rt >= (uint32_t)(B - nfin)) fin = (int)rt - (B - nfin);
             }
-            is_last = last;
+            fin_index = fin;
         }
     } else {
         // ---- phase 1: partial logits of 16 tokens x 16 experts over one H-split
@@ -192,11 +201,12 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         const int row = r * kDecodeTile + rr;
         if (row < a.M) publish4(prs, s * qstride + (row * kMaxE + b * kDecodeTile + cc) * 4, sum);
     }
-    if (!is_last) return;  // written by the control wave before the barrier
+    const int f = fin_index;  // written by the control wave before the barrier
+    if (f < 0) return;
 
-    // ---- phase 2 (finisher): one wave per row; lane L owns experts 4L..4L+3.
-    const int t0 = r * kDecodeTile;
-    const int nrows = min(kDecodeTile, a.M - t0);
+    // ---- phase 2 (finisher f): rows t = f + nfin*i of the row block, one
+    // wave per row; lane L owns experts 4L..4L+3.
+    const int nrows = (rows_here - f + nfin - 1) / nfin;  // this finisher's rows
     const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};
     const bool mine = lane < 4 * B;  // the lane's expert group lies in a published block
     const f32x4 sentinel4 = __builtin_bit_cast(f32x4, u32x4{kPartialSentinel, kPartialSentinel,
@@ -229,15 +239,16 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                    __builtin_amdgcn_s_memrealtime() - t_wait < 2 * kDecodePollLimitTicks)
                 __builtin_amdgcn_s_sleep(1);
             if (st == 1 && mine) {
-                const int off = ((t0 + t) * kMaxE + lane * kPerLane) * 4;
+                const int off = ((t0 + f + nfin * t) * kMaxE + lane * kPerLane) * 4;
 #pragma unroll
                 for (int q = 0; q < kMaxS; ++q) publish4(prs, off + q * qstride, sentinel4);
             }
         }
     }
     for (int it = 0; it < passes; ++it) {
-        const int t = slot_of_wave + it * kWaves;
-        const bool real = t < nrows;  // wave-uniform
+        const int i = slot_of_wave + it * kWaves;  // the finisher's i-th row
+        const bool real = i < nrows;               // wave-uniform
+        const int t = f + nfin * i;                // its row in the block
         float v[kPerLane];
         float bv[kPerLane] = {0.f, 0.f, 0.f, 0.f};
         if (real) {
@@ -289,7 +300,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                 }
             }
             if (gave_up) {
-                if (lane == 0) __hip_atomic_store(&polled[t], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (lane == 0) __hip_atomic_store(&polled[i], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 if (lane < a.k) {
                     const int64_t o = (int64_t)(t0 + t) * a.k + lane;
                     a.inds[o] = -1;
@@ -299,7 +310,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                 continue;
             }
             if (has_helper) {
-                if (lane == 0) __hip_atomic_store(&polled[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (lane == 0) __hip_atomic_store(&polled[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             } else if (mine) {
 #pragma unroll
                 for (int q = 0; q < kMaxS; ++q) publish4(prs, off + q * qstride, sentinel4);
