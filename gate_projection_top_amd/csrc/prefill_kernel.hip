@@ -196,18 +196,19 @@ __device__ __forceinline__ void pf_gather_rows(const PrefillLaunch& p, float* ti
 }
 
 // Route own rows from the exchange: wave w takes rows w, w+8, ... of
-// [r0, r0 + rows) in pairs; lane L reads the other splits' partials of
-// experts 4L..4L+3 of the pair's rows (the next pair's loads are issued
-// before the current pair is routed, so the reads overlap routing), adds them
-// to its own partials from LDS in split order, and the pair is routed in
-// lockstep.  Every split's partials are complete (each waited for its stores
-// before counting itself in).
+// [r0, r0 + rows) in groups of four (at S = 4 a split owns 32 rows, one group
+// per wave; with more, the next group's loads are issued before the current
+// one is routed, so the reads overlap routing); lane L reads the other
+// splits' partials of experts 4L..4L+3 of the group's rows, adds them to its
+// own partials from LDS in split order, and the group is routed in lockstep.
+// Every split's partials are complete (each waited for its stores before
+// counting itself in).
 template <int S>
 __device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, const float* tile_f, int tile,
                                                   int s, int64_t row0, int r0, int rows, int wave,
                                                   int lane, const float (&bv)[kPerLane])
 {
-    constexpr int G = 2;
+    constexpr int G = 4;
     const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(p.partials);
     const RowSpec spec{p.E, p.k, p.scoring, p.renorm, p.bias != nullptr};
     const int col = lane * kPerLane;
