@@ -231,6 +231,55 @@ def verify_table_case(M: int, seed: int = 0, H: int = 4096, E: int = 256, k: int
     return RouterCase(x, w, bias, k, scoring, True, name=f"table/{kind}/M{M}/k{k}/seed{seed}")
 
 
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # OCP MX FP4 codes 0..7
+
+
+def quantise_mxfp4(w: np.ndarray):
+    """Synthetic MXFP4 weights from real ones [E, H] (H % 32 == 0): per 32-block an E8M0
+    scale 2^(ceil(log2(amax / 6))) (so the block's largest magnitude fits E2M1's 6), codes
+    by nearest magnitude; even element in the low nibble.  Returns (elems uint8 [E, H/2],
+    scales uint8 [E, H/32]).  Input construction only: the router never quantises."""
+    E, H = w.shape
+    assert H % 32 == 0
+    blocks = w.astype(np.float64).reshape(E, H // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    ex = np.ceil(np.log2(np.maximum(amax, 1e-30) / 6.0)).astype(np.int64)
+    ex = np.clip(ex, 2 - 127, 252 - 127)
+    scaled = blocks / np.ldexp(1.0, ex)[:, :, None]
+    mag = np.abs(scaled)
+    code = np.abs(mag[..., None] - E2M1_MAGNITUDES).argmin(axis=-1)
+    code = code | np.where(scaled < 0, 8, 0)
+    code = code.reshape(E, H).astype(np.uint8)
+    elems = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    scales = (ex + 127).astype(np.uint8)
+    return elems, scales
+
+
+@dataclasses.dataclass
+class MxCase:
+    x: np.ndarray        # bf16 bits [M, H]
+    elems: np.ndarray    # uint8 [E, H/2]
+    scales: np.ndarray   # uint8 [E, H/32]
+    bias: Optional[np.ndarray]
+    k: int
+    scoring: int
+    renorm: bool
+    name: str = ""
+
+
+def mxfp4_case(M: int, H: int = 4096, seed: int = 0, E: int = 256, k: int = 8,
+               scoring: int = SOFTMAX, with_bias: bool = False, renorm: bool = True) -> MxCase:
+    """Router on MXFP4 gate weights: X = unit-RMS N(0,1) rows in bf16, W ~ N(0,1/H)
+    quantised to MXFP4 (quantise_mxfp4); optional U(-0.05,0.05) selection bias."""
+    rng = _rng(seed, 10)
+    x = rms_normalised_bf16(rng, M, H)
+    w = rng.standard_normal((E, H)) / np.sqrt(H)
+    elems, scales = quantise_mxfp4(w)
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32) if with_bias else None
+    return MxCase(x, elems, scales, bias, k, scoring, renorm,
+                  name=f"mxfp4/M{M}/H{H}/E{E}/k{k}/s{scoring}/b{int(with_bias)}/seed{seed}")
+
+
 def prefill_case(M: int = 8192, H: int = 7168, seed: int = 0, E: int = 256, k: int = 8) -> RouterCase:
     """Prefill router: softmax scores with U(-0.02,0.02) selection-only bias."""
     rng = _rng(seed, 6)

@@ -52,6 +52,12 @@ class Oracle:
         lib.oracle_topk_from_logits.argtypes = [P, P, i64, i64, ci, ci, ci, P, P]
         lib.oracle_router.argtypes = [P, P, P, i64, i64, i64, ci, ci, ci, P, P, P, P]
         lib.oracle_route_table.argtypes = [P, ci, ci, P, P, P, P]
+        lib.oracle_e2m1_value.argtypes = [ci]
+        lib.oracle_e2m1_value.restype = ctypes.c_double
+        lib.oracle_dequant_mxfp4.argtypes = [P, P, i64, i64, P]
+        lib.oracle_dequant_mxfp4.restype = ci
+        lib.oracle_router_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, ci, ci, ci, P, P, P, P]
+        lib.oracle_router_mxfp4.restype = ci
         lib.oracle_route_table_m2.argtypes = [P, ci, P, P, P, P]
         lib.oracle_row_scores.argtypes = [P, i64, ci, P, P]
         for f in (lib.oracle_logits, lib.oracle_topk_from_logits, lib.oracle_router,
@@ -108,6 +114,41 @@ class Oracle:
                                     self._ptr(wts), self._ptr(lg), self._ptr(ad))
         if rc:
             raise ValueError(f"oracle_router failed: {rc}")
+        return inds, wts, lg, ad
+
+    def e2m1_value(self, code: int) -> float:
+        return float(self.lib.oracle_e2m1_value(int(code)))
+
+    def dequant_mxfp4(self, elems: np.ndarray, scales: np.ndarray) -> np.ndarray:
+        """elems uint8 [E, H/2], scales uint8 [E, H/32] -> float64 [E, H]."""
+        elems = np.ascontiguousarray(elems, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        E, H = elems.shape[0], elems.shape[1] * 2
+        w = np.empty((E, H), np.float64)
+        rc = self.lib.oracle_dequant_mxfp4(self._ptr(elems), self._ptr(scales), E, H, self._ptr(w))
+        if rc:
+            raise ValueError(f"oracle_dequant_mxfp4 failed: {rc}")
+        return w
+
+    def router_mxfp4(self, x: np.ndarray, elems: np.ndarray, scales: np.ndarray,
+                     bias: Optional[np.ndarray], k: int, scoring: int, renorm: bool):
+        """Router on MXFP4 gate weights: (inds, weights, logits, absdot)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        elems = np.ascontiguousarray(elems, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        M, H = x.shape
+        E = elems.shape[0]
+        assert elems.shape[1] * 2 == H and scales.shape == (E, H // 32)
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        inds = np.empty((M, k), np.int32)
+        wts = np.empty((M, k), np.float32)
+        lg = np.empty((M, E), np.float32)
+        ad = np.empty((M, E), np.float64)
+        rc = self.lib.oracle_router_mxfp4(self._ptr(x), self._ptr(elems), self._ptr(scales),
+                                          self._ptr(b), M, H, E, k, int(scoring), int(bool(renorm)),
+                                          self._ptr(inds), self._ptr(wts), self._ptr(lg), self._ptr(ad))
+        if rc:
+            raise ValueError(f"oracle_router_mxfp4 failed: {rc}")
         return inds, wts, lg, ad
 
     def route_table(self, inds: np.ndarray):

@@ -36,7 +36,12 @@
  *    sqrt-softplus value; the bias never enters a weight;
  *  - table: slots walked token-major then rank; an expert's position is the
  *    order of its first appearance; mask bit t set when token t picked it;
- *    unused ids are -1 and unused masks 0.
+ *    unused ids are -1 and unused masks 0;
+ *  - block-scaled gate (the notes' NVFP4 gate, in the MX form gfx950 reads
+ *    natively): OCP MXFP4, E2M1 codes two per byte (even element low), one
+ *    E8M0 scale per 32 elements of a row; scales in [2, 252], so every
+ *    dequantised weight is zero or a normal bf16 value and the logits are
+ *    the exact dot product with those values, as for bf16 weights.
  */
 #include "oracle.h"
 
@@ -187,6 +192,67 @@ done:
     free(key);
     free(top_key);
     free(top_idx);
+    return rc;
+}
+
+/* MXFP4 gate weights (OCP Microscaling Formats v1.0; the gfx950 counterpart of
+ * the NVFP4 gate of the dense_router_decode notes, "NVFP4 gate"): element FP4
+ * E2M1 = sign, two exponent bits (bias 1), one mantissa bit, no inf/NaN; a
+ * shared E8M0 scale 2^(s-127) per 32 consecutive elements of a row. */
+double oracle_e2m1_value(int code)
+{
+    int sign = (code >> 3) & 1, ex = (code >> 1) & 3, man = code & 1;
+    double mag = ex == 0 ? 0.5 * man                     /* subnormal: 0 or 0.5 */
+                         : ldexp(1.0 + 0.5 * man, ex - 1);
+    return sign ? -mag : mag;
+}
+
+int oracle_dequant_mxfp4(const uint8_t* elems, const uint8_t* scales, int64_t E, int64_t H,
+                         double* w)
+{
+    if (E < 1 || H < 32 || H % 32 != 0 || !elems || !scales || !w) return ORACLE_EINVAL;
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t col = 0; col < H; ++col) {
+            int sc = scales[e * (H / 32) + col / 32];
+            if (sc < ORACLE_MX_SCALE_MIN || sc > ORACLE_MX_SCALE_MAX) return ORACLE_EINVAL;
+            int byte = elems[e * (H / 2) + col / 2];
+            int code = (col % 2 == 0) ? (byte & 15) : (byte >> 4); /* even element: low nibble */
+            w[e * H + col] = ldexp(oracle_e2m1_value(code), sc - 127);
+        }
+    return 0;
+}
+
+int oracle_router_mxfp4(const uint16_t* x, const uint8_t* elems, const uint8_t* scales,
+                        const float* bias, int64_t M, int64_t H, int64_t E, int k, int scoring,
+                        int renorm, int32_t* inds, float* weights, float* logits_out,
+                        double* absdot_out)
+{
+    if (M < 0 || H < 32 || E < 1 || k < 1 || k > E) return ORACLE_EINVAL;
+    if (M == 0) return 0;
+    if (!x) return ORACLE_EINVAL;
+    double* w = (double*)malloc((size_t)(E * H) * sizeof(double));
+    float* l = logits_out ? logits_out : (float*)malloc((size_t)(M * E) * sizeof(float));
+    if (!w || !l) {
+        free(w);
+        if (!logits_out) free(l);
+        return ORACLE_ENOMEM;
+    }
+    int rc = oracle_dequant_mxfp4(elems, scales, E, H, w);
+    for (int64_t t = 0; !rc && t < M; ++t)
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0, absacc = 0.0;
+            for (int64_t col = 0; col < H; ++col) {
+                /* bf16 times a 2-bit-mantissa power-of-two multiple: exact in double */
+                double p = bf16_value(x[t * H + col]) * w[e * H + col];
+                acc += p;
+                absacc += fabs(p);
+            }
+            l[t * E + e] = (float)acc;
+            if (absdot_out) absdot_out[t * E + e] = absacc;
+        }
+    if (!rc) rc = oracle_topk_from_logits(l, bias, M, E, k, scoring, renorm, inds, weights);
+    free(w);
+    if (!logits_out) free(l);
     return rc;
 }
 

@@ -43,6 +43,25 @@ int oracle_logits(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, in
 int oracle_topk_from_logits(const float* logits, const float* bias, int64_t M, int64_t E,
                             int k, int scoring, int renorm, int32_t* inds, float* weights);
 
+/* MXFP4 gate weights (OCP Microscaling Formats v1.0).  elems: uint8 [E, H/2],
+ * element i of a row in byte i/2, even i in the low nibble, each an FP4 E2M1
+ * code; scales: uint8 [E, H/32], E8M0: element i of row e is
+ * e2m1(code) * 2^(scales[e, i/32] - 127).  Scales outside
+ * [ORACLE_MX_SCALE_MIN, ORACLE_MX_SCALE_MAX] (every dequantised weight then
+ * is a normal bf16 value, or zero) are refused, as is H % 32 != 0. */
+#define ORACLE_MX_SCALE_MIN 2
+#define ORACLE_MX_SCALE_MAX 252
+double oracle_e2m1_value(int code);
+/* w: [E, H] doubles. */
+int oracle_dequant_mxfp4(const uint8_t* elems, const uint8_t* scales, int64_t E, int64_t H,
+                         double* w);
+/* The router on MXFP4 gate weights: logits[t,e] = fl32(sum_i x[t,i] * w[e,i])
+ * with the dequantised w, then oracle_topk_from_logits. */
+int oracle_router_mxfp4(const uint16_t* x, const uint8_t* elems, const uint8_t* scales,
+                        const float* bias, int64_t M, int64_t H, int64_t E, int k, int scoring,
+                        int renorm, int32_t* inds, float* weights, float* logits_out,
+                        double* absdot_out);
+
 /* The whole router: logits then oracle_topk_from_logits.  logits_out [M,E]
  * and absdot_out [M,E] are optional (NULL). */
 int oracle_router(const uint16_t* x, const uint16_t* w, const float* bias, int64_t M,

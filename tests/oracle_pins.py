@@ -448,6 +448,74 @@ def pin_table_invariants_any_m(o):
         assert sum(bin(int(m)).count("1") for m in mask) == M * k
 
 
+# --------------------------------------------------------------------------
+# MXFP4 gate weights
+# --------------------------------------------------------------------------
+OCP_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # the FP4 E2M1 value table of the MX format
+
+
+def pin_e2m1_table(o):
+    """The 16 E2M1 codes: the format's magnitudes for codes 0..7, sign in bit 3 (code 8 is -0)."""
+    for c in range(16):
+        v = o.e2m1_value(c)
+        sign = -1.0 if c & 8 else 1.0
+        assert v == sign * OCP_E2M1[c & 7] and math.copysign(1.0, v) == sign, (c, v)
+
+
+def _dequant_numpy(elems, scales):
+    """Independent dequantisation: nibbles unpacked low-first, table lookup, ldexp per block."""
+    E, H = elems.shape[0], elems.shape[1] * 2
+    codes = np.empty((E, H), np.int64)
+    codes[:, 0::2] = elems & 15
+    codes[:, 1::2] = elems >> 4
+    mag = np.array(OCP_E2M1)[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    return np.ldexp(mag, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+
+
+def pin_mx_dequant(o):
+    """Dequantised weight = table value x 2^(scale-127), element 2j in the low nibble of byte
+    j, one scale per 32 elements; scales outside [2, 252] and H % 32 != 0 are refused."""
+    rng = np.random.default_rng(31)
+    E, H = 5, 96
+    elems = rng.integers(0, 256, (E, H // 2)).astype(np.uint8)
+    scales = rng.integers(100, 150, (E, H // 32)).astype(np.uint8)
+    w = o.dequant_mxfp4(elems, scales)
+    assert np.array_equal(w, _dequant_numpy(elems, scales))
+    assert w[0, 0] == OCP_E2M1[elems[0, 0] & 7] * (-1 if elems[0, 0] & 8 else 1) * 2.0 ** (int(scales[0, 0]) - 127)
+    for bad in (0, 1, 253, 255):
+        s2 = scales.copy()
+        s2[2, 1] = bad
+        try:
+            o.dequant_mxfp4(elems, s2)
+        except ValueError:
+            continue
+        raise AssertionError(f"scale {bad} accepted")
+    try:
+        o.dequant_mxfp4(elems[:, :20], scales[:, :1])  # H = 40
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("H % 32 != 0 accepted")
+
+
+def pin_mx_router_is_bf16_router_on_dequantised(o):
+    """The MXFP4 router equals the bf16 router (pinned above) on the dequantised weights,
+    which are exact bf16 values: same logits, indices and weight bits, every scoring mode."""
+    from gate_projection_top_amd import workloads as W
+    modes = [(W.SOFTMAX, False, True), (W.SOFTMAX, True, True), (W.SQRT_SOFTPLUS, True, True),
+             (W.SOFTMAX, False, False)]
+    for seed, (scoring, with_bias, renorm) in enumerate(modes):
+        c = W.mxfp4_case(3, H=256, seed=seed, E=64, k=6, scoring=scoring, with_bias=with_bias,
+                         renorm=renorm)
+        wd = _dequant_numpy(c.elems, c.scales).astype(np.float32)
+        wbits = (wd.view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal((wbits.astype(np.uint32) << 16).view(np.float32), wd)  # exact in bf16
+        i1, w1, l1, _ = o.router_mxfp4(c.x, c.elems, c.scales, c.bias, c.k, c.scoring, c.renorm)
+        i2, w2, l2, _ = o.router(c.x, wbits, c.bias, c.k, c.scoring, c.renorm)
+        assert np.array_equal(i1, i2) and np.array_equal(w1.view(np.uint32), w2.view(np.uint32))
+        assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
 ALL_PINS = [
     pin_logits_small_integers, pin_logits_rational, pin_logits_one_hot, pin_logits_blas,
     pin_softplus_closed_forms, pin_softplus_logaddexp, pin_softmax_closed_forms,
@@ -457,4 +525,5 @@ ALL_PINS = [
     pin_renorm_sums_and_softmax_identity, pin_softmax_no_renorm_is_probability,
     pin_table_hand_cases, pin_table_invariants, pin_table_verify_widths,
     pin_table_invariants_any_m,
+    pin_e2m1_table, pin_mx_dequant, pin_mx_router_is_bf16_router_on_dequantised,
 ]

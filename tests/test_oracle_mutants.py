@@ -43,6 +43,11 @@ MUTANTS = [
     ("table_tail_zero", "ids[i] = -1;", "ids[i] = 0;"),
     ("table_mask_overwrite", "token_mask[pos] |= 1 << token;", "token_mask[pos] = 1 << token;"),
     ("table_slot_map_raw", "slot_to_unique[s] = pos;", "slot_to_unique[s] = s;"),
+    ("mx_nibble_order", "int code = (col % 2 == 0) ? (byte & 15) : (byte >> 4);",
+     "int code = (col % 2 == 0) ? (byte >> 4) : (byte & 15);"),
+    ("mx_scale_bias", "ldexp(oracle_e2m1_value(code), sc - 127)", "ldexp(oracle_e2m1_value(code), sc - 128)"),
+    ("e2m1_subnormal_half", "? 0.5 * man", "? 0.25 * man"),
+    ("e2m1_exponent_bias", "ldexp(1.0 + 0.5 * man, ex - 1)", "ldexp(1.0 + 0.5 * man, ex)"),
     ("table_pair_width_only", "int n = M * k;", "int n = (M > 2 ? 2 : M) * k;"),
     ("table_mask_two_tokens", "token_mask[pos] |= 1 << token;", "token_mask[pos] |= 1 << (token & 1);"),
 ]
