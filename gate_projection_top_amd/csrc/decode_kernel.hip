@@ -93,7 +93,22 @@ __device__ __forceinline__ f32x4 poll_sum(const f32x4 (&p)[kMaxS])
     return sum;
 }
 
-template <int kLoadWaves, int kMaxS>
+constexpr int kMxChunk = 2;  // MXFP4 gate: 128-wide k blocks whose loads a wave issues together
+
+// Eight E2M1 codes (one dword, element 0 in the low nibble of byte 0) times a
+// power-of-two scale, as eight bf16 values: gfx950's scaled fp4 -> bf16
+// conversion, two elements per instruction.  Exact for the contract's scales.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t codes, float scale)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int kLoadWaves, int kMaxS, bool kMx>
 __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel(DecodeLaunch a)
 {
     constexpr int kWaves = kLoadWaves + 1;  // + the control wave
@@ -149,32 +164,84 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         // ---- phase 1: partial logits of 16 tokens x 16 experts over one H-split
         const int arow = r * kDecodeTile + (lane & 15);  // MFMA A row  = token
         const int bcol = b * kDecodeTile + (lane & 15);  // MFMA B col  = expert
-        const int kq = (lane >> 4) * 8;                  // this lane's 8 of the 32 k
         const bool arow_ok = arow < a.M;
         const bool bcol_ok = bcol < a.E;
-        const uint16_t* xp = a.x + (int64_t)(arow_ok ? arow : 0) * a.H + kq;
-        const uint16_t* wp = a.w + (int64_t)(bcol_ok ? bcol : 0) * a.H + kq;
-
-        const int KS = (a.H + 31) >> 5;
-        const int ks0 = s * a.ks_per_split;
-        const int ks1 = min(KS, ks0 + a.ks_per_split);
         const bf16x8 zero = __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0});
-
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int base = ks0 + wave; base < ks1; base += kLoadWaves * kChunk) {
-            bf16x8 av[kChunk], bv[kChunk];
+        if constexpr (!kMx) {
+            const int kq = (lane >> 4) * 8;  // this lane's 8 of the 32 k
+            const uint16_t* xp = a.x + (int64_t)(arow_ok ? arow : 0) * a.H + kq;
+            const uint16_t* wp = a.w + (int64_t)(bcol_ok ? bcol : 0) * a.H + kq;
+
+            const int KS = (a.H + 31) >> 5;
+            const int ks0 = s * a.ks_per_split;
+            const int ks1 = min(KS, ks0 + a.ks_per_split);
+
+            for (int base = ks0 + wave; base < ks1; base += kLoadWaves * kChunk) {
+                bf16x8 av[kChunk], bv[kChunk];
 #pragma unroll
-            for (int c = 0; c < kChunk; ++c) {
-                const int ks = base + c * kLoadWaves;
-                const int k0 = ks * 32;
-                const bool in = ks < ks1 && (k0 + kq) < a.H;
-                av[c] = (in && arow_ok) ? load_bf16x8(xp + k0) : zero;
-                bv[c] = (in && bcol_ok) ? load_bf16x8(wp + k0) : zero;
+                for (int c = 0; c < kChunk; ++c) {
+                    const int ks = base + c * kLoadWaves;
+                    const int k0 = ks * 32;
+                    const bool in = ks < ks1 && (k0 + kq) < a.H;
+                    av[c] = (in && arow_ok) ? load_bf16x8(xp + k0) : zero;
+                    bv[c] = (in && bcol_ok) ? load_bf16x8(wp + k0) : zero;
+                }
+#pragma unroll
+                for (int c = 0; c < kChunk; ++c)
+                    if (base + c * kLoadWaves < ks1)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv[c], acc, 0, 0, 0);
             }
+        } else {
+            // MXFP4 gate, in 128-wide k blocks.  Lane (expert, g) loads the 32
+            // codes of k in [128 kb + 32 g, +32) (16 bytes) and their block's
+            // scale; MFMA step j of the block gives k-slots 8g..8g+7 the k
+            // values 128 kb + 32 g + 8 j + (0..7), for X as for W, so every k
+            // is counted once.  (H % 32 == 0: a lane's 32 codes are in or out.)
+            const int g = lane >> 4;
+            const uint16_t* xrow = a.x + (int64_t)(arow_ok ? arow : 0) * a.H;
+            const uint8_t* wrow = a.w_fp4 + (int64_t)(bcol_ok ? bcol : 0) * (a.H / 2);
+            const uint8_t* srow = a.w_scale + (int64_t)(bcol_ok ? bcol : 0) * (a.H / 32);
+            const int KB = (a.H + 127) >> 7;
+            const int kb0 = s * a.ks_per_split;
+            const int kb1 = min(KB, kb0 + a.ks_per_split);
+            for (int base = kb0 + wave; base < kb1; base += kLoadWaves * kMxChunk) {
+                u32x4 wv[kMxChunk];
+                uint32_t sv[kMxChunk];
+                bf16x8 xv[kMxChunk][4];
+                // The gate codes and scales are loaded unconditionally (a lane
+                // outside the shape reads the split's first 32 k of its clamped
+                // row, always in bounds) and masked afterwards: a byte load
+                // under a branch makes the compiler wait for it at the branch's
+                // end.  Activation rows past M stay masked off (their lanes
+                // would break up the coalescing of the real rows' loads), and
+                // the empty asm keeps every load of the batch ahead of the
+                // first MFMA.
 #pragma unroll
-            for (int c = 0; c < kChunk; ++c)
-                if (base + c * kLoadWaves < ks1)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv[c], acc, 0, 0, 0);
+                for (int c = 0; c < kMxChunk; ++c) {
+                    const int kb = base + c * kLoadWaves;
+                    const int k0 = kb * 128 + 32 * g;
+                    const bool in = kb < kb1 && k0 < a.H;
+                    const int kc = in ? k0 : kb0 * 128;
+                    const u32x4 wl = *reinterpret_cast<const u32x4*>(wrow + kc / 2);
+                    const uint32_t sl = srow[kc / 32];
+                    wv[c] = (in && bcol_ok) ? wl : u32x4{0u, 0u, 0u, 0u};
+                    sv[c] = (in && bcol_ok) ? sl : 127u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        xv[c][j] = (in && arow_ok) ? load_bf16x8(xrow + k0 + 8 * j) : zero;
+                }
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int c = 0; c < kMxChunk; ++c) {
+                    if (base + c * kLoadWaves >= kb1) continue;
+                    const float scale = __uint_as_float(sv[c] << 23);  // 2^(s - 127)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[c][j], fp4x8_to_bf16x8(wv[c][j], scale),
+                                                                      acc, 0, 0, 0);
+                }
+            }
         }
         // MFMA 16x16 result layout: lane holds rows 4*(lane/16)+i, column lane%16.
 #pragma unroll
@@ -361,15 +428,24 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream)
     const int R = (a.M + kDecodeTile - 1) / kDecodeTile;
     const int B = (a.E + kDecodeTile - 1) / kDecodeTile;
     const int grid = R * B * a.S;
-    if (a.load_waves == kDecodeNarrow.load_waves && a.S <= kDecodeNarrow.max_splits) {
-        hipLaunchKernelGGL((decode_router_kernel<kDecodeNarrow.load_waves, kDecodeNarrow.max_splits>),
-                           dim3(grid), dim3((kDecodeNarrow.load_waves + 1) * kWave), 0, stream, a);
-    } else if (a.load_waves == kDecodeWide.load_waves && a.S <= kDecodeWide.max_splits) {
-        hipLaunchKernelGGL((decode_router_kernel<kDecodeWide.load_waves, kDecodeWide.max_splits>),
-                           dim3(grid), dim3((kDecodeWide.load_waves + 1) * kWave), 0, stream, a);
-    } else {
+    const bool mx = a.w_fp4 != nullptr;
+    const bool narrow = a.load_waves == kDecodeNarrow.load_waves && a.S <= kDecodeNarrow.max_splits;
+    const bool wide = a.load_waves == kDecodeWide.load_waves && a.S <= kDecodeWide.max_splits;
+    const dim3 nb((kDecodeNarrow.load_waves + 1) * kWave), wb((kDecodeWide.load_waves + 1) * kWave);
+    if (narrow && !mx)
+        hipLaunchKernelGGL((decode_router_kernel<kDecodeNarrow.load_waves, kDecodeNarrow.max_splits, false>),
+                           dim3(grid), nb, 0, stream, a);
+    else if (narrow && mx)
+        hipLaunchKernelGGL((decode_router_kernel<kDecodeNarrow.load_waves, kDecodeNarrow.max_splits, true>),
+                           dim3(grid), nb, 0, stream, a);
+    else if (wide && !mx)
+        hipLaunchKernelGGL((decode_router_kernel<kDecodeWide.load_waves, kDecodeWide.max_splits, false>),
+                           dim3(grid), wb, 0, stream, a);
+    else if (wide && mx)
+        hipLaunchKernelGGL((decode_router_kernel<kDecodeWide.load_waves, kDecodeWide.max_splits, true>),
+                           dim3(grid), wb, 0, stream, a);
+    else
         return hipErrorInvalidValue;
-    }
     return hipGetLastError();
 }
 

@@ -19,7 +19,9 @@ struct TopkLaunch {
 // Decode: M <= 64 tokens.  Grid = R row blocks x B expert blocks x S H-splits.
 struct DecodeLaunch {
     const uint16_t* x;
-    const uint16_t* w;
+    const uint16_t* w;      // bf16 gate [E, H], or NULL with the MXFP4 gate below
+    const uint8_t* w_fp4;   // MXFP4 gate: E2M1 codes [E, H/2], even element in the low nibble
+    const uint8_t* w_scale; // MXFP4 gate: E8M0 scales [E, H/32]
     const float* bias;
     int M, H, E, k, scoring, renorm;
     int32_t* inds;
@@ -32,7 +34,7 @@ struct DecodeLaunch {
     float* partials;        // workspace [S][M][256], every slot kPartialSentinel between calls
     uint32_t* counters;     // workspace, kDecodeCounters words, zero between calls
     int S;                  // H splits
-    int ks_per_split;       // 32-wide k-steps per split
+    int ks_per_split;       // k units per split: 32-wide k-steps (bf16 gate), 128-wide blocks (MXFP4)
     int load_waves;         // geometry: kDecodeNarrow.load_waves or kDecodeWide.load_waves
 };
 

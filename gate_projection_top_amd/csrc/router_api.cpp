@@ -100,13 +100,13 @@ int check_projection(const void* x, const void* w)
 }
 
 // Decode split choice: about the geometry's target workgroup count, with at
-// least one 32-wide k-step per load wave in every split.
-void decode_splits(int M, int H, int E, int* S_out, int* ks_per_split_out, int* load_waves_out)
+// least one k unit (a 32-wide k-step, or a 128-wide MXFP4 block) per load
+// wave in every split.
+void decode_splits(int M, int KS, int E, int* S_out, int* ks_per_split_out, int* load_waves_out)
 {
     const gpt::DecodeGeometry g = gpt::decode_geometry(M);
     const int R = (M + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int B = (E + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
-    const int KS = (H + 31) / 32;
     int S = (g.target_workgroups + R * B - 1) / (R * B);
     const int by_work = KS / g.load_waves > 1 ? KS / g.load_waves : 1;
     if (S > by_work) S = by_work;
@@ -118,10 +118,11 @@ void decode_splits(int M, int H, int E, int* S_out, int* ks_per_split_out, int* 
     *load_waves_out = g.load_waves;
 }
 
-int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
-              int scoring, int renorm, int32_t* inds, float* weights, float* logits,
-              int32_t* t_ids, int32_t* t_mask, int32_t* t_s2u, int32_t* t_count,
-              hipStream_t stream)
+// w_fp4/w_scale non-NULL: the MXFP4 gate (decode sizes only; w is unused).
+int run_fused(const void* x, const void* w, const uint8_t* w_fp4, const uint8_t* w_scale,
+              const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
+              int32_t* inds, float* weights, float* logits, int32_t* t_ids, int32_t* t_mask,
+              int32_t* t_s2u, int32_t* t_count, hipStream_t stream)
 {
     hipError_t e;
     DeviceWorkspace ws;
@@ -131,6 +132,8 @@ int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H,
         gpt::DecodeLaunch a{};
         a.x = static_cast<const uint16_t*>(x);
         a.w = static_cast<const uint16_t*>(w);
+        a.w_fp4 = w_fp4;
+        a.w_scale = w_scale;
         a.bias = bias;
         a.M = (int)M;
         a.H = H;
@@ -147,8 +150,11 @@ int run_fused(const void* x, const void* w, const float* bias, int64_t M, int H,
         a.table_count = t_count;
         a.partials = ws.partials;
         a.counters = ws.counters;
-        decode_splits((int)M, H, E, &a.S, &a.ks_per_split, &a.load_waves);
+        const int units = w_fp4 ? (H + 127) / 128 : (H + 31) / 32;
+        decode_splits((int)M, units, E, &a.S, &a.ks_per_split, &a.load_waves);
         e = gpt::launch_decode(a, stream);
+    } else if (w_fp4) {
+        return ROUTER_ERR_UNSUPPORTED;
     } else {
         gpt::PrefillLaunch a{};
         a.x = static_cast<const uint16_t*>(x);
@@ -200,14 +206,15 @@ int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H
     if (M > 0x7fffffffLL / 256) return ROUTER_ERR_UNSUPPORTED;
     // 32-bit byte offsets inside one 128-row tile of X and inside W
     if ((int64_t)H * 2 * 256 > 0x7fff0000LL) return ROUTER_ERR_UNSUPPORTED;
-    return run_fused(x, w, bias, M, H, E, k, scoring, renorm, out_inds, out_weights,
-                     opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
+    return run_fused(x, w, nullptr, nullptr, bias, M, H, E, k, scoring, renorm, out_inds,
+                     out_weights, opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 // The table is built by the finisher of the single row block, in one wavefront.
 static_assert(ROUTER_TABLE_MAX_M <= gpt::kDecodeTile, "table rows share one row block");
 static_assert(ROUTER_TABLE_MAX_SLOTS <= 64, "table slots fit one wavefront");
 static_assert(ROUTER_TABLE_MAX_M <= ROUTER_DECODE_MAX_M, "table calls take the decode path");
+static_assert(ROUTER_MX_MAX_M <= ROUTER_DECODE_MAX_M, "MXFP4 calls take the decode path");
 
 int router_fwd_route_table(const void* x, const void* w, const float* bias, int M, int H, int E,
                            int k, int scoring, int renorm, int32_t* out_inds, float* out_weights,
@@ -224,9 +231,9 @@ int router_fwd_route_table(const void* x, const void* w, const float* bias, int 
     if (!out_inds || !out_weights || !out_unique_ids || !out_token_mask || !out_slot_to_unique ||
         !out_unique_count)
         return ROUTER_ERR_INVALID_ARGUMENT;
-    return run_fused(x, w, bias, M, H, E, k, scoring, renorm, out_inds, out_weights,
-                     opt_out_logits, out_unique_ids, out_token_mask, out_slot_to_unique,
-                     out_unique_count, stream);
+    return run_fused(x, w, nullptr, nullptr, bias, M, H, E, k, scoring, renorm, out_inds,
+                     out_weights, opt_out_logits, out_unique_ids, out_token_mask,
+                     out_slot_to_unique, out_unique_count, stream);
 }
 
 int router_fwd_m2_table(const void* x, const void* w, const float* bias, int H, int E, int k,
@@ -238,6 +245,23 @@ int router_fwd_m2_table(const void* x, const void* w, const float* bias, int H, 
     return router_fwd_route_table(x, w, bias, 2, H, E, k, scoring, renorm, out_inds, out_weights,
                                   opt_out_logits, out_unique_ids, out_token_mask,
                                   out_slot_to_unique, out_unique_count, stream);
+}
+
+int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale,
+                     const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
+                     int32_t* out_inds, float* out_weights, float* opt_out_logits,
+                     hipStream_t stream)
+{
+    int rc = check_common(M, E, k, scoring, renorm);
+    if (rc == ROUTER_OK) rc = check_hidden(H);
+    if (rc != ROUTER_OK) return rc;
+    if (H % 32 != 0 || M > ROUTER_MX_MAX_M) return ROUTER_ERR_UNSUPPORTED;
+    if (M == 0) return ROUTER_OK;
+    rc = check_projection(x, w_fp4);
+    if (rc != ROUTER_OK) return rc;
+    if (!w_scale || !out_inds || !out_weights) return ROUTER_ERR_INVALID_ARGUMENT;
+    return run_fused(x, nullptr, w_fp4, w_scale, bias, M, H, E, k, scoring, renorm, out_inds,
+                     out_weights, opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 int router_topk_from_logits(const float* logits, const float* bias, int64_t M, int E, int k,
@@ -276,7 +300,7 @@ const char* router_strerror(int code)
     case ROUTER_OK: return "ok";
     case ROUTER_ERR_INVALID_ARGUMENT: return "invalid argument";
     case ROUTER_ERR_UNSUPPORTED: return "shape outside the supported limits";
-    case ROUTER_ERR_MISALIGNED: return "x or w is not 16-byte aligned";
+    case ROUTER_ERR_MISALIGNED: return "x or the gate weights are not 16-byte aligned";
     case ROUTER_ERR_HIP: return "HIP runtime error";
     case ROUTER_ERR_NO_WORKSPACE: return "workspace allocation failed";
     default: return "unknown router error";

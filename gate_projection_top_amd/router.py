@@ -29,9 +29,11 @@ ERR_NO_WORKSPACE = 5
 # router_fwd_route_table limits (ROUTER_TABLE_MAX_M / ROUTER_TABLE_MAX_SLOTS)
 TABLE_MAX_M = 16
 TABLE_MAX_SLOTS = 64
+# router_fwd_mxfp4 limit (ROUTER_MX_MAX_M)
+MX_MAX_M = 64
 
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
-           "router_topk_from_logits",
+           "router_fwd_mxfp4", "router_topk_from_logits",
            "router_set_exchange_timeout_us", "router_strerror")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -63,6 +65,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_fwd_route_table.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                            P, P]
     lib.router_fwd_route_table.restype = i32
+    lib.router_fwd_mxfp4.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.router_fwd_mxfp4.restype = i32
     lib.router_topk_from_logits.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, P]
     lib.router_topk_from_logits.restype = i32
     lib.router_set_exchange_timeout_us.argtypes = [i32]
@@ -159,6 +163,35 @@ def router_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k
                                int(bool(renorm)), _ptr(inds), _ptr(wts), _ptr(logits),
                                _stream(x.device))
     _check(rc, "router_fwd")
+    return (inds, wts, logits) if logits is not None else (inds, wts)
+
+
+def router_fwd_mxfp4(x: torch.Tensor, w_fp4: torch.Tensor, w_scale: torch.Tensor,
+                     bias: Optional[torch.Tensor], k: int, scoring: int = SOFTMAX,
+                     renorm: bool = True, *, return_logits: bool = False,
+                     out_inds=None, out_weights=None, logits_out=None):
+    """Fused router on an MXFP4 gate.  x: bf16 [M,H]; w_fp4: uint8 [E,H/2]
+    (E2M1 codes, even element in the low nibble); w_scale: uint8 [E,H/32]
+    (E8M0 scales, each in [2, 252]); bias: fp32 [E] or None.  M <= MX_MAX_M.
+
+    Returns what router_fwd returns.
+    """
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    _check_tensor(w_fp4, "w_fp4", torch.uint8, 2)
+    _check_tensor(w_scale, "w_scale", torch.uint8, 2)
+    M, H = x.shape
+    E = w_fp4.shape[0]
+    if H % 32 != 0:
+        raise ValueError("the MXFP4 gate needs H % 32 == 0")
+    if tuple(w_fp4.shape) != (E, H // 2) or tuple(w_scale.shape) != (E, H // 32):
+        raise ValueError("w_fp4 must be [E, H/2] and w_scale [E, H/32]")
+    _check_bias(bias, E)
+    inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
+    with torch.cuda.device(x.device):
+        rc = load().router_fwd_mxfp4(_ptr(x), _ptr(w_fp4), _ptr(w_scale), _ptr(bias), M, H, E,
+                                     int(k), int(scoring), int(bool(renorm)), _ptr(inds), _ptr(wts),
+                                     _ptr(logits), _stream(x.device))
+    _check(rc, "router_fwd_mxfp4")
     return (inds, wts, logits) if logits is not None else (inds, wts)
 
 

@@ -18,6 +18,8 @@
  *     sqrt(softplus(logit)) with the stable softplus, selection on score plus
  *     a per-expert bias, unbiased winners' scores renormalised; the BF16 GEMM
  *     with FP32 accumulation and the row-level top-k epilogue;
+ *   - dense_router_decode commit notes, the fused NVFP4 router: the gate
+ *     projection on block-scaled FP4 weights (here OCP MXFP4);
  *   - b70 lab MTP1 M=2 note, "Unique-route router screen": the optional M=2
  *     unique-route table produced inside the router launch (here also at the
  *     other verify widths of qwisp issue #145, "Observation").
@@ -55,7 +57,7 @@
  * on any error nothing is launched and no output byte changes.  The return
  * value is ROUTER_OK or one of the codes below; router_strerror() names it.
  *
- * Concurrency: router_fwd and router_fwd_m2_table use a per-device
+ * Concurrency: the fused entry points (router_fwd*) use a per-device
  * workspace (partial sums and arrival counters).  Calls on one device must be
  * ordered (same stream, or externally synchronised); overlapping calls on
  * one device race on that workspace.  router_topk_from_logits uses none.
@@ -79,6 +81,8 @@ extern "C" {
  * ROUTER_TABLE_MAX_SLOTS = M*k slots (one wavefront builds the table). */
 #define ROUTER_TABLE_MAX_M 16
 #define ROUTER_TABLE_MAX_SLOTS 64
+/* router_fwd_mxfp4: at most this many tokens (the decode kernel). */
+#define ROUTER_MX_MAX_M 64
 
 typedef enum {
     ROUTER_SCORING_SOFTMAX = 0,
@@ -89,7 +93,7 @@ enum {
     ROUTER_OK = 0,
     ROUTER_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad enum, M < 0 */
     ROUTER_ERR_UNSUPPORTED = 2,      /* shape outside the limits above */
-    ROUTER_ERR_MISALIGNED = 3,       /* x or w not 16-byte aligned */
+    ROUTER_ERR_MISALIGNED = 3,       /* x or the gate weights not 16-byte aligned */
     ROUTER_ERR_HIP = 4,              /* a HIP runtime call failed */
     ROUTER_ERR_NO_WORKSPACE = 5      /* workspace could not be allocated */
 };
@@ -148,6 +152,26 @@ int router_fwd_route_table(const void* x, const void* w, const float* bias, int 
                            float* opt_out_logits, int32_t* out_unique_ids,
                            int32_t* out_token_mask, int32_t* out_slot_to_unique,
                            int32_t* out_unique_count, hipStream_t stream);
+
+/* router_fwd with a block-scaled FP4 gate (dense_router_decode commit notes,
+ * the fused NVFP4 block-scaled gate GEMM with the router epilogue; here in
+ * the OCP MXFP4 encoding that gfx950 converts natively):
+ *   w_fp4    uint8 [E, H/2]: FP4 E2M1 codes, element i of a row in byte
+ *            i/2, even i in the low nibble (16-byte aligned);
+ *   w_scale  uint8 [E, H/32]: E8M0 scales; element i of row e is
+ *            e2m1(code) * 2^(w_scale[e, i/32] - 127).
+ * Scales must lie in [2, 252], so that every dequantised weight is zero or
+ * a normal bf16 value; other scales give unspecified (but finite-time and
+ * in-bounds) results.  The logits are then sums of exact bf16 products
+ * accumulated in fp32, as router_fwd's are (in this kernel's own order, so
+ * not bit-identical to router_fwd on the dequantised gate), and everything
+ * after them is the same device routine.
+ * Limits: H % 32 == 0 and M <= ROUTER_MX_MAX_M (the decode kernel), else
+ * ROUTER_ERR_UNSUPPORTED; the rest as router_fwd. */
+int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale,
+                     const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
+                     int32_t* out_inds, float* out_weights, float* opt_out_logits,
+                     hipStream_t stream);
 
 /* Scoring, selection and weights on logits already in HBM (the standalone
  * logits-to-top-k of the unfused pair; dense_router_decode notes, "Current

@@ -136,3 +136,35 @@ def test_topk_rejects(lib, kw, code):
     rc = lib.router_topk_from_logits(a["logits"], None, a["M"], a["E"], a["k"], a["scoring"], 1,
                                      FAKE, FAKE, None)
     assert rc == code, (kw, rc)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scoring=2), R.ERR_INVALID_ARGUMENT),
+    (dict(renorm=3), R.ERR_INVALID_ARGUMENT),
+    (dict(M=-1), R.ERR_INVALID_ARGUMENT),
+    (dict(k=0), R.ERR_INVALID_ARGUMENT),
+    (dict(E=300), R.ERR_UNSUPPORTED),
+    (dict(H=0), R.ERR_INVALID_ARGUMENT),
+    (dict(H=4100), R.ERR_UNSUPPORTED),
+    (dict(H=4104), R.ERR_UNSUPPORTED),      # H % 8 == 0 but not a whole number of 32-blocks
+    (dict(M=R.MX_MAX_M + 1), R.ERR_UNSUPPORTED),
+    (dict(x=None), R.ERR_INVALID_ARGUMENT),
+    (dict(w=None), R.ERR_INVALID_ARGUMENT),
+    (dict(scale=None), R.ERR_INVALID_ARGUMENT),
+    (dict(inds=None), R.ERR_INVALID_ARGUMENT),
+    (dict(weights=None), R.ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE_ODD), R.ERR_MISALIGNED),
+    (dict(w=FAKE_ODD), R.ERR_MISALIGNED),
+])
+def test_mxfp4_rejects(lib, kw, code):
+    a = dict(x=FAKE, w=FAKE, scale=FAKE_ODD, M=4, H=4096, E=256, k=8, scoring=0, renorm=1,
+             inds=FAKE, weights=FAKE)
+    a.update(kw)
+    rc = lib.router_fwd_mxfp4(a["x"], a["w"], a["scale"], None, a["M"], a["H"], a["E"], a["k"],
+                              a["scoring"], a["renorm"], a["inds"], a["weights"], None, None)
+    assert rc == code, (kw, rc)
+
+
+def test_mxfp4_empty_batch_is_ok_without_pointers(lib):
+    assert lib.router_fwd_mxfp4(None, None, None, None, 0, 4096, 256, 8, 0, 1, None, None, None,
+                                None) == R.OK

@@ -1,0 +1,135 @@
+"""router_fwd_mxfp4 (the fused router on a block-scaled FP4 gate) vs the oracle.
+
+Parity rule (b) as for the bf16 gate: the oracle dequantises every MXFP4
+weight exactly and forms the fp64 dot product, the kernel converts the codes
+to bf16 on chip and accumulates in fp32.  Workloads (seeded, synthetic):
+unit-RMS activations, W ~ N(0, 1/H) quantised to MXFP4; decode widths
+M in {1, 2, 4, 8, 16, 64}; H = 4096, 7168 and ragged H (a last 128-block
+with one, two or three 32-blocks); E = 256 and E = 100.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.compare import check_router, check_topk
+from gate_projection_top_amd import router as R
+from gate_projection_top_amd import workloads as W
+from gpu_util import bf16_dev, f32_dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def u8_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def run_mx(case):
+    gi, gw, gl = R.router_fwd_mxfp4(bf16_dev(case.x), u8_dev(case.elems), u8_dev(case.scales),
+                                    f32_dev(case.bias), case.k, case.scoring, case.renorm,
+                                    return_logits=True)
+    torch.cuda.synchronize()
+    return host(gi), host(gw), host(gl)
+
+
+def check_mx(orc, case):
+    say(f"mxfp4 {case.name}")
+    gi, gw, gl = run_mx(case)
+    ref = orc.router_mxfp4(case.x, case.elems, case.scales, case.bias, case.k, case.scoring,
+                           case.renorm)
+    return check_router(orc, case, gi, gw, gl, ref=ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 64])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_decode_widths(orc, M, seed):
+    rep = check_mx(orc, W.mxfp4_case(M, H=4096, seed=seed))
+    assert rep.max_weight_rel_err <= 1e-5
+
+
+@pytest.mark.parametrize("M", [1, 2, 16])
+def test_single_token_shape(orc, M):
+    check_mx(orc, W.mxfp4_case(M, H=7168, seed=3))
+
+
+@pytest.mark.parametrize("H", [32, 96, 544, 576, 1120, 7136])
+def test_ragged_hidden(orc, H):
+    # H % 128 in {32, 64, 96}: a last 128-block holding one, two or three
+    # 32-blocks; H = 32 is a single 32-block in all
+    for M in (1, 5):
+        check_mx(orc, W.mxfp4_case(M, H=H, seed=4))
+
+
+@pytest.mark.parametrize("scoring,with_bias,renorm", [
+    (W.SOFTMAX, False, True), (W.SOFTMAX, True, True), (W.SOFTMAX, False, False),
+    (W.SQRT_SOFTPLUS, True, True), (W.SQRT_SOFTPLUS, False, False)])
+@pytest.mark.parametrize("E,k", [(256, 8), (100, 6), (16, 16)])
+def test_scoring_modes_and_experts(orc, scoring, with_bias, renorm, E, k):
+    for M in (1, 24):
+        check_mx(orc, W.mxfp4_case(M, H=2048, seed=5, E=E, k=k, scoring=scoring,
+                                   with_bias=with_bias, renorm=renorm))
+
+
+def test_scale_extremes(orc):
+    # Blocks at the contract's smallest and largest useful scales, next to
+    # ordinary ones: whole rows at scale 2 (weights down to 2^-126) and single
+    # blocks pushed up by 2^40.
+    case = W.mxfp4_case(4, H=1024, seed=6, E=64, k=8)
+    sc = case.scales.copy()
+    sc[3, :] = 2
+    sc[7, 5] = min(252, int(sc[7, 5]) + 40)
+    sc[9, ::3] = 2
+    case.scales = sc
+    check_mx(orc, case)
+
+
+def test_fused_equals_unfused(orc):
+    # The logits the MXFP4 call returns, routed by router_topk_from_logits,
+    # give bit-identical indices and weights: the same device routine.
+    for case in (W.mxfp4_case(2, H=4096, seed=7, with_bias=True, scoring=W.SQRT_SOFTPLUS, k=6),
+                 W.mxfp4_case(16, H=4096, seed=8)):
+        gi, gw, gl = run_mx(case)
+        ti, tw = R.router_topk_from_logits(torch.from_numpy(gl).cuda(), f32_dev(case.bias), case.k,
+                                           case.scoring, case.renorm)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ti), gi)
+        assert np.array_equal(host(tw).view(np.uint32), gw.view(np.uint32))
+
+
+def test_logits_output_does_not_perturb_and_repeats():
+    case = W.mxfp4_case(8, H=7168, seed=9, with_bias=True)
+    x, we, ws = bf16_dev(case.x), u8_dev(case.elems), u8_dev(case.scales)
+    b = f32_dev(case.bias)
+    i0, w0 = R.router_fwd_mxfp4(x, we, ws, b, case.k, case.scoring, case.renorm)
+    i1, w1, _ = R.router_fwd_mxfp4(x, we, ws, b, case.k, case.scoring, case.renorm, return_logits=True)
+    torch.cuda.synchronize()
+    ref_i, ref_w = host(i0), host(w0)
+    assert np.array_equal(host(i1), ref_i) and np.array_equal(host(w1), ref_w)
+    for _ in range(20):
+        i2, w2 = R.router_fwd_mxfp4(x, we, ws, b, case.k, case.scoring, case.renorm)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(i2), ref_i) and np.array_equal(host(w2), ref_w)
+
+
+def test_interleaved_with_bf16_calls(orc):
+    # bf16 and MXFP4 calls share the decode workspace: alternate them.
+    mx = W.mxfp4_case(4, H=4096, seed=10)
+    bf = W.decode_case(4, H=4096, seed=10)
+    for _ in range(3):
+        check_mx(orc, mx)
+        gi, gw, gl = R.router_fwd(bf16_dev(bf.x), bf16_dev(bf.w), f32_dev(bf.bias), bf.k,
+                                  bf.scoring, bf.renorm, return_logits=True)
+        torch.cuda.synchronize()
+        check_router(orc, bf, host(gi), host(gw), host(gl))
+
+
+def test_empty_batch():
+    case = W.mxfp4_case(1, H=256, seed=0)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    i, w = R.router_fwd_mxfp4(x, u8_dev(case.elems), u8_dev(case.scales), None, 8)
+    assert i.shape == (0, 8) and w.shape == (0, 8)
