@@ -18,7 +18,8 @@ Also reported (same JSON line):
                 sources still match it, else null;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   extras        cache-hot cycle, verify widths M=2/8 at H=4096, the biased M=2
-                table on/off delta, the standalone top-k at M=4096, and the
+                table on/off delta, the MXFP4 gate at M=1 and M=8 (H=7168, a
+                600-matrix 585 MB pool), the standalone top-k at M=4096, and the
                 8192-token prefill (tokens/s, fraction of bf16 MFMA and HBM peak).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
@@ -40,6 +41,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 LAYERS = 40
 POOL = 160
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_M1_H7168_traffic.txt")
+MX_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_mxfp4_M1_H7168_traffic.txt")
 KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
 
 
@@ -52,10 +54,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--section", choices=["all", "decode", "prefill", "topk"], default="all",
+    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "prefill", "topk"], default="all",
                     help="restrict to one workload (for counter-collection runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--mxfp4-widths", default="1,8",
+                    help="token counts of the MXFP4 section (comma-separated, each <= 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
@@ -69,11 +73,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """Bytes per decode launch from the committed counter summary, if it still applies."""
+def committed_traffic(path=TRAFFIC_SUMMARY):
+    """Bytes per decode launch from a committed counter summary, if it still applies."""
     try:
         fields = {}
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -185,6 +189,8 @@ def main():
         decode_headline(torch, R, W, dev, args, out)
     if args.section in ("all",):
         out["extras"].update(decode_extras(torch, R, W, dev, args))
+    if args.section in ("all", "mxfp4"):
+        out["extras"].update(mxfp4_extras(torch, R, W, dev, args))
     if args.section in ("all", "topk"):
         out["extras"].update(topk_extras(torch, R, W, dev, args))
     if args.section in ("all", "prefill"):
@@ -301,6 +307,38 @@ def decode_extras(torch, R, W, dev, args):
             for l in range(LAYERS)]
         ex[f"biased_M{M}_k6_us_per_call"] = round(graph_call_us(torch, calls, args.steps, args.warmup), 3)
     log("biased router done")
+    return ex
+
+
+def mxfp4_extras(torch, R, W, dev, args):
+    """router_fwd_mxfp4 at M=1 and M=8, H=7168: 40 calls per step, each with
+    its own MXFP4 gate from a 600-matrix pool (585 MB, cold)."""
+    ex = {}
+    H, E, k, pool = 7168, 256, 8, 600
+    codes, scales = W.torch_mxfp4_gate(pool, E, H, seed=30, device=dev)
+    groups = pool // LAYERS
+    for M in [int(m) for m in args.mxfp4_widths.split(",")]:
+        x = W.torch_rms_normalised_bf16((LAYERS, M, H), seed=31 + M, device=dev)
+        oi = torch.empty((LAYERS, M, k), dtype=torch.int32, device=dev)
+        ow = torch.empty((LAYERS, M, k), dtype=torch.float32, device=dev)
+
+        def call(l, widx, x=x, oi=oi, ow=ow):
+            return lambda: R.router_fwd_mxfp4(x[l], codes[widx], scales[widx], None, k, W.SOFTMAX,
+                                              True, out_inds=oi[l], out_weights=ow[l])
+
+        graphs = [GraphTimer(torch, [call(l, g * LAYERS + l) for l in range(LAYERS)])
+                  for g in range(groups)]
+        wall, ev_ms = timed_replays(torch, graphs, args.steps, args.warmup)
+        launch_us = ev_ms * 1e3 / (args.steps * LAYERS)
+        ex[f"mxfp4_decode_M{M}_H7168_us_per_call"] = round(wall * 1e6 / (args.steps * LAYERS), 3)
+        ex[f"mxfp4_decode_M{M}_H7168_launch_us"] = round(launch_us, 3)
+        if M == 1:
+            algo = E * H // 2 + E * H // 32 + M * H * 2 + M * k * 8  # codes + scales + x + outputs
+            ex["mxfp4_decode_M1_bytes_per_launch"] = algo
+            ex["mxfp4_decode_M1_hbm_frac"] = round(algo / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            ex["mxfp4_decode_M1_traffic"] = committed_traffic(MX_TRAFFIC_SUMMARY)
+        del graphs
+    log("mxfp4 done")
     return ex
 
 

@@ -205,37 +205,48 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
             const int KB = (a.H + 127) >> 7;
             const int kb0 = s * a.ks_per_split;
             const int kb1 = min(KB, kb0 + a.ks_per_split);
-            for (int base = kb0 + wave; base < kb1; base += kLoadWaves * kMxChunk) {
+            const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+            for (int base = kb0 + wave_u; base < kb1; base += kLoadWaves * kMxChunk) {
                 u32x4 wv[kMxChunk];
                 uint32_t sv[kMxChunk];
+                bool wok[kMxChunk];
                 bf16x8 xv[kMxChunk][4];
-                // The gate codes and scales are loaded unconditionally (a lane
-                // outside the shape reads the split's first 32 k of its clamped
-                // row, always in bounds) and masked afterwards: a byte load
-                // under a branch makes the compiler wait for it at the branch's
-                // end.  Activation rows past M stay masked off (their lanes
-                // would break up the coalescing of the real rows' loads), and
-                // the empty asm keeps every load of the batch ahead of the
-                // first MFMA.
+                // A block past the split is skipped by a wave-uniform branch.
+                // Inside one, the gate codes and scale are loaded by every
+                // lane (a lane past E or H reads its clamped row's first 32 k
+                // of the block, always in bounds) and masked after the batch,
+                // through a zero scale: a byte load under a per-lane branch,
+                // or a select on a loaded value ahead of the next loads, makes
+                // the compiler wait for the load there.  Activation rows past
+                // M stay masked off (their lanes would break up the
+                // coalescing of the real rows' loads).  The empty asm keeps
+                // every load of the batch ahead of the first MFMA.
 #pragma unroll
                 for (int c = 0; c < kMxChunk; ++c) {
                     const int kb = base + c * kLoadWaves;
-                    const int k0 = kb * 128 + 32 * g;
-                    const bool in = kb < kb1 && k0 < a.H;
-                    const int kc = in ? k0 : kb0 * 128;
-                    const u32x4 wl = *reinterpret_cast<const u32x4*>(wrow + kc / 2);
-                    const uint32_t sl = srow[kc / 32];
-                    wv[c] = (in && bcol_ok) ? wl : u32x4{0u, 0u, 0u, 0u};
-                    sv[c] = (in && bcol_ok) ? sl : 127u;
+                    wv[c] = u32x4{0u, 0u, 0u, 0u};
+                    sv[c] = 0u;
+                    wok[c] = false;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        xv[c][j] = (in && arow_ok) ? load_bf16x8(xrow + k0 + 8 * j) : zero;
+                    for (int j = 0; j < 4; ++j) xv[c][j] = zero;
+                    if (kb < kb1) {
+                        const int k0 = kb * 128 + 32 * g;
+                        const bool in = k0 < a.H;
+                        const int kc = in ? k0 : kb * 128;
+                        wv[c] = *reinterpret_cast<const u32x4*>(wrow + kc / 2);
+                        sv[c] = srow[kc / 32];
+                        wok[c] = in && bcol_ok;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (in && arow_ok) xv[c][j] = load_bf16x8(xrow + k0 + 8 * j);
+                    }
                 }
                 asm volatile("" ::: "memory");
 #pragma unroll
                 for (int c = 0; c < kMxChunk; ++c) {
                     if (base + c * kLoadWaves >= kb1) continue;
-                    const float scale = __uint_as_float(sv[c] << 23);  // 2^(s - 127)
+                    // 2^(s - 127); zero for a lane outside the gate
+                    const float scale = wok[c] ? __uint_as_float(sv[c] << 23) : 0.0f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[c][j], fp4x8_to_bf16x8(wv[c][j], scale),

@@ -387,3 +387,17 @@ def torch_uniform_f32(n: int, lo: float, hi: float, seed: int, device):
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return torch.rand(n, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
+
+
+def torch_mxfp4_gate(n: int, E: int, H: int, seed: int, device, scale_lo: int = 117, scale_hi: int = 122):
+    """n MXFP4 gate matrices on `device`: code bytes uniform over 0..255 (every
+    E2M1 code equally likely in both nibbles) [n, E, H/2], and E8M0 scale bytes
+    uniform over scale_lo..scale_hi [n, E, H/32] (the block scales that
+    quantising N(0, 1/H) weights at H = 4096..7168 produces)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    codes = torch.randint(0, 256, (n, E, H // 2), generator=g, device=device, dtype=torch.uint8)
+    scales = torch.randint(scale_lo, scale_hi + 1, (n, E, H // 32), generator=g, device=device,
+                           dtype=torch.uint8)
+    return codes, scales
