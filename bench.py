@@ -19,7 +19,8 @@ Also reported (same JSON line):
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   extras        cache-hot cycle, verify widths M=2/8 at H=4096, the biased M=2
                 table on/off delta, the MXFP4 gate at M=1 and M=8 (H=7168, a
-                600-matrix 585 MB pool), the standalone top-k at M=4096, and the
+                600-matrix 585 MB pool) and at the 8192-token prefill, the
+                standalone top-k at M=4096, and the
                 8192-token prefill (tokens/s, fraction of bf16 MFMA and HBM peak).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
@@ -338,6 +339,22 @@ def mxfp4_extras(torch, R, W, dev, args):
             ex["mxfp4_decode_M1_hbm_frac"] = round(algo / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
             ex["mxfp4_decode_M1_traffic"] = committed_traffic(MX_TRAFFIC_SUMMARY)
         del graphs
+    del codes, scales
+    # prefill: M=8192 tokens over four cold 117 MB activations, one MXFP4 gate
+    M = 8192
+    xs = W.torch_gaussian_bf16((4, M, H), 1.0, seed=35, device=dev)
+    pc, psc = W.torch_mxfp4_gate(1, E, H, seed=36, device=dev)
+    bp = W.torch_uniform_f32(E, -0.02, 0.02, seed=37, device=dev)
+    pi = torch.empty((M, k), dtype=torch.int32, device=dev)
+    pw = torch.empty((M, k), dtype=torch.float32, device=dev)
+    calls = [(lambda i=i: R.router_fwd_mxfp4(xs[i], pc[0], psc[0], bp, k, W.SOFTMAX, True,
+                                             out_inds=pi, out_weights=pw)) for i in range(4)]
+    p_us = graph_call_us(torch, calls, max(args.steps // 2, 2), 2)
+    tflops = 2.0 * M * E * H / (p_us * 1e-6) / 1e12
+    ex["mxfp4_prefill_M8192_H7168_event_us_per_call"] = round(p_us, 2)
+    ex["mxfp4_prefill_M8192_tokens_per_s"] = round(M / (p_us * 1e-6), 0)
+    ex["mxfp4_prefill_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
+    del xs
     log("mxfp4 done")
     return ex
 

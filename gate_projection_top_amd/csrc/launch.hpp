@@ -40,7 +40,9 @@ struct DecodeLaunch {
 
 struct PrefillLaunch {
     const uint16_t* x;
-    const uint16_t* w;
+    const uint16_t* w;      // bf16 gate [E, H], or NULL with the MXFP4 gate below
+    const uint8_t* w_fp4;   // MXFP4 gate: E2M1 codes [E, H/2] (H % 128 == 0)
+    const uint8_t* w_scale; // MXFP4 gate: E8M0 scales [E, H/32], 4-byte aligned
     const float* bias;
     int64_t M;
     int H, E, k, scoring, renorm;

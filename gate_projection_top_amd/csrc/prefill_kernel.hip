@@ -59,6 +59,13 @@ constexpr int kTileBytes = kBM * kTileStride * 4;
 constexpr int kRingBytes = kWRingOffset + kWSlots * kWStageBytes;
 constexpr int kLdsBytes = kRingBytes;
 constexpr int kFlagOffset = kLdsBytes - 16;  // one int after the ring's last use
+// MXFP4 gate: a W stage holds 256 rows of 32 code bytes (64 k) and a scale
+// stage one dword per expert (the aligned dword holding the stage's two
+// block scales); the X ring is unchanged.
+constexpr int kWStageBytesMx = kBN * kBK / 2;                     // 8 KiB
+constexpr int kSStageBytes = kBN * 4;                            // 1 KiB
+constexpr int kSRingOffset = kWRingOffset + kWSlots * kWStageBytesMx;
+static_assert(kSRingOffset + kWSlots * kSStageBytes <= kRingBytes, "MXFP4 rings fit the LDS ring");
 static_assert(kTileBytes <= kFlagOffset, "row tile and flag overlap");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -80,10 +87,18 @@ constexpr int kOutOfRange = 0x7ffffff0;  // past every descriptor limit: loads r
 // and E (W limit).
 struct DmaPlan {
     __amdgpu_buffer_rsrc_t x;  // this tile's rows of X
-    __amdgpu_buffer_rsrc_t w;  // all of W
+    __amdgpu_buffer_rsrc_t w;  // all of W (bf16), or all the MXFP4 codes
+    __amdgpu_buffer_rsrc_t sc; // MXFP4 scales
     int a_off[kDmaA], a_k[kDmaA];
     int b_off[kDmaB], b_k[kDmaB];
+    int m_off, m_k;            // MXFP4 codes: this lane's 16 bytes (one 32-block) of a stage
+    int s_off;                 // MXFP4 scales: this lane's expert row (lanes < 32)
 };
+
+// MXFP4 code rows are 32 bytes (two 16-byte halves, one 32-block each); half
+// h of row R sits in physical half h ^ sw2(R), so the 16 rows of a fragment
+// read at one k spread over all banks.
+__device__ __forceinline__ int half_swizzle(int R) { return (R >> 3) & 1; }
 
 // One 1 KiB direct-to-LDS load (lane i's 16 bytes to lds + 16 i).  Written as
 // inline asm so that the compiler does not track it: its waitcnt pass would
@@ -94,6 +109,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int byte_off, un
 {
     const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)lds);
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(byte_off), "s"(r), "{m0}"(m0) : "memory");
+}
+
+// One 256-byte direct-to-LDS dword load (lane i's 4 bytes to lds + 4 i).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, int byte_off, unsigned char* lds)
+{
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)lds);
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(byte_off), "s"(r), "{m0}"(m0) : "memory");
 }
 
 __device__ __forceinline__ void issue_x(const DmaPlan& d, unsigned char* slot, int k0, int H, int wave)
@@ -112,6 +134,18 @@ __device__ __forceinline__ void issue_w(const DmaPlan& d, unsigned char* slot, i
         const int off = (k0 + d.b_k[j] < H) ? d.b_off[j] + k0 * 2 : kOutOfRange;
         dma16(d.w, off, slot + (wave * kDmaB + j) * 1024);
     }
+}
+
+// MXFP4 stage: every wave loads 1 KiB of codes (32 rows) and, with its
+// first 32 lanes, the scale dwords of 32 experts.  Per wave and stage: two
+// loads, whatever the lane mask.
+__device__ __forceinline__ void issue_w_mx(const DmaPlan& d, unsigned char* wslot, unsigned char* sslot, int k0,
+                                           int H, int wave, int lane)
+{
+    const int off = (k0 + d.m_k < H) ? d.m_off + k0 / 2 : kOutOfRange;
+    dma16(d.w, off, wslot + wave * 1024);
+    // the stage's two scales (k0 / 32 is even) lie in the aligned dword at k0 / 32 & ~3
+    if (lane < 32) dma4(d.sc, d.s_off + ((k0 >> 5) & ~3), sslot + wave * 128);
 }
 
 // Workgroup barrier for the LDS ring.  Each wave has already waited (vmcnt)
@@ -362,6 +396,7 @@ __device__ __forceinline__ void exchange_and_route(const PrefillLaunch& p, float
     }
 }
 
+template <bool kMx>
 __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch p)
 {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
@@ -407,7 +442,17 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
         const int64_t rows_here = min((int64_t)kBM, p.M - row0);
         d.x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + row0 * p.H), 0,
                                                 (int)(rows_here * p.H * 2), 0x00020000);
-        d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), 0, p.E * p.H * 2, 0x00020000);
+        if constexpr (kMx) {
+            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_fp4), 0, p.E * (p.H / 2), 0x00020000);
+            d.sc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_scale), 0, p.E * (p.H / 32),
+                                                     0x00020000);
+            const int R = wave * 32 + (lane >> 1);
+            d.m_k = ((lane & 1) ^ half_swizzle(R)) * 32;
+            d.m_off = R * (p.H / 2) + d.m_k / 2;
+            d.s_off = (wave * 32 + (lane & 31)) * (p.H / 32);
+        } else {
+            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), 0, p.E * p.H * 2, 0x00020000);
+        }
         const int li = lane >> 3, ls = lane & 7;
 #pragma unroll
         for (int j = 0; j < kDmaA; ++j) {
@@ -436,26 +481,41 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
     // ks-1 are outstanding (they were all issued after W[ks]).
     unsigned char* const xring = lds;
     unsigned char* const wring = lds + kWRingOffset;
+    unsigned char* const sring = lds + kSRingOffset;
+    constexpr int kWLoads = kMx ? 2 : kDmaB;          // W loads per wave and stage
+    constexpr int kIterLoads = kDmaA + kWLoads;       // loads per wave and iteration
     auto issue_iteration = [&](int j) {
         if (j + 3 >= 0 && j + 3 < nstages)
             issue_x(d, xring + ((j + 3) % kXSlots) * kXStageBytes, k_begin + (j + 3) * kBK, p.H, wave);
-        if (j + 2 >= 0 && j + 2 < nstages)
-            issue_w(d, wring + ((j + 2) % kWSlots) * kWStageBytes, k_begin + (j + 2) * kBK, p.H, wave);
+        if (j + 2 >= 0 && j + 2 < nstages) {
+            if constexpr (kMx)
+                issue_w_mx(d, wring + ((j + 2) % kWSlots) * kWStageBytesMx,
+                           sring + ((j + 2) % kWSlots) * kSStageBytes, k_begin + (j + 2) * kBK, p.H, wave, lane);
+            else
+                issue_w(d, wring + ((j + 2) % kWSlots) * kWStageBytes, k_begin + (j + 2) * kBK, p.H, wave);
+        }
     };
     issue_iteration(-3);
     issue_iteration(-2);
     issue_iteration(-1);
     for (int ks = 0; ks < nstages; ++ks) {
         if (ks + 2 < nstages)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaA + kDmaB));  // vmcnt(6)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | kIterLoads);  // iteration ks-1's loads may be in flight
         else if (ks + 1 < nstages)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaB);            // vmcnt(4): only W[ks+1] after W[ks]
+            __builtin_amdgcn_s_waitcnt(0x0F70 | kWLoads);     // only W[ks+1] after W[ks]
         else
-            __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+            __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
         ring_barrier();
         issue_iteration(ks);
         const unsigned char* xs = xring + (ks % kXSlots) * kXStageBytes;
-        const unsigned char* ws = wring + (ks % kWSlots) * kWStageBytes;
+        const unsigned char* ws = wring + (ks % kWSlots) * (kMx ? kWStageBytesMx : kWStageBytes);
+        // MXFP4: the scale pair of expert R is bytes sb0, sb0 + 1 of its dword
+        const unsigned char* ss = sring + (ks % kWSlots) * kSStageBytes + (((k_begin + ks * kBK) >> 5) & 3);
+        uint32_t spair[4];
+        if constexpr (kMx) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) spair[j] = *reinterpret_cast<const uint16_t*>(ss + b_row[j] * 4);
+        }
 #pragma unroll
         for (int kk = 0; kk < kBK / 32; ++kk) {
             const int c = kk * 4 + g;
@@ -465,9 +525,18 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
                 af[i] = *reinterpret_cast<const bf16x8*>(xs + a_row[i] * kRowBytes +
                                                           ((c ^ slot_swizzle(a_row[i])) << 4));
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(ws + b_row[j] * kRowBytes +
-                                                           ((c ^ slot_swizzle(b_row[j])) << 4));
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (kMx) {
+                    // codes k = 32 kk + 8 g .. +7 of expert b_row[j]: dword g of half kk
+                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(
+                        ws + b_row[j] * (kBK / 2) + ((kk ^ half_swizzle(b_row[j])) << 4) + 4 * g);
+                    const uint32_t sbyte = (spair[j] >> (8 * kk)) & 0xffu;
+                    bfr[j] = fp4x8_to_bf16x8(codes, __uint_as_float(sbyte << 23));
+                } else {
+                    bfr[j] = *reinterpret_cast<const bf16x8*>(ws + b_row[j] * kRowBytes +
+                                                               ((c ^ slot_swizzle(b_row[j])) << 4));
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -525,7 +594,10 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream)
     const int64_t tiles = (a.M + kBM - 1) / kBM;
     const int64_t padded = (tiles + kXcds - 1) / kXcds * kXcds;
     const int64_t blocks = padded * a.S;
-    hipLaunchKernelGGL(prefill_router_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    if (a.w_fp4)
+        hipLaunchKernelGGL(prefill_router_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(prefill_router_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -634,4 +634,17 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// Eight E2M1 codes (one dword, element 0 in the low nibble of byte 0) times a
+// power-of-two scale, as eight bf16 values: gfx950's scaled fp4 -> bf16
+// conversion, two elements per instruction.  Exact for the contract's scales.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t codes, float scale)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 }  // namespace gpt

@@ -118,7 +118,7 @@ void decode_splits(int M, int KS, int E, int* S_out, int* ks_per_split_out, int*
     *load_waves_out = g.load_waves;
 }
 
-// w_fp4/w_scale non-NULL: the MXFP4 gate (decode sizes only; w is unused).
+// w_fp4/w_scale non-NULL: the MXFP4 gate (w is unused).
 int run_fused(const void* x, const void* w, const uint8_t* w_fp4, const uint8_t* w_scale,
               const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
               int32_t* inds, float* weights, float* logits, int32_t* t_ids, int32_t* t_mask,
@@ -153,12 +153,12 @@ int run_fused(const void* x, const void* w, const uint8_t* w_fp4, const uint8_t*
         const int units = w_fp4 ? (H + 127) / 128 : (H + 31) / 32;
         decode_splits((int)M, units, E, &a.S, &a.ks_per_split, &a.load_waves);
         e = gpt::launch_decode(a, stream);
-    } else if (w_fp4) {
-        return ROUTER_ERR_UNSUPPORTED;
     } else {
         gpt::PrefillLaunch a{};
         a.x = static_cast<const uint16_t*>(x);
         a.w = static_cast<const uint16_t*>(w);
+        a.w_fp4 = w_fp4;
+        a.w_scale = w_scale;
         a.bias = bias;
         a.M = M;
         a.H = H;
@@ -214,7 +214,6 @@ int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H
 static_assert(ROUTER_TABLE_MAX_M <= gpt::kDecodeTile, "table rows share one row block");
 static_assert(ROUTER_TABLE_MAX_SLOTS <= 64, "table slots fit one wavefront");
 static_assert(ROUTER_TABLE_MAX_M <= ROUTER_DECODE_MAX_M, "table calls take the decode path");
-static_assert(ROUTER_MX_MAX_M <= ROUTER_DECODE_MAX_M, "MXFP4 calls take the decode path");
 
 int router_fwd_route_table(const void* x, const void* w, const float* bias, int M, int H, int E,
                            int k, int scoring, int renorm, int32_t* out_inds, float* out_weights,
@@ -255,11 +254,17 @@ int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale
     int rc = check_common(M, E, k, scoring, renorm);
     if (rc == ROUTER_OK) rc = check_hidden(H);
     if (rc != ROUTER_OK) return rc;
-    if (H % 32 != 0 || M > ROUTER_MX_MAX_M) return ROUTER_ERR_UNSUPPORTED;
+    if (H % 32 != 0) return ROUTER_ERR_UNSUPPORTED;
+    // the prefill kernel moves a 64-wide stage's two scales as one aligned dword
+    if (M > ROUTER_DECODE_MAX_M && H % 128 != 0) return ROUTER_ERR_UNSUPPORTED;
     if (M == 0) return ROUTER_OK;
     rc = check_projection(x, w_fp4);
     if (rc != ROUTER_OK) return rc;
     if (!w_scale || !out_inds || !out_weights) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (M > ROUTER_DECODE_MAX_M && ((uintptr_t)w_scale & 3u) != 0) return ROUTER_ERR_MISALIGNED;
+    if (M > 0x7fffffffLL / 256) return ROUTER_ERR_UNSUPPORTED;
+    // 32-bit byte offsets inside one 128-row tile of X
+    if ((int64_t)H * 2 * 256 > 0x7fff0000LL) return ROUTER_ERR_UNSUPPORTED;
     return run_fused(x, nullptr, w_fp4, w_scale, bias, M, H, E, k, scoring, renorm, out_inds,
                      out_weights, opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
 }

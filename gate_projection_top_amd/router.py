@@ -29,8 +29,8 @@ ERR_NO_WORKSPACE = 5
 # router_fwd_route_table limits (ROUTER_TABLE_MAX_M / ROUTER_TABLE_MAX_SLOTS)
 TABLE_MAX_M = 16
 TABLE_MAX_SLOTS = 64
-# router_fwd_mxfp4 limit (ROUTER_MX_MAX_M)
-MX_MAX_M = 64
+# router_fwd runs the decode kernel up to this many tokens (ROUTER_DECODE_MAX_M)
+DECODE_MAX_M = 64
 
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
            "router_fwd_mxfp4", "router_topk_from_logits",
@@ -172,7 +172,8 @@ def router_fwd_mxfp4(x: torch.Tensor, w_fp4: torch.Tensor, w_scale: torch.Tensor
                      out_inds=None, out_weights=None, logits_out=None):
     """Fused router on an MXFP4 gate.  x: bf16 [M,H]; w_fp4: uint8 [E,H/2]
     (E2M1 codes, even element in the low nibble); w_scale: uint8 [E,H/32]
-    (E8M0 scales, each in [2, 252]); bias: fp32 [E] or None.  M <= MX_MAX_M.
+    (E8M0 scales, each in [2, 252]); bias: fp32 [E] or None.  H % 32 == 0, and
+    H % 128 == 0 when M > DECODE_MAX_M.
 
     Returns what router_fwd returns.
     """

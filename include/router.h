@@ -81,8 +81,6 @@ extern "C" {
  * ROUTER_TABLE_MAX_SLOTS = M*k slots (one wavefront builds the table). */
 #define ROUTER_TABLE_MAX_M 16
 #define ROUTER_TABLE_MAX_SLOTS 64
-/* router_fwd_mxfp4: at most this many tokens (the decode kernel). */
-#define ROUTER_MX_MAX_M 64
 
 typedef enum {
     ROUTER_SCORING_SOFTMAX = 0,
@@ -93,7 +91,7 @@ enum {
     ROUTER_OK = 0,
     ROUTER_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad enum, M < 0 */
     ROUTER_ERR_UNSUPPORTED = 2,      /* shape outside the limits above */
-    ROUTER_ERR_MISALIGNED = 3,       /* x or the gate weights not 16-byte aligned */
+    ROUTER_ERR_MISALIGNED = 3,       /* x or the gate weights not aligned as stated */
     ROUTER_ERR_HIP = 4,              /* a HIP runtime call failed */
     ROUTER_ERR_NO_WORKSPACE = 5      /* workspace could not be allocated */
 };
@@ -159,15 +157,17 @@ int router_fwd_route_table(const void* x, const void* w, const float* bias, int 
  *   w_fp4    uint8 [E, H/2]: FP4 E2M1 codes, element i of a row in byte
  *            i/2, even i in the low nibble (16-byte aligned);
  *   w_scale  uint8 [E, H/32]: E8M0 scales; element i of row e is
- *            e2m1(code) * 2^(w_scale[e, i/32] - 127).
+ *            e2m1(code) * 2^(w_scale[e, i/32] - 127) (4-byte aligned when
+ *            M > ROUTER_DECODE_MAX_M, else ROUTER_ERR_MISALIGNED).
  * Scales must lie in [2, 252], so that every dequantised weight is zero or
  * a normal bf16 value; other scales give unspecified (but finite-time and
  * in-bounds) results.  The logits are then sums of exact bf16 products
  * accumulated in fp32, as router_fwd's are (in this kernel's own order, so
  * not bit-identical to router_fwd on the dequantised gate), and everything
  * after them is the same device routine.
- * Limits: H % 32 == 0 and M <= ROUTER_MX_MAX_M (the decode kernel), else
- * ROUTER_ERR_UNSUPPORTED; the rest as router_fwd. */
+ * Limits: H % 32 == 0, and H % 128 == 0 when M > ROUTER_DECODE_MAX_M (the
+ * prefill kernel), else ROUTER_ERR_UNSUPPORTED; the rest as router_fwd.
+ * The decode/prefill split is router_fwd's. */
 int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale,
                      const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
                      int32_t* out_inds, float* out_weights, float* opt_out_logits,

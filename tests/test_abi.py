@@ -147,7 +147,8 @@ def test_topk_rejects(lib, kw, code):
     (dict(H=0), R.ERR_INVALID_ARGUMENT),
     (dict(H=4100), R.ERR_UNSUPPORTED),
     (dict(H=4104), R.ERR_UNSUPPORTED),      # H % 8 == 0 but not a whole number of 32-blocks
-    (dict(M=R.MX_MAX_M + 1), R.ERR_UNSUPPORTED),
+    (dict(M=R.DECODE_MAX_M + 1, H=4128), R.ERR_UNSUPPORTED),  # prefill needs H % 128 == 0
+    (dict(M=R.DECODE_MAX_M + 1, scale=ctypes.c_void_p(0x1002)), R.ERR_MISALIGNED),
     (dict(x=None), R.ERR_INVALID_ARGUMENT),
     (dict(w=None), R.ERR_INVALID_ARGUMENT),
     (dict(scale=None), R.ERR_INVALID_ARGUMENT),

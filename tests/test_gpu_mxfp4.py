@@ -1,11 +1,13 @@
 """router_fwd_mxfp4 (the fused router on a block-scaled FP4 gate) vs the oracle.
 
 Parity rule (b) as for the bf16 gate: the oracle dequantises every MXFP4
-weight exactly and forms the fp64 dot product, the kernel converts the codes
-to bf16 on chip and accumulates in fp32.  Workloads (seeded, synthetic):
+weight exactly and forms the fp64 dot product, the kernels convert the codes
+to bf16 on chip and accumulate in fp32.  Workloads (seeded, synthetic):
 unit-RMS activations, W ~ N(0, 1/H) quantised to MXFP4; decode widths
 M in {1, 2, 4, 8, 16, 64}; H = 4096, 7168 and ragged H (a last 128-block
-with one, two or three 32-blocks); E = 256 and E = 100.
+with one, two or three 32-blocks); E = 256, 100 and 16; prefill sizes
+M in {65, 100, 333, 1000} (four K splits), 10000 (two) and 20000 (one), and
+M = 8192, H = 7168 on sampled rows.
 """
 import numpy as np
 import pytest
@@ -88,11 +90,74 @@ def test_scale_extremes(orc):
     check_mx(orc, case)
 
 
+@pytest.mark.parametrize("M", [65, 100, 333, 1000])
+@pytest.mark.parametrize("scoring,with_bias", [(W.SOFTMAX, True), (W.SOFTMAX, False),
+                                               (W.SQRT_SOFTPLUS, True)])
+def test_prefill_ragged(orc, M, scoring, with_bias):
+    check_mx(orc, W.mxfp4_case(M, H=1024, seed=M, scoring=scoring, with_bias=with_bias))
+
+
+@pytest.mark.parametrize("M,H", [(10000, 256), (20000, 128)])
+def test_prefill_two_and_one_splits(orc, M, H):
+    """10000 rows = 79 tiles (two K splits); 20000 rows = 157 tiles (no split)."""
+    check_mx(orc, W.mxfp4_case(M, H=H, seed=M, with_bias=True))
+
+
+@pytest.mark.parametrize("E,k,scoring", [(100, 6, W.SQRT_SOFTPLUS), (16, 16, W.SOFTMAX)])
+def test_prefill_experts(orc, E, k, scoring):
+    check_mx(orc, W.mxfp4_case(300, H=512, seed=E, E=E, k=k, scoring=scoring, with_bias=True))
+
+
+def test_prefill_scale_extremes(orc):
+    case = W.mxfp4_case(130, H=1024, seed=16, E=64, k=8)
+    sc = case.scales.copy()
+    sc[3, :] = 2
+    sc[7, 5] = min(252, int(sc[7, 5]) + 40)
+    sc[9, ::3] = 2
+    case.scales = sc
+    check_mx(orc, case)
+
+
+def test_prefill_handover_path_matches(orc):
+    """Zero exchange wait: every split but the last hands its rows over; results unchanged."""
+    case = W.mxfp4_case(200, H=1024, seed=17, with_bias=True)
+    args = (bf16_dev(case.x), u8_dev(case.elems), u8_dev(case.scales), f32_dev(case.bias), case.k,
+            case.scoring, case.renorm)
+    say("mxfp4 prefill hand-over M=200")
+    ref = R.router_fwd_mxfp4(*args, return_logits=True)
+    try:
+        R.set_exchange_timeout_us(0)
+        got = R.router_fwd_mxfp4(*args, return_logits=True)
+        torch.cuda.synchronize()
+    finally:
+        R.set_exchange_timeout_us(200)
+    for a, g in zip(ref, got):
+        assert torch.equal(a.view(torch.int32), g.view(torch.int32))
+    check_router(orc, case, host(got[0]), host(got[1]), host(got[2]),
+                 ref=orc.router_mxfp4(case.x, case.elems, case.scales, case.bias, case.k,
+                                      case.scoring, case.renorm))
+
+
+@pytest.mark.slow
+def test_prefill_full_size_sampled(orc):
+    """M=8192, H=7168: every row self-consistent, 96 sampled rows against the full oracle."""
+    case = W.mxfp4_case(8192, H=7168, seed=18, with_bias=True)
+    say(f"mxfp4 {case.name}")
+    gi, gw, gl = run_mx(case)
+    si, sw = orc.topk_from_logits(gl, case.bias, case.k, case.scoring, case.renorm)
+    check_topk(gi, gw, si, sw, what="mxfp4 prefill own logits")
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 31, 32, 8191], rng.choice(8192, 92, replace=False)]))
+    ref = orc.router_mxfp4(case.x[rows], case.elems, case.scales, case.bias, case.k, case.scoring,
+                           case.renorm)
+    check_router(orc, case, gi[rows], gw[rows], gl[rows], ref=ref, rows=rows)
+
+
 def test_fused_equals_unfused(orc):
     # The logits the MXFP4 call returns, routed by router_topk_from_logits,
     # give bit-identical indices and weights: the same device routine.
     for case in (W.mxfp4_case(2, H=4096, seed=7, with_bias=True, scoring=W.SQRT_SOFTPLUS, k=6),
-                 W.mxfp4_case(16, H=4096, seed=8)):
+                 W.mxfp4_case(16, H=4096, seed=8), W.mxfp4_case(200, H=512, seed=9, with_bias=True)):
         gi, gw, gl = run_mx(case)
         ti, tw = R.router_topk_from_logits(torch.from_numpy(gl).cuda(), f32_dev(case.bias), case.k,
                                            case.scoring, case.renorm)
