@@ -58,6 +58,12 @@ class Oracle:
         lib.oracle_dequant_mxfp4.restype = ci
         lib.oracle_router_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, ci, ci, ci, P, P, P, P]
         lib.oracle_router_mxfp4.restype = ci
+        lib.oracle_bf16_round.argtypes = [ctypes.c_float]
+        lib.oracle_bf16_round.restype = ctypes.c_uint16
+        lib.oracle_gather_shared_add.argtypes = [P, i64, i64, P, P, P, i64, ci, P]
+        lib.oracle_gather_shared_add.restype = ci
+        lib.oracle_table_rows.argtypes = [P, P, ci, ci, ci, P]
+        lib.oracle_table_rows.restype = ci
         lib.oracle_route_table_m2.argtypes = [P, ci, P, P, P, P]
         lib.oracle_row_scores.argtypes = [P, i64, ci, P, P]
         for f in (lib.oracle_logits, lib.oracle_topk_from_logits, lib.oracle_router,
@@ -179,6 +185,41 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_route_table_m2 failed: {rc}")
         return ids, mask, s2u, int(cnt[0])
+
+    def bf16_round(self, f: float) -> int:
+        """BF16 bits of an fp32 value, to nearest, ties to even."""
+        return int(self.lib.oracle_bf16_round(float(np.float32(f))))
+
+    def gather_shared_add(self, y: np.ndarray, slot_rows: np.ndarray, weights: np.ndarray,
+                          shared: np.ndarray) -> np.ndarray:
+        """Routed gather + shared add.  y: bf16 bits [R, D]; slot_rows: int32 [M, k];
+        weights: fp32 [M, k]; shared: bf16 bits [M, D].  Returns bf16 bits [M, D]."""
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        slot_rows = np.ascontiguousarray(slot_rows, dtype=np.int32)
+        weights = np.ascontiguousarray(weights, dtype=np.float32)
+        shared = np.ascontiguousarray(shared, dtype=np.uint16)
+        R, D = y.shape
+        M, k = slot_rows.shape
+        assert weights.shape == (M, k) and shared.shape == (M, D)
+        out = np.empty((M, D), np.uint16)
+        rc = self.lib.oracle_gather_shared_add(self._ptr(y), R, D, self._ptr(slot_rows),
+                                               self._ptr(weights), self._ptr(shared), M, k,
+                                               self._ptr(out))
+        if rc:
+            raise ValueError(f"oracle_gather_shared_add failed: {rc}")
+        return out
+
+    def table_rows(self, token_mask: np.ndarray, slot_to_unique: np.ndarray, count: int, M: int,
+                   k: int) -> np.ndarray:
+        """Compact expert-output rows [M, k] that the unique-route table implies."""
+        token_mask = np.ascontiguousarray(token_mask, dtype=np.int32)
+        slot_to_unique = np.ascontiguousarray(slot_to_unique, dtype=np.int32)
+        rows = np.empty(M * k, np.int32)
+        rc = self.lib.oracle_table_rows(self._ptr(token_mask), self._ptr(slot_to_unique), int(count),
+                                        int(M), int(k), self._ptr(rows))
+        if rc:
+            raise ValueError(f"oracle_table_rows failed: {rc}")
+        return rows.reshape(M, k)
 
     def row_scores(self, row: np.ndarray, scoring: int):
         row = np.ascontiguousarray(row, dtype=np.float32)

@@ -305,3 +305,100 @@ int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* tok
 {
     return oracle_route_table(inds, 2, k, ids, token_mask, slot_to_unique, count);
 }
+
+/* ------------------------------------------------------------------------
+ * Routed gather + shared-expert add (B70 note, "Exact arithmetic": the
+ * routed outputs are accumulated in FP32, that sum is rounded to BF16, the
+ * shared expert's BF16 output is added, and the result is rounded to BF16).
+ * Readings where the note is silent: token t takes its slots j = 0..k-1 in
+ * order; a slot with row r >= 0 adds the fp32 product fl32(w[t,j] * y[r,d])
+ * to an fp32 accumulator that starts at +0 (the product and the sum each
+ * round once: no fused multiply-add); a slot with row -1 (an expert with no
+ * local output row) adds nothing; the BF16 + BF16 addition is an fp32
+ * addition rounded once to BF16; every rounding to BF16 is to nearest, ties
+ * to even.
+ * ------------------------------------------------------------------------ */
+static float bf16_to_float(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+uint16_t oracle_bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(f)) return (uint16_t)(sign | 0x7fc0u);
+    if (isinf(f)) return (uint16_t)(sign | 0x7f80u);
+    /* the two BF16 neighbours of |f|: its truncation and the next magnitude up */
+    const uint16_t lo = (uint16_t)((u >> 16) & 0x7fffu);
+    const uint16_t hi = (uint16_t)(lo + 1u);
+    const double a = fabs((double)f);
+    const double vlo = (double)bf16_to_float(lo);
+    /* past the largest finite value the next step up is 2^128 (infinity) */
+    const double vhi = hi >= 0x7f80u ? ldexp(1.0, 128) : (double)bf16_to_float(hi);
+    uint16_t mag;
+    if (a - vlo < vhi - a)
+        mag = lo;
+    else if (vhi - a < a - vlo)
+        mag = hi;
+    else
+        mag = (lo & 1u) ? hi : lo;  /* tie: the even neighbour */
+    return (uint16_t)(sign | mag);
+}
+
+int oracle_gather_shared_add(const uint16_t* y, int64_t y_rows, int64_t D, const int32_t* slot_rows,
+                             const float* weights, const uint16_t* shared, int64_t M, int k,
+                             uint16_t* out)
+{
+    if (M < 0 || k < 1 || D < 1 || y_rows < 0) return ORACLE_EINVAL;
+    for (int64_t s = 0; s < M * k; ++s)
+        if (slot_rows[s] < -1 || slot_rows[s] >= y_rows) return ORACLE_EINVAL;
+    for (int64_t t = 0; t < M; ++t) {
+        for (int64_t d = 0; d < D; ++d) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                int64_t r = slot_rows[t * k + j];
+                if (r < 0) continue;
+                const float p = weights[t * k + j] * bf16_to_float(y[r * D + d]);
+                acc = acc + p;
+            }
+            const float routed = bf16_to_float(oracle_bf16_round(acc));
+            const float sum = routed + bf16_to_float(shared[t * D + d]);
+            out[t * D + d] = oracle_bf16_round(sum);
+        }
+    }
+    return 0;
+}
+
+/* Rows of the compact expert-output layout the unique-route table implies
+ * (B70 note, "Why literal source-direct GEMM1 is not funded": each unique
+ * expert computes only its tokens' rows, [token0], [token1] or
+ * [token0, token1]).  Reading: the experts' row blocks follow the table's
+ * order, and inside a block the tokens come in token order, so slot
+ * s = t*k + j (expert u = slot_to_unique[s]) reads row
+ *   sum over v < u of popcount(token_mask[v])  +  the number of tokens
+ *   below t in token_mask[u].
+ * Fails if the table is inconsistent (u out of range, or bit t of
+ * token_mask[u] clear). */
+int oracle_table_rows(const int32_t* token_mask, const int32_t* slot_to_unique, int count, int M,
+                      int k, int32_t* slot_rows)
+{
+    if (M < 1 || M > 31 || k < 1 || count < 0 || count > M * k) return ORACLE_EINVAL;
+    for (int s = 0; s < M * k; ++s) {
+        const int t = s / k;
+        const int u = slot_to_unique[s];
+        if (u < 0 || u >= count) return ORACLE_EINVAL;
+        if (((token_mask[u] >> t) & 1) == 0) return ORACLE_EINVAL;
+        int before = 0;
+        for (int v = 0; v < u; ++v)
+            for (int q = 0; q < M; ++q) before += (token_mask[v] >> q) & 1;
+        int within = 0;
+        for (int q = 0; q < t; ++q) within += (token_mask[u] >> q) & 1;
+        slot_rows[s] = before + within;
+    }
+    return 0;
+}

@@ -11,7 +11,10 @@
  * postNorm[H] -> gateLogits[E] followed by a top-8 whose tie order is part of
  * the contract), the dense-router decode notes (sqrt(softplus) activation,
  * selection on score plus bias with unbiased weights kept beside the key,
- * renormalised winners) and the B70 MTP1 M=2 note (the unique-route table).
+ * renormalised winners) and the B70 MTP1 M=2 note (the unique-route table,
+ * and the routed gather + shared-expert add that consumes the routes, whose
+ * FP32 -> BF16 -> + BF16 -> BF16 chain fixes its precision, so that part
+ * works in fp32 and BF16 as the note states rather than in fp64).
  *
  * All functions return 0 on success and a negative value on bad arguments.
  */
@@ -88,6 +91,26 @@ int oracle_route_table_m2(const int32_t* inds, int k, int32_t* ids, int32_t* tok
  * the sqrt-softplus value otherwise). */
 int oracle_row_scores(const float* logits_row, int64_t E, int scoring, double* score,
                       double* unbiased);
+
+/* Round an fp32 value to BF16 bits: to nearest, ties to even; overflow to
+ * infinity; NaN stays a (quiet) NaN. */
+uint16_t oracle_bf16_round(float f);
+
+/* Routed gather + shared-expert add (B70 note, "Exact arithmetic"):
+ *   out[t,d] = bf16( bf16( acc ) + shared[t,d] ),
+ *   acc = fp32 sum over slots j in order of fl32(weights[t,j] * y[r,d]),
+ *         r = slot_rows[t*k + j], slots with r == -1 skipped.
+ * y: bf16 bits [y_rows, D]; slot_rows: int32 [M*k], each in [-1, y_rows);
+ * weights: fp32 [M*k]; shared, out: bf16 bits [M, D]. */
+int oracle_gather_shared_add(const uint16_t* y, int64_t y_rows, int64_t D, const int32_t* slot_rows,
+                             const float* weights, const uint16_t* shared, int64_t M, int k,
+                             uint16_t* out);
+
+/* slot_rows [M*k] of the compact expert-output layout that the unique-route
+ * table (token_mask, slot_to_unique, count) implies: unique experts in table
+ * order, each with the rows of its tokens in token order (1 <= M <= 31). */
+int oracle_table_rows(const int32_t* token_mask, const int32_t* slot_to_unique, int count, int M,
+                      int k, int32_t* slot_rows);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,14 @@ retypes the oracle's own code path:
     renormalisation equals a softmax over the winners alone, the bias moves
     the selection but never a weight;
   * table: encounter order equals dict.fromkeys, hand-worked identical and
-    disjoint token pairs, structural invariants.
+    disjoint token pairs, structural invariants;
+  * BF16 rounding: exact rational rounding to the nearest BF16 (ties to
+    even) over random, tie and overflow-edge fp32 patterns;
+  * gather + shared add: exact dyadic cases (every fp32 step exact, so only
+    the two BF16 roundings act), hand-worked cases for the slot order, the
+    separate multiply and add and the intermediate BF16 rounding, all-remote
+    = shared, weight-1 single slot = the row, duplicated rows = summed
+    weights; compact table rows by hand and by structural invariants.
 
 tests/test_oracle_mutants.py plants plausible mistakes in copies of oracle.c
 and requires every planted mistake to fail at least one pin.
@@ -516,6 +523,178 @@ def pin_mx_router_is_bf16_router_on_dequantised(o):
         assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
+# --------------------------------------------------------------------------
+# routed gather + shared-expert add, and the table's compact rows
+# --------------------------------------------------------------------------
+def bf16_rne_fraction(f: float) -> int:
+    """BF16 bits of a finite fp32 value, by exact rational rounding to the
+    nearest multiple of the BF16 spacing at its binade (ties to even)."""
+    f = float(np.float32(f))
+    sign = 0x8000 if math.copysign(1.0, f) < 0 else 0
+    if f == 0.0:
+        return sign
+    A = abs(Fraction(f))
+    _, ex = math.frexp(abs(f))           # |f| = m * 2^ex, m in [0.5, 1)
+    e = max(ex - 1, -126)                # binade exponent; subnormal spacing below 2^-126
+    spacing = Fraction(2) ** (e - 7)     # 7 fraction bits
+    n = round(A / spacing)               # Python rounds a Fraction half to even
+    value = n * spacing
+    if value >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    bits = int(np.array([float(value)], np.float32).view(np.uint32)[0]) >> 16
+    assert bf16_fraction(bits) == value
+    return sign | bits
+
+
+def bf16_bits(v: float) -> int:
+    """Bits of a value that BF16 represents exactly."""
+    b = int(np.array([v], np.float32).view(np.uint32)[0])
+    assert b & 0xFFFF == 0, v
+    return b >> 16
+
+
+def pin_bf16_round(o):
+    rng = np.random.default_rng(40)
+    pats = rng.integers(0, 2 ** 32, 4000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, 500, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    near_max = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x00008000, 0x00018000,
+                         0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001], np.uint32)
+    for u in np.concatenate([pats, ties, near_max, near_max | 0x80000000]):
+        f = float(np.array([u], np.uint32).view(np.float32)[0])
+        if not math.isfinite(f):
+            continue
+        got = o.bf16_round(f)
+        assert got == bf16_rne_fraction(f), (hex(int(u)), hex(got), hex(bf16_rne_fraction(f)))
+    assert o.bf16_round(float("inf")) == 0x7F80 and o.bf16_round(float("-inf")) == 0xFF80
+    nan = o.bf16_round(float("nan"))
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
+
+
+def _gather(o, y_vals, rows, w, shared_vals):
+    y = np.array([[bf16_bits(v) for v in r] for r in y_vals], np.uint16)
+    sh = np.array([[bf16_bits(v) for v in r] for r in shared_vals], np.uint16)
+    return o.gather_shared_add(y, np.array(rows, np.int32), np.array(w, np.float32), sh)
+
+
+def pin_gather_exact_dyadic(o):
+    """Small dyadic values: every fp32 product and partial sum is exact, so the
+    output is the exact routed sum rounded to BF16, plus the shared value,
+    rounded to BF16 (both roundings from exact rationals)."""
+    rng = np.random.default_rng(41)
+    R, D, M, k = 5, 48, 3, 6
+    yv = rng.integers(-8, 9, (R, D)).astype(np.float64)
+    wchoices = np.array([0.25, 0.5, 0.75, 1.0, 1.5, 2.0, -0.25, -0.5, -0.75, -1.0, -1.5, -2.0])
+    for trial in range(6):
+        rows = rng.integers(-1, R, (M, k))
+        if trial == 0:
+            rows[:] = -1                      # all remote
+        if trial == 1:
+            rows[0, :] = 2                    # one row in every slot of token 0
+        w = rng.choice(wchoices, (M, k))
+        sv = rng.integers(-16, 17, (M, D)) * 0.5
+        out = _gather(o, yv, rows, w, sv)
+        for t in range(M):
+            for d in range(D):
+                S = sum(Fraction(float(w[t, j])) * Fraction(float(yv[rows[t, j], d]))
+                        for j in range(k) if rows[t, j] >= 0)
+                routed = bf16_fraction(bf16_rne_fraction(float(S)))
+                want = bf16_rne_fraction(float(routed + Fraction(float(sv[t, d]))))
+                assert int(out[t, d]) == want, (trial, t, d, hex(int(out[t, d])), hex(want))
+
+
+def pin_gather_hand_cases(o):
+    """Worked cases whose expected bits follow from the rounding chain by hand."""
+    # fp32 accumulation in slot order: 2^24 + 1 rounds back to 2^24, then -2^24
+    # leaves 0 (the exact sum, or the reverse order, gives 1)
+    out = _gather(o, [[2.0 ** 12], [1.0], [-(2.0 ** 12)]], [[0, 1, 2]], [[2.0 ** 12, 1.0, 2.0 ** 12]],
+                  [[0.0]])
+    assert int(out[0, 0]) == 0x0000, hex(int(out[0, 0]))
+    # separate multiply and add: fl32((1 + 2^-23)(1 + 2^-7)) drops 2^-30, so the
+    # sum is 2^-23 exactly (a fused multiply-add keeps 2^-23 + 2^-30 = 0x3401)
+    out = _gather(o, [[1.0 + 2.0 ** -7]], [[0, 0]], [[-1.0, 1.0 + 2.0 ** -23]], [[0.0]])
+    assert int(out[0, 0]) == 0x3400, hex(int(out[0, 0]))
+    # the routed sum 1 + 2^-8 + 2^-9 first rounds to BF16 1 + 2^-7; adding the
+    # shared 2^-8 gives a tie, 1 + 1.5 * 2^-7, which goes to the even 1 + 2^-6
+    # (without the intermediate rounding: 1 + 1.25 * 2^-7 -> 1 + 2^-7 = 0x3F81)
+    out = _gather(o, [[1.0], [1.0]], [[0, 1]], [[1.0, 2.0 ** -8 + 2.0 ** -9]], [[2.0 ** -8]])
+    assert int(out[0, 0]) == 0x3F82, hex(int(out[0, 0]))
+    # a remote slot (row -1) adds nothing, wherever it sits
+    a = _gather(o, [[3.0], [5.0]], [[0, -1, 1]], [[0.5, 4.0, 0.25]], [[1.0]])
+    b = _gather(o, [[3.0], [5.0]], [[0, 1, -1]], [[0.5, 0.25, 9.0]], [[1.0]])
+    assert int(a[0, 0]) == int(b[0, 0]) == bf16_bits(3.75), (hex(int(a[0, 0])), hex(int(b[0, 0])))
+
+
+def pin_gather_invariants(o):
+    rng = np.random.default_rng(42)
+    R, D, M, k = 4, 40, 2, 6
+    y = W.gaussian_bf16(rng, (R, D), 1.0)
+    shared = W.gaussian_bf16(rng, (M, D), 1.0)
+    w = rng.uniform(0.05, 0.3, (M, k)).astype(np.float32)
+    # every slot remote: the output is the shared expert's output
+    out = o.gather_shared_add(y, np.full((M, k), -1, np.int32), w, shared)
+    sh = W.bf16_bits_to_f32(shared)
+    assert np.array_equal(out[sh != 0], shared[sh != 0])
+    # one slot with weight 1, shared 0: the output is that expert row (BF16 is exact through the chain)
+    zero = np.zeros((1, D), np.uint16)
+    out = o.gather_shared_add(y, np.array([[3]], np.int32), np.ones((1, 1), np.float32), zero)
+    yr = W.bf16_bits_to_f32(y[3:4])
+    assert np.array_equal(out[yr != 0], y[3:4][yr != 0])
+    # a duplicated row with weights a and b equals one slot of weight a + b
+    # when every product and sum is exact (dyadic weights, small integer rows)
+    yi = np.array([[bf16_bits(float(v)) for v in rng.integers(-8, 9, D)]], np.uint16)
+    dup = o.gather_shared_add(yi, np.array([[0, 0, -1]], np.int32),
+                              np.array([[0.75, 0.5, 3.0]], np.float32), zero)
+    one = o.gather_shared_add(yi, np.array([[0, -1, -1]], np.int32),
+                              np.array([[1.25, 0.0, 0.0]], np.float32), zero)
+    assert np.array_equal(dup, one)
+    # a row outside [-1, R) is refused
+    for bad in (R, -2):
+        try:
+            o.gather_shared_add(y, np.array([[bad]], np.int32), np.ones((1, 1), np.float32), zero)
+        except ValueError:
+            continue
+        raise AssertionError(f"row {bad} accepted")
+
+
+def pin_table_rows_hand_cases(o):
+    # token 0 picks 5, 7, 9 and token 1 picks 7, 9, 2: blocks [5: t0] [7: t0 t1] [9: t0 t1] [2: t1]
+    ids, mask, s2u, cnt = o.route_table(np.array([[5, 7, 9], [7, 9, 2]]))
+    rows = o.table_rows(mask, s2u, cnt, 2, 3)
+    assert rows.tolist() == [[0, 1, 3], [2, 4, 5]], rows.tolist()
+    # identical tokens: each expert's block holds both tokens
+    ids, mask, s2u, cnt = o.route_table(np.array([[3, 4], [3, 4]]))
+    assert o.table_rows(mask, s2u, cnt, 2, 2).tolist() == [[0, 2], [1, 3]]
+    # disjoint tokens: one row per slot, in slot order
+    ids, mask, s2u, cnt = o.route_table(np.array([[1, 2], [3, 4]]))
+    assert o.table_rows(mask, s2u, cnt, 2, 2).tolist() == [[0, 1], [2, 3]]
+    # a table whose slot names an expert the token did not pick is refused
+    try:
+        o.table_rows(np.array([1, 1], np.int32), np.array([0, 1, 0, 1], np.int32), 2, 2, 2)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("inconsistent table accepted")
+
+
+def pin_table_rows_invariants(o):
+    rng = np.random.default_rng(43)
+    for M in (1, 2, 3, 5, 8, 16):
+        for _ in range(6):
+            k = int(rng.integers(1, 5))
+            E = int(rng.integers(k, 3 * k + 2))
+            inds = np.stack([rng.choice(E, k, replace=False) for _ in range(M)]).astype(np.int32)
+            ids, mask, s2u, cnt = o.route_table(inds)
+            rows = o.table_rows(mask, s2u, cnt, M, k)
+            pairs = {}
+            for t in range(M):
+                for j in range(k):
+                    pairs[(int(s2u[t * k + j]), t)] = int(rows[t, j])
+            # one row per distinct (expert, token), covering 0..n-1 in (table order, token) order
+            assert sorted(pairs.values()) == list(range(len(pairs)))
+            assert [pairs[key] for key in sorted(pairs)] == list(range(len(pairs)))
+            assert len(pairs) == M * k  # top-k experts are distinct within a token
+
+
 ALL_PINS = [
     pin_logits_small_integers, pin_logits_rational, pin_logits_one_hot, pin_logits_blas,
     pin_softplus_closed_forms, pin_softplus_logaddexp, pin_softmax_closed_forms,
@@ -526,4 +705,6 @@ ALL_PINS = [
     pin_table_hand_cases, pin_table_invariants, pin_table_verify_widths,
     pin_table_invariants_any_m,
     pin_e2m1_table, pin_mx_dequant, pin_mx_router_is_bf16_router_on_dequantised,
+    pin_bf16_round, pin_gather_exact_dyadic, pin_gather_hand_cases, pin_gather_invariants,
+    pin_table_rows_hand_cases, pin_table_rows_invariants,
 ]

@@ -50,6 +50,21 @@ MUTANTS = [
     ("e2m1_exponent_bias", "ldexp(1.0 + 0.5 * man, ex - 1)", "ldexp(1.0 + 0.5 * man, ex)"),
     ("table_pair_width_only", "int n = M * k;", "int n = (M > 2 ? 2 : M) * k;"),
     ("table_mask_two_tokens", "token_mask[pos] |= 1 << token;", "token_mask[pos] |= 1 << (token & 1);"),
+    ("bf16_ties_away", "mag = (lo & 1u) ? hi : lo;  /* tie: the even neighbour */", "mag = hi;"),
+    ("bf16_truncates", "if (a - vlo < vhi - a)", "if (1)"),
+    ("gather_no_intermediate_round", "const float routed = bf16_to_float(oracle_bf16_round(acc));",
+     "const float routed = acc;"),
+    ("gather_reversed_slots", "for (int j = 0; j < k; ++j) {\n                int64_t r = slot_rows[t * k + j];",
+     "for (int j = k - 1; j >= 0; --j) {\n                int64_t r = slot_rows[t * k + j];"),
+    ("gather_fused_multiply_add",
+     "const float p = weights[t * k + j] * bf16_to_float(y[r * D + d]);\n                acc = acc + p;",
+     "acc = fmaf(weights[t * k + j], bf16_to_float(y[r * D + d]), acc);"),
+    ("gather_double_accumulator", "float acc = 0.0f;", "double acc = 0.0;"),
+    ("gather_remote_reads_row0", "if (r < 0) continue;", "if (r < 0) r = 0;"),
+    ("gather_drops_shared", "const float sum = routed + bf16_to_float(shared[t * D + d]);",
+     "const float sum = routed;"),
+    ("table_rows_token_inclusive", "for (int q = 0; q < t; ++q) within", "for (int q = 0; q <= t; ++q) within"),
+    ("table_rows_no_block_offset", "for (int v = 0; v < u; ++v)", "for (int v = 0; v < 0; ++v)"),
 ]
 
 
