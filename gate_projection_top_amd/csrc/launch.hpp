@@ -56,7 +56,23 @@ struct PrefillLaunch {
     uint32_t spin_ticks;    // bounded wait for sibling splits (100 MHz realtime ticks)
 };
 
+// Routed gather + shared-expert add: out[t] = bf16(bf16(sum_j w[t,j] y[row(t,j)]) + shared[t]).
+struct GatherLaunch {
+    const uint16_t* y;               // expert output rows, bf16 [y_rows, D]
+    int64_t y_rows;                  // rows outside [0, y_rows) add nothing
+    const int32_t* slot_rows;        // [M, k] rows of y, -1 = none; NULL: rows from the table
+    const int32_t* token_mask;       // unique-route table (rows in its compact layout)
+    const int32_t* slot_to_unique;
+    const int32_t* unique_count;
+    const float* weights;            // [M, k]
+    const uint16_t* shared;          // bf16 [M, D]
+    uint16_t* out;                   // bf16 [M, D] (may be `shared`)
+    int64_t M;
+    int k, D;
+};
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 int prefill_splits(int64_t M);

@@ -269,6 +269,55 @@ int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale
                      out_weights, opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
+int router_gather_shared_add(const void* y, int64_t y_rows, const int32_t* slot_rows,
+                             const float* weights, const void* shared, int64_t M, int k, int D,
+                             void* out, hipStream_t stream)
+{
+    if (M < 0 || k < 1 || D < 1 || y_rows < 0) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (k > ROUTER_MAX_K || D % 8 != 0) return ROUTER_ERR_UNSUPPORTED;
+    if (M == 0) return ROUTER_OK;
+    if (!slot_rows || !weights || !shared || !out || (!y && y_rows > 0)) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (!aligned16(y) || !aligned16(shared) || !aligned16(out)) return ROUTER_ERR_MISALIGNED;
+    if (M * (((int64_t)D + 1023) / 1024) > 0x7fffffffLL) return ROUTER_ERR_UNSUPPORTED;
+    gpt::GatherLaunch a{};
+    a.y = static_cast<const uint16_t*>(y);
+    a.y_rows = y_rows;
+    a.slot_rows = slot_rows;
+    a.weights = weights;
+    a.shared = static_cast<const uint16_t*>(shared);
+    a.out = static_cast<uint16_t*>(out);
+    a.M = M;
+    a.k = k;
+    a.D = D;
+    return gpt::launch_gather(a, stream) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+int router_gather_shared_add_table(const void* y, const int32_t* token_mask,
+                                   const int32_t* slot_to_unique, const int32_t* unique_count,
+                                   const float* weights, const void* shared, int M, int k, int D,
+                                   void* out, hipStream_t stream)
+{
+    if (M < 1 || k < 1 || D < 1) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (k > ROUTER_MAX_K || D % 8 != 0 || M > ROUTER_TABLE_MAX_M || M * k > ROUTER_TABLE_MAX_SLOTS)
+        return ROUTER_ERR_UNSUPPORTED;
+    if (!y || !token_mask || !slot_to_unique || !unique_count || !weights || !shared || !out)
+        return ROUTER_ERR_INVALID_ARGUMENT;
+    if (!aligned16(y) || !aligned16(shared) || !aligned16(out)) return ROUTER_ERR_MISALIGNED;
+    gpt::GatherLaunch a{};
+    a.y = static_cast<const uint16_t*>(y);
+    a.y_rows = (int64_t)M * k;  // the compact layout never has more rows than slots
+    a.token_mask = token_mask;
+    a.slot_to_unique = slot_to_unique;
+    a.unique_count = unique_count;
+    a.weights = weights;
+    a.shared = static_cast<const uint16_t*>(shared);
+    a.out = static_cast<uint16_t*>(out);
+    a.M = M;
+    a.k = k;
+    a.D = D;
+    return gpt::launch_gather(a, stream) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
 int router_topk_from_logits(const float* logits, const float* bias, int64_t M, int E, int k,
                             int scoring, int renorm, int32_t* out_inds, float* out_weights,
                             hipStream_t stream)

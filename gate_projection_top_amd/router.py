@@ -33,7 +33,8 @@ TABLE_MAX_SLOTS = 64
 DECODE_MAX_M = 64
 
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
-           "router_fwd_mxfp4", "router_topk_from_logits",
+           "router_fwd_mxfp4", "router_topk_from_logits", "router_gather_shared_add",
+           "router_gather_shared_add_table",
            "router_set_exchange_timeout_us", "router_strerror")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -67,6 +68,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_fwd_route_table.restype = i32
     lib.router_fwd_mxfp4.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
     lib.router_fwd_mxfp4.restype = i32
+    lib.router_gather_shared_add.argtypes = [P, i64, P, P, P, i64, i32, i32, P, P]
+    lib.router_gather_shared_add.restype = i32
+    lib.router_gather_shared_add_table.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P]
+    lib.router_gather_shared_add_table.restype = i32
     lib.router_topk_from_logits.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, P]
     lib.router_topk_from_logits.restype = i32
     lib.router_set_exchange_timeout_us.argtypes = [i32]
@@ -294,3 +299,56 @@ def router_topk_from_logits(logits: torch.Tensor, bias: Optional[torch.Tensor], 
                                             _stream(logits.device))
     _check(rc, "router_topk_from_logits")
     return inds, wts
+
+
+def router_gather_shared_add(y: torch.Tensor, slot_rows: torch.Tensor, weights: torch.Tensor,
+                             shared: torch.Tensor, *, out: Optional[torch.Tensor] = None):
+    """Routed gather + shared-expert add.  y: bf16 [R, D]; slot_rows: int32 [M, k]
+    (-1 = no row); weights: fp32 [M, k]; shared: bf16 [M, D].  Returns bf16 [M, D]
+    (`out` may be `shared`)."""
+    _check_tensor(y, "y", torch.bfloat16, 2)
+    _check_tensor(slot_rows, "slot_rows", torch.int32, 2)
+    _check_tensor(weights, "weights", torch.float32, 2)
+    _check_tensor(shared, "shared", torch.bfloat16, 2)
+    R, D = y.shape
+    M, k = slot_rows.shape
+    if tuple(weights.shape) != (M, k) or tuple(shared.shape) != (M, D):
+        raise ValueError("weights must be [M, k] and shared [M, D]")
+    if out is None:
+        out = torch.empty((M, D), dtype=torch.bfloat16, device=y.device)
+    _check_tensor(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, D):
+        raise ValueError("out must be [M, D]")
+    with torch.cuda.device(y.device):
+        rc = load().router_gather_shared_add(_ptr(y), R, _ptr(slot_rows), _ptr(weights), _ptr(shared),
+                                             M, k, D, _ptr(out), _stream(y.device))
+    _check(rc, "router_gather_shared_add")
+    return out
+
+
+def router_gather_shared_add_table(y: torch.Tensor, table: dict, weights: torch.Tensor,
+                                   shared: torch.Tensor, *, out: Optional[torch.Tensor] = None):
+    """The gather with rows from a unique-route table (the dict router_fwd_route_table
+    returns: token_mask, slot_to_unique, unique_count).  y: bf16 [M*k, D] in the
+    table's compact layout; weights: fp32 [M, k]; shared: bf16 [M, D]."""
+    _check_tensor(y, "y", torch.bfloat16, 2)
+    _check_tensor(weights, "weights", torch.float32, 2)
+    _check_tensor(shared, "shared", torch.bfloat16, 2)
+    M, k = weights.shape
+    D = shared.shape[1]
+    if tuple(shared.shape) != (M, D) or y.shape[1] != D or y.shape[0] < M * k:
+        raise ValueError("shared must be [M, D] and y at least [M*k, D]")
+    mask, s2u, cnt = table["token_mask"], table["slot_to_unique"], table["unique_count"]
+    for name, t in (("token_mask", mask), ("slot_to_unique", s2u), ("unique_count", cnt)):
+        _check_tensor(t, name, torch.int32, 1)
+    if mask.numel() < M * k or s2u.numel() < M * k or cnt.numel() < 1:
+        raise ValueError("table arrays are too short for M*k slots")
+    if out is None:
+        out = torch.empty((M, D), dtype=torch.bfloat16, device=y.device)
+    _check_tensor(out, "out", torch.bfloat16, 2)
+    with torch.cuda.device(y.device):
+        rc = load().router_gather_shared_add_table(_ptr(y), _ptr(mask), _ptr(s2u), _ptr(cnt),
+                                                   _ptr(weights), _ptr(shared), M, k, D, _ptr(out),
+                                                   _stream(y.device))
+    _check(rc, "router_gather_shared_add_table")
+    return out

@@ -401,3 +401,66 @@ def torch_mxfp4_gate(n: int, E: int, H: int, seed: int, device, scale_lo: int = 
     scales = torch.randint(scale_lo, scale_hi + 1, (n, E, H // 32), generator=g, device=device,
                            dtype=torch.uint8)
     return codes, scales
+
+
+# ---------------------------------------------------------------------------
+# routed gather + shared-expert add inputs
+# ---------------------------------------------------------------------------
+GATHER_PATTERNS = ("typical", "same", "disjoint", "overlap", "within_dup", "all_dup", "all_local",
+                   "all_remote", "some_remote", "ties")
+
+
+@dataclasses.dataclass
+class GatherCase:
+    y: np.ndarray          # bf16 bits [R, D]: expert output rows
+    slot_rows: np.ndarray  # int32 [M, k], -1 = no local row
+    weights: np.ndarray    # fp32 [M, k]
+    shared: np.ndarray     # bf16 bits [M, D]
+    name: str = ""
+
+
+def gather_case(M: int, k: int, D: int, pattern: str = "typical", seed: int = 0,
+                R: Optional[int] = None) -> GatherCase:
+    """Synthetic expert outputs for the gather: y ~ N(0,1) rows and shared ~ N(0,1)
+    in bf16, router-like weights (U(0,1) per slot, scaled to sum to 1 per token,
+    fp32), and a slot -> row map of the named route class (the B70 note's test
+    classes: same / disjoint / cross-token overlap / within-token duplicate /
+    all-duplicate / all-local / all-remote; "ties" uses small integer rows and
+    dyadic weights so that many BF16 roundings are exact ties)."""
+    assert pattern in GATHER_PATTERNS, pattern
+    rng = _rng(seed, 12)
+    R = M * k if R is None else R
+    y = gaussian_bf16(rng, (R, D), 1.0)
+    shared = gaussian_bf16(rng, (M, D), 1.0)
+    u = rng.uniform(0.05, 1.0, (M, k))
+    w = (u / u.sum(axis=1, keepdims=True)).astype(np.float32)
+    if pattern == "typical":
+        rows = np.stack([rng.choice(R, k, replace=False) for _ in range(M)])
+    elif pattern == "same":
+        rows = np.tile(rng.choice(R, k, replace=False), (M, 1))
+    elif pattern == "disjoint":
+        rows = (np.arange(M * k).reshape(M, k)) % R
+    elif pattern == "overlap":
+        base = rng.choice(R, k, replace=False)
+        rows = np.stack([np.roll(base, t) if t % 2 else base for t in range(M)])
+        rows[:, -1] = rng.integers(0, R, M)
+    elif pattern == "within_dup":
+        rows = np.stack([rng.choice(R, k, replace=False) for _ in range(M)])
+        if k > 1:
+            rows[:, 1] = rows[:, 0]
+    elif pattern == "all_dup":
+        rows = np.zeros((M, k), np.int64)
+    elif pattern == "all_local":
+        rows = np.stack([rng.permutation(R)[:k] for _ in range(M)])
+    elif pattern == "all_remote":
+        rows = np.full((M, k), -1)
+    elif pattern == "some_remote":
+        rows = np.stack([rng.choice(R, k, replace=False) for _ in range(M)])
+        rows[rng.random((M, k)) < 0.4] = -1
+    else:  # ties
+        y = f32_to_bf16_bits(rng.integers(-8, 9, (R, D)).astype(np.float32))
+        shared = f32_to_bf16_bits((rng.integers(-16, 17, (M, D)) * 0.5).astype(np.float32))
+        w = rng.choice(np.array([0.25, 0.5, 0.75, 1.0, 1.5, -0.5], np.float32), (M, k))
+        rows = np.stack([rng.choice(R, k, replace=R < k) for _ in range(M)])
+    return GatherCase(y, rows.astype(np.int32), w.astype(np.float32), shared,
+                      name=f"gather/{pattern}/M{M}/k{k}/D{D}/R{R}/seed{seed}")

@@ -20,6 +20,8 @@
  *     with FP32 accumulation and the row-level top-k epilogue;
  *   - dense_router_decode commit notes, the fused NVFP4 router: the gate
  *     projection on block-scaled FP4 weights (here OCP MXFP4);
+ *   - b70 lab MTP1 M=2 note, "Outcome" and "Exact arithmetic": the routed
+ *     gather fused with the shared-expert BF16 add that follows the router;
  *   - b70 lab MTP1 M=2 note, "Unique-route router screen": the optional M=2
  *     unique-route table produced inside the router launch (here also at the
  *     other verify widths of qwisp issue #145, "Observation").
@@ -57,7 +59,7 @@
  * on any error nothing is launched and no output byte changes.  The return
  * value is ROUTER_OK or one of the codes below; router_strerror() names it.
  *
- * Concurrency: the fused entry points (router_fwd*) use a per-device
+ * Concurrency: the fused router entry points (router_fwd*) use a per-device
  * workspace (partial sums and arrival counters).  Calls on one device must be
  * ordered (same stream, or externally synchronised); overlapping calls on
  * one device race on that workspace.  router_topk_from_logits uses none.
@@ -172,6 +174,46 @@ int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale
                      const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
                      int32_t* out_inds, float* out_weights, float* opt_out_logits,
                      hipStream_t stream);
+
+/* The step after the router: routed gather fused with the shared-expert
+ * add (b70 lab MTP1 M=2 note, "Outcome"), with the note's rounding chain
+ * ("Exact arithmetic": FP32 routed accumulation -> BF16 -> add shared BF16
+ * -> BF16):
+ *   out[t,d] = bf16( bf16(acc) + shared[t,d] ),
+ *   acc      = fp32 sum over slots j = 0..k-1 of token t, in order, of
+ *              fl32(weights[t,j] * y[r,d]), r = slot_rows[t,j]; the product
+ *              and each addition round separately (no fused multiply-add);
+ *   bf16()   = round to nearest, ties to even (NaN stays NaN).
+ * A slot whose row is -1 (its expert has no local output row) adds
+ * nothing; so does a row outside [0, y_rows), which is a caller error the
+ * kernel cannot report.  With no row in any slot, out = bf16(0 + shared).
+ *   y          bf16 [y_rows, D]  expert output rows (16-byte aligned)
+ *   slot_rows  int32 [M, k]      row of y per slot, or -1
+ *   weights    fp32 [M, k]       the router's weights (router_fwd's out_weights)
+ *   shared     bf16 [M, D]       shared-expert output (16-byte aligned)
+ *   out        bf16 [M, D]       may be `shared` (in place); must not overlap y
+ * Limits: 1 <= k <= ROUTER_MAX_K, D % 8 == 0, M >= 0 (M == 0 is a no-op).
+ * Uses no workspace. */
+int router_gather_shared_add(const void* y, int64_t y_rows, const int32_t* slot_rows,
+                             const float* weights, const void* shared, int64_t M, int k, int D,
+                             void* out, hipStream_t stream);
+
+/* router_gather_shared_add with the rows taken from a unique-route table
+ * (router_fwd_route_table's token_mask, slot_to_unique and unique_count,
+ * read on the device).  The expert outputs are in the compact layout the
+ * table implies (same note, "Why literal source-direct GEMM1 is not
+ * funded": each unique expert computes only its tokens' rows): unique
+ * experts in table order, each with one row per token of its mask in token
+ * order, so slot (t, j) of expert u reads row
+ *   sum over unique v < u of popcount(token_mask[v])
+ *   + popcount(token_mask[u] & ((1 << t) - 1)).
+ * y must hold M*k rows (the most the layout can use).  Limits as
+ * router_fwd_route_table (1 <= M <= ROUTER_TABLE_MAX_M, M*k <=
+ * ROUTER_TABLE_MAX_SLOTS) and as router_gather_shared_add. */
+int router_gather_shared_add_table(const void* y, const int32_t* token_mask,
+                                   const int32_t* slot_to_unique, const int32_t* unique_count,
+                                   const float* weights, const void* shared, int M, int k, int D,
+                                   void* out, hipStream_t stream);
 
 /* Scoring, selection and weights on logits already in HBM (the standalone
  * logits-to-top-k of the unfused pair; dense_router_decode notes, "Current

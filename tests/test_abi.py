@@ -169,3 +169,53 @@ def test_mxfp4_rejects(lib, kw, code):
 def test_mxfp4_empty_batch_is_ok_without_pointers(lib):
     assert lib.router_fwd_mxfp4(None, None, None, None, 0, 4096, 256, 8, 0, 1, None, None, None,
                                 None) == R.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), R.ERR_INVALID_ARGUMENT),
+    (dict(k=0), R.ERR_INVALID_ARGUMENT),
+    (dict(k=17), R.ERR_UNSUPPORTED),
+    (dict(D=0), R.ERR_INVALID_ARGUMENT),
+    (dict(D=12), R.ERR_UNSUPPORTED),
+    (dict(y_rows=-1), R.ERR_INVALID_ARGUMENT),
+    (dict(rows=None), R.ERR_INVALID_ARGUMENT),
+    (dict(weights=None), R.ERR_INVALID_ARGUMENT),
+    (dict(shared=None), R.ERR_INVALID_ARGUMENT),
+    (dict(out=None), R.ERR_INVALID_ARGUMENT),
+    (dict(y=None), R.ERR_INVALID_ARGUMENT),
+    (dict(y=FAKE_ODD), R.ERR_MISALIGNED),
+    (dict(shared=FAKE_ODD), R.ERR_MISALIGNED),
+    (dict(out=FAKE_ODD), R.ERR_MISALIGNED),
+])
+def test_gather_rejects(lib, kw, code):
+    a = dict(y=FAKE, y_rows=12, rows=FAKE, weights=FAKE, shared=FAKE, M=2, k=6, D=7168, out=FAKE)
+    a.update(kw)
+    rc = lib.router_gather_shared_add(a["y"], a["y_rows"], a["rows"], a["weights"], a["shared"],
+                                      a["M"], a["k"], a["D"], a["out"], None)
+    assert rc == code, (kw, rc)
+
+
+def test_gather_empty_batch_is_ok_without_pointers(lib):
+    assert lib.router_gather_shared_add(None, 0, None, None, None, 0, 6, 7168, None, None) == R.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), R.ERR_INVALID_ARGUMENT),
+    (dict(M=17), R.ERR_UNSUPPORTED),
+    (dict(M=9, k=8), R.ERR_UNSUPPORTED),      # 72 slots > ROUTER_TABLE_MAX_SLOTS
+    (dict(k=17), R.ERR_UNSUPPORTED),
+    (dict(D=20), R.ERR_UNSUPPORTED),
+    (dict(y=None), R.ERR_INVALID_ARGUMENT),
+    (dict(mask=None), R.ERR_INVALID_ARGUMENT),
+    (dict(s2u=None), R.ERR_INVALID_ARGUMENT),
+    (dict(count=None), R.ERR_INVALID_ARGUMENT),
+    (dict(weights=None), R.ERR_INVALID_ARGUMENT),
+    (dict(y=FAKE_ODD), R.ERR_MISALIGNED),
+])
+def test_gather_table_rejects(lib, kw, code):
+    a = dict(y=FAKE, mask=FAKE, s2u=FAKE, count=FAKE, weights=FAKE, shared=FAKE, M=2, k=6, D=7168,
+             out=FAKE)
+    a.update(kw)
+    rc = lib.router_gather_shared_add_table(a["y"], a["mask"], a["s2u"], a["count"], a["weights"],
+                                            a["shared"], a["M"], a["k"], a["D"], a["out"], None)
+    assert rc == code, (kw, rc)
