@@ -20,7 +20,9 @@ Also reported (same JSON line):
   extras        cache-hot cycle, verify widths M=2/8 at H=4096, the biased M=2
                 table on/off delta, the MXFP4 gate at M=1 and M=8 (H=7168, a
                 600-matrix 585 MB pool) and at the 8192-token prefill, the
-                standalone top-k at M=4096, and the
+                routed gather + shared-expert add at M=2 (explicit rows, all
+                remote, table rows) and at M=4096, the standalone top-k at
+                M=4096, and the
                 8192-token prefill (tokens/s, fraction of bf16 MFMA and HBM peak).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
@@ -43,7 +45,9 @@ LAYERS = 40
 POOL = 160
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_M1_H7168_traffic.txt")
 MX_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_mxfp4_M1_H7168_traffic.txt")
+GATHER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gather_shared_add_M2_k6_D7168_traffic.txt")
 KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
+GATHER_SOURCES = ["gather_kernel.hip", "route_common.hpp", "launch.hpp", "router_api.cpp"]
 
 
 def log(msg):
@@ -55,27 +59,30 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "prefill", "topk"], default="all",
+    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "gather", "prefill", "topk"],
+                    default="all",
                     help="restrict to one workload (for counter-collection runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--mxfp4-widths", default="1,8",
                     help="token counts of the MXFP4 section (comma-separated, each <= 64)")
+    ap.add_argument("--gather-disjoint-only", action="store_true",
+                    help="gather section: only the M=2 explicit-row case (counter-collection runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(names=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "gate_projection_top_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(path=TRAFFIC_SUMMARY):
-    """Bytes per decode launch from a committed counter summary, if it still applies."""
+def committed_traffic(path=TRAFFIC_SUMMARY, sources=KERNEL_SOURCES):
+    """Bytes per launch from a committed counter summary, if the kernel sources still match it."""
     try:
         fields = {}
         with open(path) as f:
@@ -83,7 +90,7 @@ def committed_traffic(path=TRAFFIC_SUMMARY):
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        if fields.get("kernel_sources_sha256_16") != kernel_source_digest():
+        if fields.get("kernel_sources_sha256_16") != kernel_source_digest(sources):
             return None
         return float(fields["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -192,6 +199,8 @@ def main():
         out["extras"].update(decode_extras(torch, R, W, dev, args))
     if args.section in ("all", "mxfp4"):
         out["extras"].update(mxfp4_extras(torch, R, W, dev, args))
+    if args.section in ("all", "gather"):
+        out["extras"].update(gather_extras(torch, R, W, dev, args))
     if args.section in ("all", "topk"):
         out["extras"].update(topk_extras(torch, R, W, dev, args))
     if args.section in ("all", "prefill"):
@@ -356,6 +365,73 @@ def mxfp4_extras(torch, R, W, dev, args):
     ex["mxfp4_prefill_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
     del xs
     log("mxfp4 done")
+    return ex
+
+
+def gather_extras(torch, R, W, dev, args):
+    """Routed gather + shared-expert add at the MTP1 pair (M=2, k=6, D=7168): 40
+    calls per step, each layer's 12 expert output rows from a 1600-layer pool
+    (275 MB, cold); the table variant on a table the router produced; all-remote
+    routes; and M=4096, k=8 (bandwidth)."""
+    ex = {}
+    M, k, D, pool = 2, 6, 7168, 1600
+    ys = W.torch_gaussian_bf16((pool, M * k, D), 1.0, seed=40, device=dev)
+    shared = W.torch_gaussian_bf16((LAYERS, M, D), 1.0, seed=41, device=dev)
+    u = W.torch_uniform_f32(LAYERS * M * k, 0.05, 1.0, seed=42, device=dev).view(LAYERS, M, k)
+    wts = (u / u.sum(dim=2, keepdim=True)).contiguous()
+    out = torch.empty((LAYERS, M, D), dtype=torch.bfloat16, device=dev)
+    disjoint = torch.arange(M * k, dtype=torch.int32, device=dev).view(M, k)   # 12 distinct rows
+    remote = torch.full((M, k), -1, dtype=torch.int32, device=dev)
+    groups = pool // LAYERS
+
+    def timed(rows_of, label):
+        graphs = [GraphTimer(torch, [(lambda l=l, g=g: R.router_gather_shared_add(
+            ys[g * LAYERS + l], rows_of, wts[l], shared[l], out=out[l])) for l in range(LAYERS)])
+            for g in range(groups)]
+        wall, ev_ms = timed_replays(torch, graphs, args.steps, args.warmup)
+        n = args.steps * LAYERS
+        ex[f"gather_M2_k6_D7168_{label}_us_per_call"] = round(wall * 1e6 / n, 3)
+        ex[f"gather_M2_k6_D7168_{label}_launch_us"] = round(ev_ms * 1e3 / n, 3)
+        return ev_ms * 1e3 / n
+
+    launch_us = timed(disjoint, "disjoint")
+    algo = M * k * D * 2 + 2 * M * D * 2 + M * k * 8  # rows read + shared + out + map/weights
+    ex["gather_M2_k6_D7168_bytes_per_launch"] = algo
+    ex["gather_M2_k6_D7168_hbm_frac"] = round(algo / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    ex["gather_M2_k6_D7168_traffic"] = committed_traffic(GATHER_TRAFFIC_SUMMARY, GATHER_SOURCES)
+    if args.gather_disjoint_only:
+        return ex
+    timed(remote, "all_remote")
+
+    # the table variant, on the table the decode router emits for one biased MTP1 pair
+    case = W.verify_table_case(2, seed=4, k=k, biased=True)
+    xb = torch.from_numpy(case.x.view("int16")).view(torch.bfloat16).to(dev)
+    wg = torch.from_numpy(case.w.view("int16")).view(torch.bfloat16).to(dev)
+    bb = torch.from_numpy(case.bias).to(dev)
+    tab = R.router_fwd_route_table(xb, wg, bb, k, case.scoring, case.renorm)
+    ex["gather_table_unique_experts"] = int(tab["unique_count"].item())
+    graphs = [GraphTimer(torch, [(lambda l=l, g=g: R.router_gather_shared_add_table(
+        ys[g * LAYERS + l], tab, tab["weights"], shared[l], out=out[l])) for l in range(LAYERS)])
+        for g in range(groups)]
+    wall, ev_ms = timed_replays(torch, graphs, args.steps, args.warmup)
+    ex["gather_M2_k6_D7168_table_us_per_call"] = round(wall * 1e6 / (args.steps * LAYERS), 3)
+    del graphs, ys
+
+    # bandwidth: M=4096 tokens, k=8 distinct rows each (470 MB of expert rows)
+    Mb, kb = 4096, 8
+    yb = W.torch_gaussian_bf16((Mb * kb, D), 1.0, seed=43, device=dev)
+    sb = W.torch_gaussian_bf16((Mb, D), 1.0, seed=44, device=dev)
+    rb = torch.arange(Mb * kb, dtype=torch.int32, device=dev).view(Mb, kb)
+    ub = W.torch_uniform_f32(Mb * kb, 0.05, 1.0, seed=45, device=dev).view(Mb, kb)
+    wb = (ub / ub.sum(dim=1, keepdim=True)).contiguous()
+    ob = torch.empty((Mb, D), dtype=torch.bfloat16, device=dev)
+    b_us = graph_call_us(torch, [lambda: R.router_gather_shared_add(yb, rb, wb, sb, out=ob)],
+                         max(args.steps // 2, 2), 2)
+    bbytes = Mb * kb * D * 2 + 2 * Mb * D * 2 + Mb * kb * 8
+    ex["gather_M4096_k8_D7168_event_us_per_call"] = round(b_us, 2)
+    ex["gather_M4096_k8_D7168_hbm_frac"] = round(bbytes / (b_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    del yb
+    log("gather done")
     return ex
 
 

@@ -38,7 +38,8 @@ __device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float
 // fp32 -> BF16, to nearest, ties to even
 __device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-// kMaxK: k rounded up to 4, 8 or 16 (the unrolled slot count).
+// kMaxK: k rounded up to 4, 6, 8 or 16 (the unrolled slot count; a slot
+// past k costs a load, so the common k = 6 and k = 8 have their own).
 template <bool kTable, int kMaxK>
 __global__ __launch_bounds__(kGatherThreads) void gather_shared_add_kernel(GatherLaunch a)
 {
@@ -145,6 +146,9 @@ hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream)
     if (a.k <= 4) {
         if (table) hipLaunchKernelGGL((gather_shared_add_kernel<true, 4>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((gather_shared_add_kernel<false, 4>), grid, block, 0, stream, a);
+    } else if (a.k <= 6) {
+        if (table) hipLaunchKernelGGL((gather_shared_add_kernel<true, 6>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((gather_shared_add_kernel<false, 6>), grid, block, 0, stream, a);
     } else if (a.k <= 8) {
         if (table) hipLaunchKernelGGL((gather_shared_add_kernel<true, 8>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((gather_shared_add_kernel<false, 8>), grid, block, 0, stream, a);
