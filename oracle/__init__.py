@@ -64,6 +64,8 @@ class Oracle:
         lib.oracle_gather_shared_add.restype = ci
         lib.oracle_table_rows.argtypes = [P, P, ci, ci, ci, P]
         lib.oracle_table_rows.restype = ci
+        lib.oracle_expert_gemm1_table.argtypes = [P, P, i64, i64, i64, P, P, ci, ci, P, P]
+        lib.oracle_expert_gemm1_table.restype = ci
         lib.oracle_route_table_m2.argtypes = [P, ci, P, P, P, P]
         lib.oracle_row_scores.argtypes = [P, i64, ci, P, P]
         for f in (lib.oracle_logits, lib.oracle_topk_from_logits, lib.oracle_router,
@@ -220,6 +222,27 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_table_rows failed: {rc}")
         return rows.reshape(M, k)
+
+    def expert_gemm1_table(self, x: np.ndarray, w1: np.ndarray, unique_ids: np.ndarray,
+                           token_mask: np.ndarray, count: int):
+        """Expert GEMM1 on the table's compact rows.  x: bf16 bits [M, D];
+        w1: bf16 bits [E, F, D].  Returns (exact [rows, F] float64, absdot [rows, F])."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        w1 = np.ascontiguousarray(w1, dtype=np.uint16)
+        ids = np.ascontiguousarray(unique_ids, dtype=np.int32)
+        mask = np.ascontiguousarray(token_mask, dtype=np.int32)
+        M, D = x.shape
+        E, F, D2 = w1.shape
+        assert D2 == D
+        nrows = sum(bin(int(m) & ((1 << M) - 1)).count("1") for m in mask[:count])
+        out = np.empty((max(nrows, 1), F), np.float64)
+        ad = np.empty((max(nrows, 1), F), np.float64)
+        rc = self.lib.oracle_expert_gemm1_table(self._ptr(x), self._ptr(w1), E, F, D, self._ptr(ids),
+                                                self._ptr(mask), int(count), M, self._ptr(out),
+                                                self._ptr(ad))
+        if rc < 0:
+            raise ValueError(f"oracle_expert_gemm1_table failed: {rc}")
+        return out[:rc], ad[:rc]
 
     def row_scores(self, row: np.ndarray, scoring: int):
         row = np.ascontiguousarray(row, dtype=np.float32)

@@ -402,3 +402,45 @@ int oracle_table_rows(const int32_t* token_mask, const int32_t* slot_to_unique, 
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Expert GEMM1 on the unique-route table (B70 note, "Why literal
+ * source-direct GEMM1 is not funded": once identical (token, expert) routes
+ * are deduplicated upstream, each expert has the affine rows [token0],
+ * [token1] or [token0, token1]; the table is consumed by the GEMMs).
+ * Reading: unique expert u (expert id unique_ids[u]) multiplies the rows of
+ * the tokens in token_mask[u] by its GEMM1 weights w1[id] ([F, D], one
+ * output feature per row); the product of token t lands in the compact row
+ * oracle_table_rows gives (unique experts in table order, tokens in token
+ * order).  The exact dot products are returned in double, with the sums of
+ * absolute products for the tolerance; the kernel rounds to BF16.
+ * ------------------------------------------------------------------------ */
+int oracle_expert_gemm1_table(const uint16_t* x, const uint16_t* w1, int64_t E, int64_t F, int64_t D,
+                              const int32_t* unique_ids, const int32_t* token_mask, int count, int M,
+                              double* out, double* absdot)
+{
+    if (M < 1 || M > 31 || E < 1 || F < 1 || D < 1 || count < 0) return ORACLE_EINVAL;
+    int row = 0;
+    for (int u = 0; u < count; ++u) {
+        const int64_t id = unique_ids[u];
+        if (id < 0 || id >= E) return ORACLE_EINVAL;
+        const uint16_t* wexp = w1 + id * F * D;
+        for (int t = 0; t < M; ++t) {
+            if (((token_mask[u] >> t) & 1) == 0) continue;
+            const uint16_t* xr = x + (int64_t)t * D;
+            for (int64_t f = 0; f < F; ++f) {
+                const uint16_t* wrow = wexp + f * D;
+                double dot = 0.0, amag = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    const double prod = bf16_value(xr[d]) * bf16_value(wrow[d]);
+                    dot += prod;
+                    amag += fabs(prod);
+                }
+                out[(int64_t)row * F + f] = dot;
+                if (absdot) absdot[(int64_t)row * F + f] = amag;
+            }
+            ++row;  /* rows follow the table's compact layout */
+        }
+    }
+    return row;  /* number of rows written */
+}

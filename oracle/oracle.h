@@ -112,6 +112,16 @@ int oracle_gather_shared_add(const uint16_t* y, int64_t y_rows, int64_t D, const
 int oracle_table_rows(const int32_t* token_mask, const int32_t* slot_to_unique, int count, int M,
                       int k, int32_t* slot_rows);
 
+/* Expert GEMM1 on the table's compact rows: for unique expert u < count
+ * (expert unique_ids[u]) and each token t of token_mask[u], in table order
+ * then token order, out[row, f] = sum_d x[t,d] * w1[unique_ids[u], f, d]
+ * exactly in double (absdot: the sum of |products|, may be NULL).
+ * x: bf16 bits [M, D]; w1: bf16 bits [E, F, D]; out, absdot: [rows, F].
+ * Returns the number of rows written (>= 0) or a negative error. */
+int oracle_expert_gemm1_table(const uint16_t* x, const uint16_t* w1, int64_t E, int64_t F, int64_t D,
+                              const int32_t* unique_ids, const int32_t* token_mask, int count, int M,
+                              double* out, double* absdot);
+
 #ifdef __cplusplus
 }
 #endif

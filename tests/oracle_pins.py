@@ -695,6 +695,71 @@ def pin_table_rows_invariants(o):
             assert len(pairs) == M * k  # top-k experts are distinct within a token
 
 
+def _small_int_bf16(rng, shape, lo=-6, hi=7):
+    v = rng.integers(lo, hi, shape)
+    return v, W.f32_to_bf16_bits(v.astype(np.float32))
+
+
+def pin_gemm1_hand_table(o):
+    """Token 0 picks experts 5, 7, 9 and token 1 picks 7, 9, 2: the compact rows are
+    (5,t0) (7,t0) (7,t1) (9,t0) (9,t1) (2,t1); small integers make every product exact."""
+    rng = np.random.default_rng(50)
+    D, F, E = 24, 5, 10
+    xv, x = _small_int_bf16(rng, (2, D))
+    wv, w1 = _small_int_bf16(rng, (E, F, D))
+    ids, mask, s2u, cnt = o.route_table(np.array([[5, 7, 9], [7, 9, 2]]))
+    out, ad = o.expert_gemm1_table(x, w1, ids, mask, cnt)
+    order = [(5, 0), (7, 0), (7, 1), (9, 0), (9, 1), (2, 1)]
+    want = np.array([[int(np.dot(xv[t], wv[e, f])) for f in range(F)] for e, t in order])
+    assert out.shape == want.shape and np.array_equal(out, want.astype(np.float64)), (out, want)
+    want_ad = np.array([[int(np.dot(np.abs(xv[t]), np.abs(wv[e, f]))) for f in range(F)] for e, t in order])
+    assert np.array_equal(ad, want_ad.astype(np.float64))
+
+
+def pin_gemm1_one_hot(o):
+    """One-hot weight rows pick single activations exactly."""
+    rng = np.random.default_rng(51)
+    M, D, F, E = 3, 40, 7, 6
+    x = W.gaussian_bf16(rng, (M, D), 1.0)
+    w1 = np.zeros((E, F, D), np.uint16)
+    pick = rng.integers(0, D, (E, F))
+    for e in range(E):
+        for f in range(F):
+            w1[e, f, pick[e, f]] = 0x3F80  # 1.0
+    inds = np.array([[4, 1], [1, 5], [0, 4]], np.int32)
+    ids, mask, s2u, cnt = o.route_table(inds)
+    out, _ = o.expert_gemm1_table(x, w1, ids, mask, cnt)
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    r = 0
+    for u in range(cnt):
+        for t in range(M):
+            if (int(mask[u]) >> t) & 1:
+                assert np.array_equal(out[r], xf[t, pick[ids[u]]]), (u, t)
+                r += 1
+    assert r == out.shape[0]
+
+
+def pin_gemm1_blas_and_table_rows(o):
+    """Random bf16 data: each (token, expert) row equals numpy's float64 product,
+    at the row the table's slot map gives."""
+    rng = np.random.default_rng(52)
+    for M, k in ((1, 4), (2, 6), (5, 3)):
+        D, F, E = 64, 9, 12
+        x = W.gaussian_bf16(rng, (M, D), 1.0)
+        w1 = W.gaussian_bf16(rng, (E, F, D), 0.2)
+        inds = np.stack([rng.choice(E, k, replace=False) for _ in range(M)]).astype(np.int32)
+        ids, mask, s2u, cnt = o.route_table(inds)
+        out, _ = o.expert_gemm1_table(x, w1, ids, mask, cnt)
+        rows = o.table_rows(mask, s2u, cnt, M, k)
+        xf = W.bf16_bits_to_f32(x).astype(np.float64)
+        wf = W.bf16_bits_to_f32(w1).astype(np.float64)
+        for t in range(M):
+            for j in range(k):
+                ref = wf[inds[t, j]] @ xf[t]
+                got = out[rows[t, j]]
+                assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), (M, t, j)
+
+
 ALL_PINS = [
     pin_logits_small_integers, pin_logits_rational, pin_logits_one_hot, pin_logits_blas,
     pin_softplus_closed_forms, pin_softplus_logaddexp, pin_softmax_closed_forms,
@@ -707,4 +772,5 @@ ALL_PINS = [
     pin_e2m1_table, pin_mx_dequant, pin_mx_router_is_bf16_router_on_dequantised,
     pin_bf16_round, pin_gather_exact_dyadic, pin_gather_hand_cases, pin_gather_invariants,
     pin_table_rows_hand_cases, pin_table_rows_invariants,
+    pin_gemm1_hand_table, pin_gemm1_one_hot, pin_gemm1_blas_and_table_rows,
 ]

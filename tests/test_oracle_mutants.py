@@ -65,6 +65,15 @@ MUTANTS = [
      "const float sum = routed;"),
     ("table_rows_token_inclusive", "for (int q = 0; q < t; ++q) within", "for (int q = 0; q <= t; ++q) within"),
     ("table_rows_no_block_offset", "for (int v = 0; v < u; ++v)", "for (int v = 0; v < 0; ++v)"),
+    ("gemm1_expert_by_slot", "const uint16_t* wexp = w1 + id * F * D;",
+     "const uint16_t* wexp = w1 + (int64_t)(u % E) * F * D;"),
+    ("gemm1_transposed_weights", "const double prod = bf16_value(xr[d]) * bf16_value(wrow[d]);",
+     "const double prod = bf16_value(xr[d]) * bf16_value(wexp[((d * F + f) % (F * D))]);"),
+    ("gemm1_tokens_reversed", "const uint16_t* xr = x + (int64_t)t * D;",
+     "const uint16_t* xr = x + (int64_t)(M - 1 - t) * D;"),
+    ("gemm1_drops_last_term", "for (int64_t d = 0; d < D; ++d) {\n                    const double prod",
+     "for (int64_t d = 0; d + 1 < D; ++d) {\n                    const double prod"),
+    ("gemm1_absdot_signed", "amag += fabs(prod);", "amag += prod;"),
 ]
 
 
