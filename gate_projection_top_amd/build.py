@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "librouter.so")
 
 SOURCES = ["router_api.cpp", "topk_kernel.hip", "decode_kernel.hip", "prefill_kernel.hip",
-           "gather_kernel.hip"]
+           "gather_kernel.hip", "gemm1_kernel.hip"]
 HEADERS = ["route_common.hpp", "launch.hpp", "coherent.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -71,7 +71,20 @@ struct GatherLaunch {
     int k, D;
 };
 
+// Expert GEMM1 on the unique-route table's compact rows.
+struct Gemm1Launch {
+    const uint16_t* x;               // bf16 [M, D] token activations
+    const uint16_t* w1;              // bf16 [E, F, D] every expert's GEMM1 weights
+    const int32_t* unique_ids;       // the table (device)
+    const int32_t* token_mask;
+    const int32_t* unique_count;
+    uint16_t* out;                   // bf16 [M*k, F] compact rows
+    int64_t E, F, D;
+    int M, k;
+};
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+hipError_t launch_gemm1(const Gemm1Launch& a, hipStream_t stream);
 hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);

@@ -318,6 +318,33 @@ int router_gather_shared_add_table(const void* y, const int32_t* token_mask,
     return gpt::launch_gather(a, stream) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
+int router_expert_gemm1_table(const void* x, const void* w1, int E, int64_t F, int D,
+                              const int32_t* unique_ids, const int32_t* token_mask,
+                              const int32_t* unique_count, int M, int k, void* out,
+                              hipStream_t stream)
+{
+    if (M < 1 || k < 1 || E < 1 || F < 1 || D < 1) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (k > ROUTER_MAX_K || M > ROUTER_TABLE_MAX_M || M * k > ROUTER_TABLE_MAX_SLOTS || D % 8 != 0)
+        return ROUTER_ERR_UNSUPPORTED;
+    if ((int64_t)M * k * ((F + 63) / 64) > 0x7fffffffLL) return ROUTER_ERR_UNSUPPORTED;
+    if (!x || !w1 || !unique_ids || !token_mask || !unique_count || !out)
+        return ROUTER_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w1)) return ROUTER_ERR_MISALIGNED;
+    gpt::Gemm1Launch a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.w1 = static_cast<const uint16_t*>(w1);
+    a.unique_ids = unique_ids;
+    a.token_mask = token_mask;
+    a.unique_count = unique_count;
+    a.out = static_cast<uint16_t*>(out);
+    a.E = E;
+    a.F = F;
+    a.D = D;
+    a.M = M;
+    a.k = k;
+    return gpt::launch_gemm1(a, stream) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
 int router_topk_from_logits(const float* logits, const float* bias, int64_t M, int E, int k,
                             int scoring, int renorm, int32_t* out_inds, float* out_weights,
                             hipStream_t stream)

@@ -34,7 +34,7 @@ DECODE_MAX_M = 64
 
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
            "router_fwd_mxfp4", "router_topk_from_logits", "router_gather_shared_add",
-           "router_gather_shared_add_table",
+           "router_gather_shared_add_table", "router_expert_gemm1_table",
            "router_set_exchange_timeout_us", "router_strerror")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -72,6 +72,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_gather_shared_add.restype = i32
     lib.router_gather_shared_add_table.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P]
     lib.router_gather_shared_add_table.restype = i32
+    lib.router_expert_gemm1_table.argtypes = [P, P, i32, i64, i32, P, P, P, i32, i32, P, P]
+    lib.router_expert_gemm1_table.restype = i32
     lib.router_topk_from_logits.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, P]
     lib.router_topk_from_logits.restype = i32
     lib.router_set_exchange_timeout_us.argtypes = [i32]
@@ -351,4 +353,32 @@ def router_gather_shared_add_table(y: torch.Tensor, table: dict, weights: torch.
                                                    _ptr(weights), _ptr(shared), M, k, D, _ptr(out),
                                                    _stream(y.device))
     _check(rc, "router_gather_shared_add_table")
+    return out
+
+
+def router_expert_gemm1_table(x: torch.Tensor, w1: torch.Tensor, table: dict, k: int, *,
+                              out: Optional[torch.Tensor] = None):
+    """Expert GEMM1 on the table's compact rows.  x: bf16 [M, D]; w1: bf16 [E, F, D];
+    table: router_fwd_route_table's dict (unique_ids, token_mask, unique_count).
+    Returns bf16 [M*k, F] (rows past the layout's last are left as they were)."""
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    _check_tensor(w1, "w1", torch.bfloat16, 3)
+    M, D = x.shape
+    E, F, D2 = w1.shape
+    if D2 != D:
+        raise ValueError("x and w1 disagree on D")
+    ids, mask, cnt = table["unique_ids"], table["token_mask"], table["unique_count"]
+    for name, t in (("unique_ids", ids), ("token_mask", mask), ("unique_count", cnt)):
+        _check_tensor(t, name, torch.int32, 1)
+    if ids.numel() < M * k or mask.numel() < M * k or cnt.numel() < 1:
+        raise ValueError("table arrays are too short for M*k slots")
+    if out is None:
+        out = torch.empty((M * k, F), dtype=torch.bfloat16, device=x.device)
+    _check_tensor(out, "out", torch.bfloat16, 2)
+    if out.shape[0] < M * k or out.shape[1] != F:
+        raise ValueError("out must be at least [M*k, F]")
+    with torch.cuda.device(x.device):
+        rc = load().router_expert_gemm1_table(_ptr(x), _ptr(w1), E, F, D, _ptr(ids), _ptr(mask),
+                                              _ptr(cnt), M, int(k), _ptr(out), _stream(x.device))
+    _check(rc, "router_expert_gemm1_table")
     return out

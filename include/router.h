@@ -22,6 +22,8 @@
  *     projection on block-scaled FP4 weights (here OCP MXFP4);
  *   - b70 lab MTP1 M=2 note, "Outcome" and "Exact arithmetic": the routed
  *     gather fused with the shared-expert BF16 add that follows the router;
+ *   - b70 lab MTP1 M=2 note, "Why literal source-direct GEMM1 is not
+ *     funded": the expert GEMM1 that consumes the unique-route table;
  *   - b70 lab MTP1 M=2 note, "Unique-route router screen": the optional M=2
  *     unique-route table produced inside the router launch (here also at the
  *     other verify widths of qwisp issue #145, "Observation").
@@ -214,6 +216,28 @@ int router_gather_shared_add_table(const void* y, const int32_t* token_mask,
                                    const int32_t* slot_to_unique, const int32_t* unique_count,
                                    const float* weights, const void* shared, int M, int k, int D,
                                    void* out, hipStream_t stream);
+
+/* Expert GEMM1 consuming the unique-route table (b70 lab MTP1 M=2 note,
+ * "Why literal source-direct GEMM1 is not funded": after deduplicating
+ * identical (token, expert) routes, each expert has the rows [token0],
+ * [token1] or [token0, token1]).  For each unique expert u < unique_count
+ * (expert unique_ids[u]) and each token t of token_mask[u]:
+ *   out[row, f] = bf16( sum over d of x[t,d] * w1[unique_ids[u], f, d] ),
+ * accumulated in fp32 (order of the fp32 sum is the kernel's), rounded once
+ * to nearest-even BF16, with row = the compact row router_gather_shared_add_table
+ * reads (unique experts in table order, each with its tokens in token order).
+ * Each expert's weights are read once per call, however many tokens use it.
+ *   x           bf16 [M, D]       token activations (16-byte aligned)
+ *   w1          bf16 [E, F, D]    every expert's GEMM1 weights (16-byte aligned)
+ *   unique_ids, token_mask, unique_count: router_fwd_route_table's outputs
+ *   out         bf16 [M*k, F]     rows past the layout's last are not written
+ * A unique id outside [0, E) writes nothing for that expert.
+ * Limits: 1 <= M <= ROUTER_TABLE_MAX_M, M*k <= ROUTER_TABLE_MAX_SLOTS,
+ * 1 <= k <= ROUTER_MAX_K, D % 8 == 0.  Uses no workspace. */
+int router_expert_gemm1_table(const void* x, const void* w1, int E, int64_t F, int D,
+                              const int32_t* unique_ids, const int32_t* token_mask,
+                              const int32_t* unique_count, int M, int k, void* out,
+                              hipStream_t stream);
 
 /* Scoring, selection and weights on logits already in HBM (the standalone
  * logits-to-top-k of the unfused pair; dense_router_decode notes, "Current

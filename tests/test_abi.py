@@ -219,3 +219,27 @@ def test_gather_table_rejects(lib, kw, code):
     rc = lib.router_gather_shared_add_table(a["y"], a["mask"], a["s2u"], a["count"], a["weights"],
                                             a["shared"], a["M"], a["k"], a["D"], a["out"], None)
     assert rc == code, (kw, rc)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), R.ERR_INVALID_ARGUMENT),
+    (dict(M=17), R.ERR_UNSUPPORTED),
+    (dict(M=9, k=8), R.ERR_UNSUPPORTED),
+    (dict(k=0), R.ERR_INVALID_ARGUMENT),
+    (dict(E=0), R.ERR_INVALID_ARGUMENT),
+    (dict(F=0), R.ERR_INVALID_ARGUMENT),
+    (dict(D=0), R.ERR_INVALID_ARGUMENT),
+    (dict(D=100), R.ERR_UNSUPPORTED),
+    (dict(x=None), R.ERR_INVALID_ARGUMENT),
+    (dict(w1=None), R.ERR_INVALID_ARGUMENT),
+    (dict(ids=None), R.ERR_INVALID_ARGUMENT),
+    (dict(out=None), R.ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE_ODD), R.ERR_MISALIGNED),
+    (dict(w1=FAKE_ODD), R.ERR_MISALIGNED),
+])
+def test_gemm1_table_rejects(lib, kw, code):
+    a = dict(x=FAKE, w1=FAKE, E=256, F=4096, D=7168, ids=FAKE, mask=FAKE, count=FAKE, M=2, k=6, out=FAKE)
+    a.update(kw)
+    rc = lib.router_expert_gemm1_table(a["x"], a["w1"], a["E"], a["F"], a["D"], a["ids"], a["mask"],
+                                       a["count"], a["M"], a["k"], a["out"], None)
+    assert rc == code, (kw, rc)
