@@ -21,8 +21,9 @@ Also reported (same JSON line):
                 table on/off delta, the MXFP4 gate at M=1 and M=8 (H=7168, a
                 600-matrix 585 MB pool) and at the 8192-token prefill, the
                 routed gather + shared-expert add at M=2 (explicit rows, all
-                remote, table rows) and at M=4096, the standalone top-k at
-                M=4096, and the
+                remote, table rows) and at M=4096, the expert GEMM1 on the
+                table at M=2 (F=4096, D=7168, 15 GB of expert weights), the
+                standalone top-k at M=4096, and the
                 8192-token prefill (tokens/s, fraction of bf16 MFMA and HBM peak).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
@@ -46,8 +47,10 @@ POOL = 160
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_M1_H7168_traffic.txt")
 MX_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_mxfp4_M1_H7168_traffic.txt")
 GATHER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gather_shared_add_M2_k6_D7168_traffic.txt")
+GEMM1_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_gemm1_M2_k6_F4096_D7168_traffic.txt")
 KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
 GATHER_SOURCES = ["gather_kernel.hip", "route_common.hpp", "launch.hpp", "router_api.cpp"]
+GEMM1_SOURCES = ["gemm1_kernel.hip", "route_common.hpp", "coherent.hpp", "launch.hpp", "router_api.cpp"]
 
 
 def log(msg):
@@ -59,7 +62,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "gather", "prefill", "topk"],
+    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "gather", "gemm1", "prefill", "topk"],
                     default="all",
                     help="restrict to one workload (for counter-collection runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -201,6 +204,8 @@ def main():
         out["extras"].update(mxfp4_extras(torch, R, W, dev, args))
     if args.section in ("all", "gather"):
         out["extras"].update(gather_extras(torch, R, W, dev, args))
+    if args.section in ("all", "gemm1"):
+        out["extras"].update(gemm1_extras(torch, R, W, dev, args))
     if args.section in ("all", "topk"):
         out["extras"].update(topk_extras(torch, R, W, dev, args))
     if args.section in ("all", "prefill"):
@@ -432,6 +437,42 @@ def gather_extras(torch, R, W, dev, args):
     ex["gather_M4096_k8_D7168_hbm_frac"] = round(bbytes / (b_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     del yb
     log("gather done")
+    return ex
+
+
+def gemm1_extras(torch, R, W, dev, args):
+    """Expert GEMM1 on the unique-route table at the MTP1 pair: M=2, k=6, E=256
+    experts of F=4096 (gate and up, 2 x 2048) by D=7168 in bf16 (15 GB of expert
+    weights); 40 calls per step, each on the table one router call produced for
+    its own pair of tokens, so every call reads its unique experts' weights cold."""
+    ex = {}
+    M, k, E, F, D = 2, 6, 256, 4096, 7168
+    log(f"generating expert weights: {E}x{F}x{D} bf16")
+    w1 = torch.empty((E, F, D), dtype=torch.bfloat16, device=dev)
+    for e0 in range(0, E, 16):
+        w1[e0:e0 + 16] = W.torch_gaussian_bf16((16, F, D), 0.02, seed=60 + e0, device=dev)
+    gate = W.torch_gaussian_bf16((E, D), 1.0 / D ** 0.5, seed=61, device=dev)
+    bias = W.torch_uniform_f32(E, -0.05, 0.05, seed=62, device=dev)
+    xs = W.torch_rms_normalised_bf16((LAYERS, M, D), seed=63, device=dev)
+    tables = [R.router_fwd_route_table(xs[l], gate, bias, k, W.SQRT_SOFTPLUS, True) for l in range(LAYERS)]
+    torch.cuda.synchronize()
+    uniq = [int(t["unique_count"].item()) for t in tables]
+    outs = torch.empty((LAYERS, M * k, F), dtype=torch.bfloat16, device=dev)
+    g = GraphTimer(torch, [(lambda l=l: R.router_expert_gemm1_table(xs[l], w1, tables[l], k, out=outs[l]))
+                           for l in range(LAYERS)])
+    wall, ev_ms = timed_replays(torch, [g], max(args.steps // 2, 2), 2)
+    n = max(args.steps // 2, 2) * LAYERS
+    launch_us = ev_ms * 1e3 / n
+    mean_u = sum(uniq) / len(uniq)
+    algo = mean_u * F * D * 2 + M * D * 2 + M * k * F * 2  # unique experts' weights + x + the M*k rows written
+    ex["gemm1_M2_k6_F4096_D7168_us_per_call"] = round(wall * 1e6 / n, 2)
+    ex["gemm1_M2_k6_F4096_D7168_launch_us"] = round(launch_us, 2)
+    ex["gemm1_mean_unique_experts"] = round(mean_u, 2)
+    ex["gemm1_bytes_per_launch"] = round(algo)
+    ex["gemm1_hbm_frac"] = round(algo / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    ex["gemm1_traffic"] = committed_traffic(GEMM1_TRAFFIC_SUMMARY, GEMM1_SOURCES)
+    del g, w1
+    log("gemm1 done")
     return ex
 
 
