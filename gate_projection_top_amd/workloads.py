@@ -280,6 +280,46 @@ def mxfp4_case(M: int, H: int = 4096, seed: int = 0, E: int = 256, k: int = 8,
                   name=f"mxfp4/M{M}/H{H}/E{E}/k{k}/s{scoring}/b{int(with_bias)}/seed{seed}")
 
 
+def _e4m3_magnitudes() -> np.ndarray:
+    """The 127 non-negative finite OCP FP8 E4M3 magnitudes, indexed by code 0..126."""
+    c = np.arange(127)
+    ex, fr = c >> 3, (c & 7).astype(np.float64)
+    return np.where(ex == 0, fr / 8.0 * 2.0 ** -6, (1.0 + fr / 8.0) * np.exp2(ex - 7.0))
+
+
+E4M3_MAGNITUDES = _e4m3_magnitudes()
+
+
+def quantise_mxfp8(w: np.ndarray):
+    """Synthetic MXFP8 (E4M3) weights from real ones [E, H] (H % 32 == 0): per 32-block an
+    E8M0 scale 2^(ceil(log2(amax / 448))) (the block's largest magnitude fits E4M3's 448),
+    clamped to scale bytes 10..246, codes by nearest magnitude, sign in bit 7.  Returns
+    (elems uint8 [E, H], scales uint8 [E, H/32]).  Input construction only."""
+    E, H = w.shape
+    assert H % 32 == 0
+    blocks = w.astype(np.float64).reshape(E, H // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    ex = np.ceil(np.log2(np.maximum(amax, 1e-30) / 448.0)).astype(np.int64)
+    ex = np.clip(ex, 10 - 127, 246 - 127)
+    scaled = blocks / np.ldexp(1.0, ex)[:, :, None]
+    code = np.abs(np.abs(scaled)[..., None] - E4M3_MAGNITUDES).argmin(axis=-1)
+    code = code | np.where(scaled < 0, 0x80, 0)
+    return code.reshape(E, H).astype(np.uint8), (ex + 127).astype(np.uint8)
+
+
+def mxfp8_case(M: int, H: int = 4096, seed: int = 0, E: int = 256, k: int = 8,
+               scoring: int = SOFTMAX, with_bias: bool = False, renorm: bool = True) -> MxCase:
+    """Router on MXFP8 gate weights: X = unit-RMS N(0,1) rows in bf16, W ~ N(0,1/H)
+    quantised to MXFP8 (quantise_mxfp8); optional U(-0.05,0.05) selection bias."""
+    rng = _rng(seed, 13)
+    x = rms_normalised_bf16(rng, M, H)
+    w = rng.standard_normal((E, H)) / np.sqrt(H)
+    elems, scales = quantise_mxfp8(w)
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32) if with_bias else None
+    return MxCase(x, elems, scales, bias, k, scoring, renorm,
+                  name=f"mxfp8/M{M}/H{H}/E{E}/k{k}/s{scoring}/b{int(with_bias)}/seed{seed}")
+
+
 def prefill_case(M: int = 8192, H: int = 7168, seed: int = 0, E: int = 256, k: int = 8) -> RouterCase:
     """Prefill router: softmax scores with U(-0.02,0.02) selection-only bias."""
     rng = _rng(seed, 6)
@@ -464,3 +504,16 @@ def gather_case(M: int, k: int, D: int, pattern: str = "typical", seed: int = 0,
         rows = np.stack([rng.choice(R, k, replace=R < k) for _ in range(M)])
     return GatherCase(y, rows.astype(np.int32), w.astype(np.float32), shared,
                       name=f"gather/{pattern}/M{M}/k{k}/D{D}/R{R}/seed{seed}")
+
+
+def torch_mxfp8_gate(n: int, E: int, H: int, seed: int, device, scale_lo: int = 116, scale_hi: int = 121):
+    """n MXFP8 gate matrices on `device`: E4M3 code bytes uniform over the finite codes
+    [n, E, H] and E8M0 scale bytes uniform over scale_lo..scale_hi [n, E, H/32]."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    codes = torch.randint(0, 256, (n, E, H), generator=g, device=device, dtype=torch.uint8)
+    codes = torch.where((codes & 0x7F) == 0x7F, codes ^ 0x01, codes)  # NaN patterns -> +-1.75*2^8
+    scales = torch.randint(scale_lo, scale_hi + 1, (n, E, H // 32), generator=g, device=device,
+                           dtype=torch.uint8)
+    return codes, scales

@@ -58,6 +58,12 @@ class Oracle:
         lib.oracle_dequant_mxfp4.restype = ci
         lib.oracle_router_mxfp4.argtypes = [P, P, P, P, i64, i64, i64, ci, ci, ci, P, P, P, P]
         lib.oracle_router_mxfp4.restype = ci
+        lib.oracle_e4m3_value.argtypes = [ci]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_dequant_mxfp8.argtypes = [P, P, i64, i64, P]
+        lib.oracle_dequant_mxfp8.restype = ci
+        lib.oracle_router_mxfp8.argtypes = [P, P, P, P, i64, i64, i64, ci, ci, ci, P, P, P, P]
+        lib.oracle_router_mxfp8.restype = ci
         lib.oracle_bf16_round.argtypes = [ctypes.c_float]
         lib.oracle_bf16_round.restype = ctypes.c_uint16
         lib.oracle_gather_shared_add.argtypes = [P, i64, i64, P, P, P, i64, ci, P]
@@ -157,6 +163,40 @@ class Oracle:
                                           self._ptr(inds), self._ptr(wts), self._ptr(lg), self._ptr(ad))
         if rc:
             raise ValueError(f"oracle_router_mxfp4 failed: {rc}")
+        return inds, wts, lg, ad
+
+    def e4m3_value(self, code: int) -> float:
+        return float(self.lib.oracle_e4m3_value(int(code)))
+
+    def dequant_mxfp8(self, elems: np.ndarray, scales: np.ndarray) -> np.ndarray:
+        elems = np.ascontiguousarray(elems, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        E, H = elems.shape
+        w = np.empty((E, H), np.float64)
+        rc = self.lib.oracle_dequant_mxfp8(self._ptr(elems), self._ptr(scales), E, H, self._ptr(w))
+        if rc:
+            raise ValueError(f"oracle_dequant_mxfp8 failed: {rc}")
+        return w
+
+    def router_mxfp8(self, x: np.ndarray, elems: np.ndarray, scales: np.ndarray,
+                     bias: Optional[np.ndarray], k: int, scoring: int, renorm: bool):
+        """Router on MXFP8 gate weights: (inds, weights, logits, absdot)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        elems = np.ascontiguousarray(elems, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        M, H = x.shape
+        E = elems.shape[0]
+        assert elems.shape[1] == H and scales.shape == (E, H // 32)
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        inds = np.empty((M, k), np.int32)
+        wts = np.empty((M, k), np.float32)
+        lg = np.empty((M, E), np.float32)
+        ad = np.empty((M, E), np.float64)
+        rc = self.lib.oracle_router_mxfp8(self._ptr(x), self._ptr(elems), self._ptr(scales),
+                                          self._ptr(b), M, H, E, k, int(scoring), int(bool(renorm)),
+                                          self._ptr(inds), self._ptr(wts), self._ptr(lg), self._ptr(ad))
+        if rc:
+            raise ValueError(f"oracle_router_mxfp8 failed: {rc}")
         return inds, wts, lg, ad
 
     def route_table(self, inds: np.ndarray):

@@ -222,6 +222,32 @@ int oracle_dequant_mxfp4(const uint8_t* elems, const uint8_t* scales, int64_t E,
     return 0;
 }
 
+/* The router on dequantised block-scaled weights w [E, H] (doubles): exact
+ * dot products with the bf16 activations, then the router's selection. */
+static int router_on_dequantised(const uint16_t* x, const double* w, const float* bias, int64_t M,
+                                 int64_t H, int64_t E, int k, int scoring, int renorm,
+                                 int32_t* inds, float* weights, float* logits_out,
+                                 double* absdot_out)
+{
+    float* l = logits_out ? logits_out : (float*)calloc((size_t)(M * E), sizeof(float));
+    if (!l) return ORACLE_ENOMEM;
+    for (int64_t t = 0; t < M; ++t)
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0, absacc = 0.0;
+            for (int64_t col = 0; col < H; ++col) {
+                /* bf16 times a block-scaled FP4/FP8 value: exact in double */
+                double p = bf16_value(x[t * H + col]) * w[e * H + col];
+                acc += p;
+                absacc += fabs(p);
+            }
+            l[t * E + e] = (float)acc;
+            if (absdot_out) absdot_out[t * E + e] = absacc;
+        }
+    int rc = oracle_topk_from_logits(l, bias, M, E, k, scoring, renorm, inds, weights);
+    if (!logits_out) free(l);
+    return rc;
+}
+
 int oracle_router_mxfp4(const uint16_t* x, const uint8_t* elems, const uint8_t* scales,
                         const float* bias, int64_t M, int64_t H, int64_t E, int k, int scoring,
                         int renorm, int32_t* inds, float* weights, float* logits_out,
@@ -231,28 +257,57 @@ int oracle_router_mxfp4(const uint16_t* x, const uint8_t* elems, const uint8_t* 
     if (M == 0) return 0;
     if (!x) return ORACLE_EINVAL;
     double* w = (double*)malloc((size_t)(E * H) * sizeof(double));
-    float* l = logits_out ? logits_out : (float*)malloc((size_t)(M * E) * sizeof(float));
-    if (!w || !l) {
-        free(w);
-        if (!logits_out) free(l);
-        return ORACLE_ENOMEM;
-    }
+    if (!w) return ORACLE_ENOMEM;
     int rc = oracle_dequant_mxfp4(elems, scales, E, H, w);
-    for (int64_t t = 0; !rc && t < M; ++t)
-        for (int64_t e = 0; e < E; ++e) {
-            double acc = 0.0, absacc = 0.0;
-            for (int64_t col = 0; col < H; ++col) {
-                /* bf16 times a 2-bit-mantissa power-of-two multiple: exact in double */
-                double p = bf16_value(x[t * H + col]) * w[e * H + col];
-                acc += p;
-                absacc += fabs(p);
-            }
-            l[t * E + e] = (float)acc;
-            if (absdot_out) absdot_out[t * E + e] = absacc;
-        }
-    if (!rc) rc = oracle_topk_from_logits(l, bias, M, E, k, scoring, renorm, inds, weights);
+    if (!rc)
+        rc = router_on_dequantised(x, w, bias, M, H, E, k, scoring, renorm, inds, weights, logits_out,
+                                   absdot_out);
     free(w);
-    if (!logits_out) free(l);
+    return rc;
+}
+
+/* OCP FP8 E4M3 (OCP 8-bit Floating Point Specification; Microscaling
+ * Formats v1.0 element type): sign bit 7, exponent bits 6..3 with bias 7,
+ * mantissa bits 2..0; exponent field 0 is subnormal, frac/8 * 2^-6; the
+ * pattern S.1111.111 is NaN; there are no infinities (largest value 448). */
+double oracle_e4m3_value(int code)
+{
+    const int negative = (code >> 7) & 1, biased = (code >> 3) & 15, frac = code & 7;
+    if (biased == 15 && frac == 7) return NAN;
+    const double magnitude = biased == 0 ? ldexp(frac / 8.0, -6) : ldexp(1.0 + frac / 8.0, biased - 7);
+    return negative ? -magnitude : magnitude;
+}
+
+int oracle_dequant_mxfp8(const uint8_t* elems, const uint8_t* scales, int64_t E, int64_t H,
+                         double* w)
+{
+    if (E < 1 || H < 32 || H % 32 != 0 || !elems || !scales || !w) return ORACLE_EINVAL;
+    for (int64_t row = 0; row < E; ++row)
+        for (int64_t idx = 0; idx < H; ++idx) {
+            const int s8 = scales[row * (H / 32) + idx / 32];
+            if (s8 < ORACLE_MX8_SCALE_MIN || s8 > ORACLE_MX8_SCALE_MAX) return ORACLE_EINVAL;
+            const double v = oracle_e4m3_value(elems[row * H + idx]);  /* one code per byte */
+            if (isnan(v)) return ORACLE_EINVAL;
+            w[row * H + idx] = ldexp(v, s8 - 127);
+        }
+    return 0;
+}
+
+int oracle_router_mxfp8(const uint16_t* x, const uint8_t* elems, const uint8_t* scales,
+                        const float* bias, int64_t M, int64_t H, int64_t E, int k, int scoring,
+                        int renorm, int32_t* inds, float* weights, float* logits_out,
+                        double* absdot_out)
+{
+    if (M < 0 || H < 32 || E < 1 || k < 1 || k > E) return ORACLE_EINVAL;
+    if (M == 0) return 0;
+    if (!x) return ORACLE_EINVAL;
+    double* w8 = (double*)malloc((size_t)(E * H) * sizeof(double));
+    if (!w8) return ORACLE_ENOMEM;
+    int rc = oracle_dequant_mxfp8(elems, scales, E, H, w8);
+    if (!rc)
+        rc = router_on_dequantised(x, w8, bias, M, H, E, k, scoring, renorm, inds, weights,
+                                   logits_out, absdot_out);
+    free(w8);
     return rc;
 }
 

@@ -65,6 +65,23 @@ int oracle_router_mxfp4(const uint16_t* x, const uint8_t* elems, const uint8_t* 
                         int renorm, int32_t* inds, float* weights, float* logits_out,
                         double* absdot_out);
 
+/* MXFP8 gate weights (OCP Microscaling Formats v1.0, FP8 E4M3 elements):
+ * elems: uint8 [E, H], one E4M3 code per element; scales: uint8 [E, H/32],
+ * E8M0: element i of row e is e4m3(code) * 2^(scales[e, i/32] - 127).
+ * Scales outside [ORACLE_MX8_SCALE_MIN, ORACLE_MX8_SCALE_MAX] or NaN codes
+ * are refused (inside, every dequantised weight is zero or a normal bf16
+ * value: the smallest E4M3 magnitude is 2^-9, the largest 448). */
+#define ORACLE_MX8_SCALE_MIN 10
+#define ORACLE_MX8_SCALE_MAX 246
+double oracle_e4m3_value(int code);
+int oracle_dequant_mxfp8(const uint8_t* elems, const uint8_t* scales, int64_t E, int64_t H,
+                         double* w);
+/* The router on MXFP8 gate weights (as oracle_router_mxfp4). */
+int oracle_router_mxfp8(const uint16_t* x, const uint8_t* elems, const uint8_t* scales,
+                        const float* bias, int64_t M, int64_t H, int64_t E, int k, int scoring,
+                        int renorm, int32_t* inds, float* weights, float* logits_out,
+                        double* absdot_out);
+
 /* The whole router: logits then oracle_topk_from_logits.  logits_out [M,E]
  * and absdot_out [M,E] are optional (NULL). */
 int oracle_router(const uint16_t* x, const uint16_t* w, const float* bias, int64_t M,

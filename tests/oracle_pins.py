@@ -760,6 +760,82 @@ def pin_gemm1_blas_and_table_rows(o):
                 assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), (M, t, j)
 
 
+# OCP FP8 E4M3 values worked out by hand from the format's definition (sign,
+# 4-bit exponent with bias 7, 3-bit mantissa, subnormals at exponent 0, NaN at
+# S.1111.111, no infinities)
+E4M3_HAND = {0x00: 0.0, 0x01: 2.0 ** -9, 0x02: 2.0 ** -8, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+             0x0F: 1.875 * 2.0 ** -6, 0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0,
+             0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0x80: -0.0, 0x81: -(2.0 ** -9), 0xB8: -1.0,
+             0xC4: -3.0, 0xFE: -448.0}
+
+
+def _e4m3_numpy(codes):
+    """E4M3 decoding with numpy's vector arithmetic (no loop over the format)."""
+    c = codes.astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 15
+    fr = (c & 7).astype(np.float64)
+    mag = np.where(ex == 0, fr / 8.0 * 2.0 ** -6, (1.0 + fr / 8.0) * np.exp2(ex - 7.0))
+    return sign * mag
+
+
+def pin_e4m3_table(o):
+    for code, v in E4M3_HAND.items():
+        got = o.e4m3_value(code)
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), (hex(code), got, v)
+    assert math.isnan(o.e4m3_value(0x7F)) and math.isnan(o.e4m3_value(0xFF))
+    finite = [c for c in range(256) if c & 0x7F != 0x7F]
+    assert np.array_equal(np.array([o.e4m3_value(c) for c in finite]), _e4m3_numpy(np.array(finite)))
+    assert max(abs(o.e4m3_value(c)) for c in finite) == 448.0
+
+
+def pin_mx8_dequant(o):
+    rng = np.random.default_rng(60)
+    E, H = 5, 96
+    codes = rng.integers(0, 256, (E, H)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C
+    scales = rng.integers(10, 247, (E, H // 32)).astype(np.uint8)
+    w = o.dequant_mxfp8(codes, scales)
+    ref = _e4m3_numpy(codes) * np.exp2(np.repeat(scales.astype(np.float64), 32, axis=1) - 127.0)
+    assert np.array_equal(w, ref)
+    for bad_scale in (9, 247):
+        sc = scales.copy()
+        sc[2, 1] = bad_scale
+        try:
+            o.dequant_mxfp8(codes, sc)
+        except ValueError:
+            continue
+        raise AssertionError(f"scale {bad_scale} accepted")
+    nan_codes = codes.copy()
+    nan_codes[1, 7] = 0xFF
+    try:
+        o.dequant_mxfp8(nan_codes, scales)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("NaN code accepted")
+
+
+def pin_mx8_router_is_bf16_router_on_dequantised(o):
+    """Every dequantised MXFP8 weight is a bf16 value, so the MXFP8 router equals the
+    bf16 router on those weights bit for bit."""
+    rng = np.random.default_rng(61)
+    M, H, E, k = 3, 128, 32, 4
+    x = W.gaussian_bf16(rng, (M, H), 1.0)
+    codes = rng.integers(0, 256, (E, H)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x2A
+    scales = rng.integers(115, 125, (E, H // 32)).astype(np.uint8)
+    wd = o.dequant_mxfp8(codes, scales)
+    wb = W.f32_to_bf16_bits(wd.astype(np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(wb).astype(np.float64), wd)
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    for scoring in (SOFTMAX, SQRT_SOFTPLUS):
+        a = o.router_mxfp8(x, codes, scales, bias, k, scoring, True)
+        b = o.router(x, wb, bias, k, scoring, True)
+        for p, q in zip(a, b):
+            assert np.array_equal(p, q)
+
+
 ALL_PINS = [
     pin_logits_small_integers, pin_logits_rational, pin_logits_one_hot, pin_logits_blas,
     pin_softplus_closed_forms, pin_softplus_logaddexp, pin_softmax_closed_forms,
@@ -773,4 +849,5 @@ ALL_PINS = [
     pin_bf16_round, pin_gather_exact_dyadic, pin_gather_hand_cases, pin_gather_invariants,
     pin_table_rows_hand_cases, pin_table_rows_invariants,
     pin_gemm1_hand_table, pin_gemm1_one_hot, pin_gemm1_blas_and_table_rows,
+    pin_e4m3_table, pin_mx8_dequant, pin_mx8_router_is_bf16_router_on_dequantised,
 ]

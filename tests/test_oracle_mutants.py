@@ -74,6 +74,11 @@ MUTANTS = [
     ("gemm1_drops_last_term", "for (int64_t d = 0; d < D; ++d) {\n                    const double prod",
      "for (int64_t d = 0; d + 1 < D; ++d) {\n                    const double prod"),
     ("gemm1_absdot_signed", "amag += fabs(prod);", "amag += prod;"),
+    ("e4m3_exponent_bias", "ldexp(1.0 + frac / 8.0, biased - 7)", "ldexp(1.0 + frac / 8.0, biased - 8)"),
+    ("e4m3_subnormal_exponent", "ldexp(frac / 8.0, -6)", "ldexp(frac / 8.0, -7)"),
+    ("e4m3_nan_pattern", "if (biased == 15 && frac == 7) return NAN;", "if (biased == 15 && frac >= 6) return NAN;"),
+    ("e4m3_sign_dropped", "return negative ? -magnitude : magnitude;", "return magnitude;"),
+    ("mx8_scale_bias", "w[row * H + idx] = ldexp(v, s8 - 127);", "w[row * H + idx] = ldexp(v, s8 - 126);"),
 ]
 
 
