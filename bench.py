@@ -18,8 +18,8 @@ Also reported (same JSON line):
                 sources still match it, else null;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   extras        cache-hot cycle, verify widths M=2/8 at H=4096, the biased M=2
-                table on/off delta, the MXFP4 gate at M=1 and M=8 (H=7168, a
-                600-matrix 585 MB pool) and at the 8192-token prefill, the
+                table on/off delta, the MXFP4 and MXFP8 gates at M=1 and M=8
+                (H=7168, 585 / 606 MB pools) and at the 8192-token prefill, the
                 routed gather + shared-expert add at M=2 (explicit rows, all
                 remote, table rows) and at M=4096, the expert GEMM1 on the
                 table at M=2 (F=4096, D=7168, 15 GB of expert weights), the
@@ -45,7 +45,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 LAYERS = 40
 POOL = 160
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_M1_H7168_traffic.txt")
-MX_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_mxfp4_M1_H7168_traffic.txt")
+MX_TRAFFIC_SUMMARY = {f: os.path.join(ROOT, "profiles", f"decode_router_{f}_M1_H7168_traffic.txt")
+                      for f in ("mxfp4", "mxfp8")}
 GATHER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gather_shared_add_M2_k6_D7168_traffic.txt")
 GEMM1_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_gemm1_M2_k6_F4096_D7168_traffic.txt")
 KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
@@ -62,13 +63,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "gather", "gemm1", "prefill", "topk"],
+    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "mxfp8", "gather", "gemm1", "prefill", "topk"],
                     default="all",
                     help="restrict to one workload (for counter-collection runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--mxfp4-widths", default="1,8",
                     help="token counts of the MXFP4 section (comma-separated, each <= 64)")
+    ap.add_argument("--mxfp8-widths", default="1,8",
+                    help="token counts of the MXFP8 section (comma-separated, each <= 64)")
     ap.add_argument("--gather-disjoint-only", action="store_true",
                     help="gather section: only the M=2 explicit-row case (counter-collection runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -200,8 +203,9 @@ def main():
         decode_headline(torch, R, W, dev, args, out)
     if args.section in ("all",):
         out["extras"].update(decode_extras(torch, R, W, dev, args))
-    if args.section in ("all", "mxfp4"):
-        out["extras"].update(mxfp4_extras(torch, R, W, dev, args))
+    for fmt in ("mxfp4", "mxfp8"):
+        if args.section in ("all", fmt):
+            out["extras"].update(block_scaled_extras(torch, R, W, dev, args, fmt))
     if args.section in ("all", "gather"):
         out["extras"].update(gather_extras(torch, R, W, dev, args))
     if args.section in ("all", "gemm1"):
@@ -325,51 +329,59 @@ def decode_extras(torch, R, W, dev, args):
     return ex
 
 
-def mxfp4_extras(torch, R, W, dev, args):
-    """router_fwd_mxfp4 at M=1 and M=8, H=7168: 40 calls per step, each with
-    its own MXFP4 gate from a 600-matrix pool (585 MB, cold)."""
+def block_scaled_extras(torch, R, W, dev, args, fmt):
+    """The router on a block-scaled gate (fmt "mxfp4" or "mxfp8") at the decode
+    widths of --<fmt>-widths, H=7168: 40 calls per step, each with its own gate
+    from a pool larger than twice the Infinity Cache (MXFP4: 600 matrices,
+    585 MB; MXFP8: 320 matrices, 606 MB), cold; and the 8192-token prefill."""
     ex = {}
-    H, E, k, pool = 7168, 256, 8, 600
-    codes, scales = W.torch_mxfp4_gate(pool, E, H, seed=30, device=dev)
+    H, E, k = 7168, 256, 8
+    if fmt == "mxfp4":
+        pool, gate, fwd, widths = 600, W.torch_mxfp4_gate, R.router_fwd_mxfp4, args.mxfp4_widths
+        code_bytes, seeds = E * H // 2, (30, 31, 35, 36, 37)
+    else:
+        pool, gate, fwd, widths = 320, W.torch_mxfp8_gate, R.router_fwd_mxfp8, args.mxfp8_widths
+        code_bytes, seeds = E * H, (40, 41, 45, 46, 47)
+    codes, scales = gate(pool, E, H, seed=seeds[0], device=dev)
     groups = pool // LAYERS
-    for M in [int(m) for m in args.mxfp4_widths.split(",")]:
-        x = W.torch_rms_normalised_bf16((LAYERS, M, H), seed=31 + M, device=dev)
+    for M in [int(m) for m in widths.split(",")]:
+        x = W.torch_rms_normalised_bf16((LAYERS, M, H), seed=seeds[1] + M, device=dev)
         oi = torch.empty((LAYERS, M, k), dtype=torch.int32, device=dev)
         ow = torch.empty((LAYERS, M, k), dtype=torch.float32, device=dev)
 
         def call(l, widx, x=x, oi=oi, ow=ow):
-            return lambda: R.router_fwd_mxfp4(x[l], codes[widx], scales[widx], None, k, W.SOFTMAX,
-                                              True, out_inds=oi[l], out_weights=ow[l])
+            return lambda: fwd(x[l], codes[widx], scales[widx], None, k, W.SOFTMAX,
+                               True, out_inds=oi[l], out_weights=ow[l])
 
         graphs = [GraphTimer(torch, [call(l, g * LAYERS + l) for l in range(LAYERS)])
                   for g in range(groups)]
         wall, ev_ms = timed_replays(torch, graphs, args.steps, args.warmup)
         launch_us = ev_ms * 1e3 / (args.steps * LAYERS)
-        ex[f"mxfp4_decode_M{M}_H7168_us_per_call"] = round(wall * 1e6 / (args.steps * LAYERS), 3)
-        ex[f"mxfp4_decode_M{M}_H7168_launch_us"] = round(launch_us, 3)
+        ex[f"{fmt}_decode_M{M}_H7168_us_per_call"] = round(wall * 1e6 / (args.steps * LAYERS), 3)
+        ex[f"{fmt}_decode_M{M}_H7168_launch_us"] = round(launch_us, 3)
         if M == 1:
-            algo = E * H // 2 + E * H // 32 + M * H * 2 + M * k * 8  # codes + scales + x + outputs
-            ex["mxfp4_decode_M1_bytes_per_launch"] = algo
-            ex["mxfp4_decode_M1_hbm_frac"] = round(algo / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-            ex["mxfp4_decode_M1_traffic"] = committed_traffic(MX_TRAFFIC_SUMMARY)
+            algo = code_bytes + E * H // 32 + M * H * 2 + M * k * 8  # codes + scales + x + outputs
+            ex[f"{fmt}_decode_M1_bytes_per_launch"] = algo
+            ex[f"{fmt}_decode_M1_hbm_frac"] = round(algo / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            ex[f"{fmt}_decode_M1_traffic"] = committed_traffic(MX_TRAFFIC_SUMMARY[fmt])
         del graphs
     del codes, scales
-    # prefill: M=8192 tokens over four cold 117 MB activations, one MXFP4 gate
+    # prefill: M=8192 tokens over four cold 117 MB activations, one gate
     M = 8192
-    xs = W.torch_gaussian_bf16((4, M, H), 1.0, seed=35, device=dev)
-    pc, psc = W.torch_mxfp4_gate(1, E, H, seed=36, device=dev)
-    bp = W.torch_uniform_f32(E, -0.02, 0.02, seed=37, device=dev)
+    xs = W.torch_gaussian_bf16((4, M, H), 1.0, seed=seeds[2], device=dev)
+    pc, psc = gate(1, E, H, seed=seeds[3], device=dev)
+    bp = W.torch_uniform_f32(E, -0.02, 0.02, seed=seeds[4], device=dev)
     pi = torch.empty((M, k), dtype=torch.int32, device=dev)
     pw = torch.empty((M, k), dtype=torch.float32, device=dev)
-    calls = [(lambda i=i: R.router_fwd_mxfp4(xs[i], pc[0], psc[0], bp, k, W.SOFTMAX, True,
-                                             out_inds=pi, out_weights=pw)) for i in range(4)]
+    calls = [(lambda i=i: fwd(xs[i], pc[0], psc[0], bp, k, W.SOFTMAX, True,
+                              out_inds=pi, out_weights=pw)) for i in range(4)]
     p_us = graph_call_us(torch, calls, max(args.steps // 2, 2), 2)
     tflops = 2.0 * M * E * H / (p_us * 1e-6) / 1e12
-    ex["mxfp4_prefill_M8192_H7168_event_us_per_call"] = round(p_us, 2)
-    ex["mxfp4_prefill_M8192_tokens_per_s"] = round(M / (p_us * 1e-6), 0)
-    ex["mxfp4_prefill_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
+    ex[f"{fmt}_prefill_M8192_H7168_event_us_per_call"] = round(p_us, 2)
+    ex[f"{fmt}_prefill_M8192_tokens_per_s"] = round(M / (p_us * 1e-6), 0)
+    ex[f"{fmt}_prefill_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
     del xs
-    log("mxfp4 done")
+    log(f"{fmt} done")
     return ex
 
 

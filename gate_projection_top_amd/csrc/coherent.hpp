@@ -12,6 +12,7 @@
 namespace gpt {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCoherent = 16;  // buffer cache-policy bit: device scope

@@ -93,9 +93,9 @@ __device__ __forceinline__ f32x4 poll_sum(const f32x4 (&p)[kMaxS])
     return sum;
 }
 
-constexpr int kMxChunk = 2;  // MXFP4 gate: 128-wide k blocks whose loads a wave issues together
+constexpr int kMxChunk = 2;  // block-scaled gate: 128-wide k blocks whose loads a wave issues together
 
-template <int kLoadWaves, int kMaxS, bool kMx>
+template <int kLoadWaves, int kMaxS, int kFmt>
 __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel(DecodeLaunch a)
 {
     constexpr int kWaves = kLoadWaves + 1;  // + the control wave
@@ -155,7 +155,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         const bool bcol_ok = bcol < a.E;
         const bf16x8 zero = __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0});
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (!kMx) {
+        if constexpr (kFmt == kGateBf16) {
             const int kq = (lane >> 4) * 8;  // this lane's 8 of the 32 k
             const uint16_t* xp = a.x + (int64_t)(arow_ok ? arow : 0) * a.H + kq;
             const uint16_t* wp = a.w + (int64_t)(bcol_ok ? bcol : 0) * a.H + kq;
@@ -180,21 +180,24 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv[c], acc, 0, 0, 0);
             }
         } else {
-            // MXFP4 gate, in 128-wide k blocks.  Lane (expert, g) loads the 32
-            // codes of k in [128 kb + 32 g, +32) (16 bytes) and their block's
-            // scale; MFMA step j of the block gives k-slots 8g..8g+7 the k
-            // values 128 kb + 32 g + 8 j + (0..7), for X as for W, so every k
-            // is counted once.  (H % 32 == 0: a lane's 32 codes are in or out.)
+            // Block-scaled gate, in 128-wide k blocks.  Lane (expert, g) loads
+            // the 32 codes of k in [128 kb + 32 g, +32) (16 bytes of MXFP4, 32
+            // of MXFP8) and their block's scale; MFMA step j of the block gives
+            // k-slots 8g..8g+7 the k values 128 kb + 32 g + 8 j + (0..7), for X
+            // as for W, so every k is counted once.  (H % 32 == 0: a lane's 32
+            // codes are in or out.)
+            constexpr int kCodeBytes = kFmt == kGateMxfp8 ? 2 : 1;  // MXFP8: 2x16 bytes per 32 codes
+            constexpr int kRowDiv = kFmt == kGateMxfp8 ? 1 : 2;     // code bytes per row = H / kRowDiv
             const int g = lane >> 4;
             const uint16_t* xrow = a.x + (int64_t)(arow_ok ? arow : 0) * a.H;
-            const uint8_t* wrow = a.w_fp4 + (int64_t)(bcol_ok ? bcol : 0) * (a.H / 2);
+            const uint8_t* wrow = a.w_codes + (int64_t)(bcol_ok ? bcol : 0) * (a.H / kRowDiv);
             const uint8_t* srow = a.w_scale + (int64_t)(bcol_ok ? bcol : 0) * (a.H / 32);
             const int KB = (a.H + 127) >> 7;
             const int kb0 = s * a.ks_per_split;
             const int kb1 = min(KB, kb0 + a.ks_per_split);
             const int wave_u = __builtin_amdgcn_readfirstlane(wave);
             for (int base = kb0 + wave_u; base < kb1; base += kLoadWaves * kMxChunk) {
-                u32x4 wv[kMxChunk];
+                u32x4 wv[kMxChunk][kCodeBytes];
                 uint32_t sv[kMxChunk];
                 bool wok[kMxChunk];
                 bf16x8 xv[kMxChunk][4];
@@ -211,7 +214,8 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
 #pragma unroll
                 for (int c = 0; c < kMxChunk; ++c) {
                     const int kb = base + c * kLoadWaves;
-                    wv[c] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int h = 0; h < kCodeBytes; ++h) wv[c][h] = u32x4{0u, 0u, 0u, 0u};
                     sv[c] = 0u;
                     wok[c] = false;
 #pragma unroll
@@ -220,7 +224,9 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                         const int k0 = kb * 128 + 32 * g;
                         const bool in = k0 < a.H;
                         const int kc = in ? k0 : kb * 128;
-                        wv[c] = *reinterpret_cast<const u32x4*>(wrow + kc / 2);
+#pragma unroll
+                        for (int h = 0; h < kCodeBytes; ++h)
+                            wv[c][h] = *reinterpret_cast<const u32x4*>(wrow + kc / kRowDiv + 16 * h);
                         sv[c] = srow[kc / 32];
                         wok[c] = in && bcol_ok;
 #pragma unroll
@@ -235,9 +241,14 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                     // 2^(s - 127); zero for a lane outside the gate
                     const float scale = wok[c] ? __uint_as_float(sv[c] << 23) : 0.0f;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[c][j], fp4x8_to_bf16x8(wv[c][j], scale),
-                                                                      acc, 0, 0, 0);
+                    for (int j = 0; j < 4; ++j) {
+                        bf16x8 wj;
+                        if constexpr (kFmt == kGateMxfp8)  // codes 8j..8j+7: dwords 2j, 2j+1
+                            wj = fp8x8_to_bf16x8(wv[c][j / 2][(2 * j) % 4], wv[c][j / 2][(2 * j + 1) % 4], scale);
+                        else
+                            wj = fp4x8_to_bf16x8(wv[c][0][j], scale);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[c][j], wj, acc, 0, 0, 0);
+                    }
                 }
             }
         }
@@ -426,24 +437,20 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream)
     const int R = (a.M + kDecodeTile - 1) / kDecodeTile;
     const int B = (a.E + kDecodeTile - 1) / kDecodeTile;
     const int grid = R * B * a.S;
-    const bool mx = a.w_fp4 != nullptr;
     const bool narrow = a.load_waves == kDecodeNarrow.load_waves && a.S <= kDecodeNarrow.max_splits;
     const bool wide = a.load_waves == kDecodeWide.load_waves && a.S <= kDecodeWide.max_splits;
     const dim3 nb((kDecodeNarrow.load_waves + 1) * kWave), wb((kDecodeWide.load_waves + 1) * kWave);
-    if (narrow && !mx)
-        hipLaunchKernelGGL((decode_router_kernel<kDecodeNarrow.load_waves, kDecodeNarrow.max_splits, false>),
-                           dim3(grid), nb, 0, stream, a);
-    else if (narrow && mx)
-        hipLaunchKernelGGL((decode_router_kernel<kDecodeNarrow.load_waves, kDecodeNarrow.max_splits, true>),
-                           dim3(grid), nb, 0, stream, a);
-    else if (wide && !mx)
-        hipLaunchKernelGGL((decode_router_kernel<kDecodeWide.load_waves, kDecodeWide.max_splits, false>),
-                           dim3(grid), wb, 0, stream, a);
-    else if (wide && mx)
-        hipLaunchKernelGGL((decode_router_kernel<kDecodeWide.load_waves, kDecodeWide.max_splits, true>),
-                           dim3(grid), wb, 0, stream, a);
-    else
-        return hipErrorInvalidValue;
+#define GPT_DECODE_LAUNCH(GEO, FMT, BLOCK)                                                           \
+    hipLaunchKernelGGL((decode_router_kernel<GEO.load_waves, GEO.max_splits, FMT>), dim3(grid), BLOCK, 0, \
+                       stream, a)
+    if (narrow && a.w_format == kGateBf16) GPT_DECODE_LAUNCH(kDecodeNarrow, kGateBf16, nb);
+    else if (narrow && a.w_format == kGateMxfp4) GPT_DECODE_LAUNCH(kDecodeNarrow, kGateMxfp4, nb);
+    else if (narrow && a.w_format == kGateMxfp8) GPT_DECODE_LAUNCH(kDecodeNarrow, kGateMxfp8, nb);
+    else if (wide && a.w_format == kGateBf16) GPT_DECODE_LAUNCH(kDecodeWide, kGateBf16, wb);
+    else if (wide && a.w_format == kGateMxfp4) GPT_DECODE_LAUNCH(kDecodeWide, kGateMxfp4, wb);
+    else if (wide && a.w_format == kGateMxfp8) GPT_DECODE_LAUNCH(kDecodeWide, kGateMxfp8, wb);
+    else return hipErrorInvalidValue;
+#undef GPT_DECODE_LAUNCH
     return hipGetLastError();
 }
 

@@ -16,12 +16,18 @@ struct TopkLaunch {
     float* weights;
 };
 
+// Gate weight formats: bf16, or block-scaled (OCP MX: E8M0 scale per 32
+// elements) with FP4 E2M1 or FP8 E4M3 elements.
+enum GateFormat : int { kGateBf16 = 0, kGateMxfp4 = 1, kGateMxfp8 = 2 };
+
 // Decode: M <= 64 tokens.  Grid = R row blocks x B expert blocks x S H-splits.
 struct DecodeLaunch {
     const uint16_t* x;
-    const uint16_t* w;      // bf16 gate [E, H], or NULL with the MXFP4 gate below
-    const uint8_t* w_fp4;   // MXFP4 gate: E2M1 codes [E, H/2], even element in the low nibble
-    const uint8_t* w_scale; // MXFP4 gate: E8M0 scales [E, H/32]
+    const uint16_t* w;      // bf16 gate [E, H], or NULL with a block-scaled gate below
+    int w_format;           // GateFormat
+    const uint8_t* w_codes; // block-scaled gate codes: MXFP4 [E, H/2] (even element in the
+                            // low nibble) or MXFP8 [E, H] (one E4M3 code per byte)
+    const uint8_t* w_scale; // block-scaled gate: E8M0 scales [E, H/32]
     const float* bias;
     int M, H, E, k, scoring, renorm;
     int32_t* inds;
@@ -34,15 +40,16 @@ struct DecodeLaunch {
     float* partials;        // workspace [S][M][256], every slot kPartialSentinel between calls
     uint32_t* counters;     // workspace, kDecodeCounters words, zero between calls
     int S;                  // H splits
-    int ks_per_split;       // k units per split: 32-wide k-steps (bf16 gate), 128-wide blocks (MXFP4)
+    int ks_per_split;       // k units per split: 32-wide k-steps (bf16 gate), 128-wide blocks (MX)
     int load_waves;         // geometry: kDecodeNarrow.load_waves or kDecodeWide.load_waves
 };
 
 struct PrefillLaunch {
     const uint16_t* x;
-    const uint16_t* w;      // bf16 gate [E, H], or NULL with the MXFP4 gate below
-    const uint8_t* w_fp4;   // MXFP4 gate: E2M1 codes [E, H/2] (H % 128 == 0)
-    const uint8_t* w_scale; // MXFP4 gate: E8M0 scales [E, H/32], 4-byte aligned
+    const uint16_t* w;      // bf16 gate [E, H], or NULL with a block-scaled gate below
+    int w_format;           // GateFormat
+    const uint8_t* w_codes; // MXFP4 [E, H/2] or MXFP8 [E, H] codes (H % 128 == 0)
+    const uint8_t* w_scale; // E8M0 scales [E, H/32], 4-byte aligned
     const float* bias;
     int64_t M;
     int H, E, k, scoring, renorm;

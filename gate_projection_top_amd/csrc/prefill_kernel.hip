@@ -59,13 +59,14 @@ constexpr int kTileBytes = kBM * kTileStride * 4;
 constexpr int kRingBytes = kWRingOffset + kWSlots * kWStageBytes;
 constexpr int kLdsBytes = kRingBytes;
 constexpr int kFlagOffset = kLdsBytes - 16;  // one int after the ring's last use
-// MXFP4 gate: a W stage holds 256 rows of 32 code bytes (64 k) and a scale
-// stage one dword per expert (the aligned dword holding the stage's two
-// block scales); the X ring is unchanged.
-constexpr int kWStageBytesMx = kBN * kBK / 2;                     // 8 KiB
+// Block-scaled gate: a W stage holds 256 rows of 64 k codes (32 bytes of
+// MXFP4, 64 of MXFP8) and a scale stage one dword per expert (the aligned
+// dword holding the stage's two block scales); the X ring is unchanged.
+template <int kFmt> constexpr int kCodeRowBytes = kFmt == kGateMxfp8 ? kBK : kBK / 2;
+template <int kFmt> constexpr int kWStageBytesOf = kFmt == kGateBf16 ? kWStageBytes : kBN * kCodeRowBytes<kFmt>;
 constexpr int kSStageBytes = kBN * 4;                            // 1 KiB
-constexpr int kSRingOffset = kWRingOffset + kWSlots * kWStageBytesMx;
-static_assert(kSRingOffset + kWSlots * kSStageBytes <= kRingBytes, "MXFP4 rings fit the LDS ring");
+constexpr int kSRingOffset = kWRingOffset + kWSlots * kWStageBytesOf<kGateMxfp8>;
+static_assert(kSRingOffset + kWSlots * kSStageBytes <= kRingBytes, "block-scaled rings fit the LDS ring");
 static_assert(kTileBytes <= kFlagOffset, "row tile and flag overlap");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -87,18 +88,19 @@ constexpr int kOutOfRange = 0x7ffffff0;  // past every descriptor limit: loads r
 // and E (W limit).
 struct DmaPlan {
     __amdgpu_buffer_rsrc_t x;  // this tile's rows of X
-    __amdgpu_buffer_rsrc_t w;  // all of W (bf16), or all the MXFP4 codes
-    __amdgpu_buffer_rsrc_t sc; // MXFP4 scales
+    __amdgpu_buffer_rsrc_t w;  // all of W (bf16), or all the block-scaled codes
+    __amdgpu_buffer_rsrc_t sc; // block scales
     int a_off[kDmaA], a_k[kDmaA];
     int b_off[kDmaB], b_k[kDmaB];
-    int m_off, m_k;            // MXFP4 codes: this lane's 16 bytes (one 32-block) of a stage
-    int s_off;                 // MXFP4 scales: this lane's expert row (lanes < 32)
+    int m_off[2], m_k[2];      // codes: this lane's 16 bytes of a stage, per code load
+    int s_off;                 // scales: this lane's expert row (lanes < 32)
 };
 
-// MXFP4 code rows are 32 bytes (two 16-byte halves, one 32-block each); half
-// h of row R sits in physical half h ^ sw2(R), so the 16 rows of a fragment
-// read at one k spread over all banks.
-__device__ __forceinline__ int half_swizzle(int R) { return (R >> 3) & 1; }
+// Code rows hold 16-byte chunks: MXFP4 two (one 32-block each), MXFP8 four
+// (16 k each).  Chunk c of row R sits in physical chunk c ^ sw(R), so the 16
+// rows of a fragment read at one k spread over all banks.
+__device__ __forceinline__ int half_swizzle(int R) { return (R >> 3) & 1; }     // MXFP4, 32-byte rows
+__device__ __forceinline__ int quarter_swizzle(int R) { return (R >> 2) & 3; }  // MXFP8, 64-byte rows
 
 // One 1 KiB direct-to-LDS load (lane i's 16 bytes to lds + 16 i).  Written as
 // inline asm so that the compiler does not track it: its waitcnt pass would
@@ -136,14 +138,20 @@ __device__ __forceinline__ void issue_w(const DmaPlan& d, unsigned char* slot, i
     }
 }
 
-// MXFP4 stage: every wave loads 1 KiB of codes (32 rows) and, with its
-// first 32 lanes, the scale dwords of 32 experts.  Per wave and stage: two
-// loads, whatever the lane mask.
+// Block-scaled stage: every wave loads the codes of 32 rows (1 KiB of
+// MXFP4, 2 KiB of MXFP8) and, with its first 32 lanes, the scale dwords of
+// 32 experts.  Per wave and stage: kLoads + 1 loads, whatever the lane mask.
+template <int kFmt>
 __device__ __forceinline__ void issue_w_mx(const DmaPlan& d, unsigned char* wslot, unsigned char* sslot, int k0,
                                            int H, int wave, int lane)
 {
-    const int off = (k0 + d.m_k < H) ? d.m_off + k0 / 2 : kOutOfRange;
-    dma16(d.w, off, wslot + wave * 1024);
+    constexpr int kLoads = kCodeRowBytes<kFmt> / 32;  // 1 KiB code loads per wave
+    constexpr int kRowDiv = kFmt == kGateMxfp8 ? 1 : 2;
+#pragma unroll
+    for (int b = 0; b < kLoads; ++b) {
+        const int off = (k0 + d.m_k[b] < H) ? d.m_off[b] + k0 / kRowDiv : kOutOfRange;
+        dma16(d.w, off, wslot + (wave * kLoads + b) * 1024);
+    }
     // the stage's two scales (k0 / 32 is even) lie in the aligned dword at k0 / 32 & ~3
     if (lane < 32) dma4(d.sc, d.s_off + ((k0 >> 5) & ~3), sslot + wave * 128);
 }
@@ -396,7 +404,7 @@ __device__ __forceinline__ void exchange_and_route(const PrefillLaunch& p, float
     }
 }
 
-template <bool kMx>
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch p)
 {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
@@ -442,13 +450,23 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
         const int64_t rows_here = min((int64_t)kBM, p.M - row0);
         d.x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + row0 * p.H), 0,
                                                 (int)(rows_here * p.H * 2), 0x00020000);
-        if constexpr (kMx) {
-            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_fp4), 0, p.E * (p.H / 2), 0x00020000);
+        if constexpr (kFmt == kGateMxfp4) {
+            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_codes), 0, p.E * (p.H / 2), 0x00020000);
+            const int R = wave * 32 + (lane >> 1);
+            d.m_k[0] = ((lane & 1) ^ half_swizzle(R)) * 32;
+            d.m_off[0] = R * (p.H / 2) + d.m_k[0] / 2;
+        } else if constexpr (kFmt == kGateMxfp8) {
+            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_codes), 0, p.E * p.H, 0x00020000);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int R = wave * 32 + b * 16 + (lane >> 2);
+                d.m_k[b] = ((lane & 3) ^ quarter_swizzle(R)) * 16;
+                d.m_off[b] = R * p.H + d.m_k[b];
+            }
+        }
+        if constexpr (kFmt != kGateBf16) {
             d.sc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_scale), 0, p.E * (p.H / 32),
                                                      0x00020000);
-            const int R = wave * 32 + (lane >> 1);
-            d.m_k = ((lane & 1) ^ half_swizzle(R)) * 32;
-            d.m_off = R * (p.H / 2) + d.m_k / 2;
             d.s_off = (wave * 32 + (lane & 31)) * (p.H / 32);
         } else {
             d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), 0, p.E * p.H * 2, 0x00020000);
@@ -482,14 +500,16 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
     unsigned char* const xring = lds;
     unsigned char* const wring = lds + kWRingOffset;
     unsigned char* const sring = lds + kSRingOffset;
-    constexpr int kWLoads = kMx ? 2 : kDmaB;          // W loads per wave and stage
+    constexpr bool kMx = kFmt != kGateBf16;
+    constexpr int kWStage = kWStageBytesOf<kFmt>;
+    constexpr int kWLoads = kMx ? kCodeRowBytes<kFmt> / 32 + 1 : kDmaB;  // W loads per wave and stage
     constexpr int kIterLoads = kDmaA + kWLoads;       // loads per wave and iteration
     auto issue_iteration = [&](int j) {
         if (j + 3 >= 0 && j + 3 < nstages)
             issue_x(d, xring + ((j + 3) % kXSlots) * kXStageBytes, k_begin + (j + 3) * kBK, p.H, wave);
         if (j + 2 >= 0 && j + 2 < nstages) {
             if constexpr (kMx)
-                issue_w_mx(d, wring + ((j + 2) % kWSlots) * kWStageBytesMx,
+                issue_w_mx<kFmt>(d, wring + ((j + 2) % kWSlots) * kWStage,
                            sring + ((j + 2) % kWSlots) * kSStageBytes, k_begin + (j + 2) * kBK, p.H, wave, lane);
             else
                 issue_w(d, wring + ((j + 2) % kWSlots) * kWStageBytes, k_begin + (j + 2) * kBK, p.H, wave);
@@ -508,8 +528,8 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
         ring_barrier();
         issue_iteration(ks);
         const unsigned char* xs = xring + (ks % kXSlots) * kXStageBytes;
-        const unsigned char* ws = wring + (ks % kWSlots) * (kMx ? kWStageBytesMx : kWStageBytes);
-        // MXFP4: the scale pair of expert R is bytes sb0, sb0 + 1 of its dword
+        const unsigned char* ws = wring + (ks % kWSlots) * kWStage;
+        // block-scaled: the scale pair of expert R is bytes sb0, sb0 + 1 of its dword
         const unsigned char* ss = sring + (ks % kWSlots) * kSStageBytes + (((k_begin + ks * kBK) >> 5) & 3);
         uint32_t spair[4];
         if constexpr (kMx) {
@@ -526,12 +546,20 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
                                                           ((c ^ slot_swizzle(a_row[i])) << 4));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if constexpr (kMx) {
+                if constexpr (kFmt == kGateMxfp4) {
                     // codes k = 32 kk + 8 g .. +7 of expert b_row[j]: dword g of half kk
                     const uint32_t codes = *reinterpret_cast<const uint32_t*>(
                         ws + b_row[j] * (kBK / 2) + ((kk ^ half_swizzle(b_row[j])) << 4) + 4 * g);
                     const uint32_t sbyte = (spair[j] >> (8 * kk)) & 0xffu;
                     bfr[j] = fp4x8_to_bf16x8(codes, __uint_as_float(sbyte << 23));
+                } else if constexpr (kFmt == kGateMxfp8) {
+                    // codes k = 32 kk + 8 g .. +7 of expert b_row[j]: half g & 1 of
+                    // 16-byte chunk 2 kk + g / 2
+                    const u32x2 codes = *reinterpret_cast<const u32x2*>(
+                        ws + b_row[j] * kBK + (((2 * kk + (g >> 1)) ^ quarter_swizzle(b_row[j])) << 4) +
+                        8 * (g & 1));
+                    const uint32_t sbyte = (spair[j] >> (8 * kk)) & 0xffu;
+                    bfr[j] = fp8x8_to_bf16x8(codes[0], codes[1], __uint_as_float(sbyte << 23));
                 } else {
                     bfr[j] = *reinterpret_cast<const bf16x8*>(ws + b_row[j] * kRowBytes +
                                                                ((c ^ slot_swizzle(b_row[j])) << 4));
@@ -594,10 +622,14 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream)
     const int64_t tiles = (a.M + kBM - 1) / kBM;
     const int64_t padded = (tiles + kXcds - 1) / kXcds * kXcds;
     const int64_t blocks = padded * a.S;
-    if (a.w_fp4)
-        hipLaunchKernelGGL(prefill_router_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    if (a.w_format == kGateMxfp4)
+        hipLaunchKernelGGL(prefill_router_kernel<kGateMxfp4>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else if (a.w_format == kGateMxfp8)
+        hipLaunchKernelGGL(prefill_router_kernel<kGateMxfp8>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else if (a.w_format == kGateBf16)
+        hipLaunchKernelGGL(prefill_router_kernel<kGateBf16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(prefill_router_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -647,4 +647,18 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t codes, float scale)
     return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Eight FP8 E4M3 codes (two dwords, element 0 in the low byte of lo) times a
+// power-of-two scale, as eight bf16 values: gfx950's scaled fp8 -> bf16
+// conversion, two elements (one 16-bit word) per instruction.  Exact for
+// the contract's scales (E4M3 has four significant bits).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi, float scale)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 }  // namespace gpt

@@ -100,7 +100,7 @@ int check_projection(const void* x, const void* w)
 }
 
 // Decode split choice: about the geometry's target workgroup count, with at
-// least one k unit (a 32-wide k-step, or a 128-wide MXFP4 block) per load
+// least one k unit (a 32-wide k-step, or a 128-wide block-scaled block) per load
 // wave in every split.
 void decode_splits(int M, int KS, int E, int* S_out, int* ks_per_split_out, int* load_waves_out)
 {
@@ -118,8 +118,8 @@ void decode_splits(int M, int KS, int E, int* S_out, int* ks_per_split_out, int*
     *load_waves_out = g.load_waves;
 }
 
-// w_fp4/w_scale non-NULL: the MXFP4 gate (w is unused).
-int run_fused(const void* x, const void* w, const uint8_t* w_fp4, const uint8_t* w_scale,
+// format kGateBf16 reads w; the block-scaled formats read w_codes and w_scale.
+int run_fused(const void* x, const void* w, int format, const uint8_t* w_codes, const uint8_t* w_scale,
               const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
               int32_t* inds, float* weights, float* logits, int32_t* t_ids, int32_t* t_mask,
               int32_t* t_s2u, int32_t* t_count, hipStream_t stream)
@@ -132,7 +132,8 @@ int run_fused(const void* x, const void* w, const uint8_t* w_fp4, const uint8_t*
         gpt::DecodeLaunch a{};
         a.x = static_cast<const uint16_t*>(x);
         a.w = static_cast<const uint16_t*>(w);
-        a.w_fp4 = w_fp4;
+        a.w_format = format;
+        a.w_codes = w_codes;
         a.w_scale = w_scale;
         a.bias = bias;
         a.M = (int)M;
@@ -150,14 +151,15 @@ int run_fused(const void* x, const void* w, const uint8_t* w_fp4, const uint8_t*
         a.table_count = t_count;
         a.partials = ws.partials;
         a.counters = ws.counters;
-        const int units = w_fp4 ? (H + 127) / 128 : (H + 31) / 32;
+        const int units = format != gpt::kGateBf16 ? (H + 127) / 128 : (H + 31) / 32;
         decode_splits((int)M, units, E, &a.S, &a.ks_per_split, &a.load_waves);
         e = gpt::launch_decode(a, stream);
     } else {
         gpt::PrefillLaunch a{};
         a.x = static_cast<const uint16_t*>(x);
         a.w = static_cast<const uint16_t*>(w);
-        a.w_fp4 = w_fp4;
+        a.w_format = format;
+        a.w_codes = w_codes;
         a.w_scale = w_scale;
         a.bias = bias;
         a.M = M;
@@ -206,7 +208,7 @@ int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H
     if (M > 0x7fffffffLL / 256) return ROUTER_ERR_UNSUPPORTED;
     // 32-bit byte offsets inside one 128-row tile of X and inside W
     if ((int64_t)H * 2 * 256 > 0x7fff0000LL) return ROUTER_ERR_UNSUPPORTED;
-    return run_fused(x, w, nullptr, nullptr, bias, M, H, E, k, scoring, renorm, out_inds,
+    return run_fused(x, w, gpt::kGateBf16, nullptr, nullptr, bias, M, H, E, k, scoring, renorm, out_inds,
                      out_weights, opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
@@ -230,7 +232,7 @@ int router_fwd_route_table(const void* x, const void* w, const float* bias, int 
     if (!out_inds || !out_weights || !out_unique_ids || !out_token_mask || !out_slot_to_unique ||
         !out_unique_count)
         return ROUTER_ERR_INVALID_ARGUMENT;
-    return run_fused(x, w, nullptr, nullptr, bias, M, H, E, k, scoring, renorm, out_inds,
+    return run_fused(x, w, gpt::kGateBf16, nullptr, nullptr, bias, M, H, E, k, scoring, renorm, out_inds,
                      out_weights, opt_out_logits, out_unique_ids, out_token_mask,
                      out_slot_to_unique, out_unique_count, stream);
 }
@@ -246,10 +248,11 @@ int router_fwd_m2_table(const void* x, const void* w, const float* bias, int H, 
                                   out_slot_to_unique, out_unique_count, stream);
 }
 
-int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale,
-                     const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
-                     int32_t* out_inds, float* out_weights, float* opt_out_logits,
-                     hipStream_t stream)
+// Shared checks and launch of the block-scaled gate formats.
+static int run_block_scaled(int format, const void* x, const uint8_t* w_codes, const uint8_t* w_scale,
+                            const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
+                            int32_t* out_inds, float* out_weights, float* opt_out_logits,
+                            hipStream_t stream)
 {
     int rc = check_common(M, E, k, scoring, renorm);
     if (rc == ROUTER_OK) rc = check_hidden(H);
@@ -258,15 +261,33 @@ int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale
     // the prefill kernel moves a 64-wide stage's two scales as one aligned dword
     if (M > ROUTER_DECODE_MAX_M && H % 128 != 0) return ROUTER_ERR_UNSUPPORTED;
     if (M == 0) return ROUTER_OK;
-    rc = check_projection(x, w_fp4);
+    rc = check_projection(x, w_codes);
     if (rc != ROUTER_OK) return rc;
     if (!w_scale || !out_inds || !out_weights) return ROUTER_ERR_INVALID_ARGUMENT;
     if (M > ROUTER_DECODE_MAX_M && ((uintptr_t)w_scale & 3u) != 0) return ROUTER_ERR_MISALIGNED;
     if (M > 0x7fffffffLL / 256) return ROUTER_ERR_UNSUPPORTED;
-    // 32-bit byte offsets inside one 128-row tile of X
+    // 32-bit byte offsets inside one 128-row tile of X and inside the codes
     if ((int64_t)H * 2 * 256 > 0x7fff0000LL) return ROUTER_ERR_UNSUPPORTED;
-    return run_fused(x, nullptr, w_fp4, w_scale, bias, M, H, E, k, scoring, renorm, out_inds,
+    return run_fused(x, nullptr, format, w_codes, w_scale, bias, M, H, E, k, scoring, renorm, out_inds,
                      out_weights, opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale,
+                     const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
+                     int32_t* out_inds, float* out_weights, float* opt_out_logits,
+                     hipStream_t stream)
+{
+    return run_block_scaled(gpt::kGateMxfp4, x, w_fp4, w_scale, bias, M, H, E, k, scoring, renorm,
+                            out_inds, out_weights, opt_out_logits, stream);
+}
+
+int router_fwd_mxfp8(const void* x, const uint8_t* w_fp8, const uint8_t* w_scale,
+                     const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
+                     int32_t* out_inds, float* out_weights, float* opt_out_logits,
+                     hipStream_t stream)
+{
+    return run_block_scaled(gpt::kGateMxfp8, x, w_fp8, w_scale, bias, M, H, E, k, scoring, renorm,
+                            out_inds, out_weights, opt_out_logits, stream);
 }
 
 int router_gather_shared_add(const void* y, int64_t y_rows, const int32_t* slot_rows,

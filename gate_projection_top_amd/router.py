@@ -33,7 +33,7 @@ TABLE_MAX_SLOTS = 64
 DECODE_MAX_M = 64
 
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
-           "router_fwd_mxfp4", "router_topk_from_logits", "router_gather_shared_add",
+           "router_fwd_mxfp4", "router_fwd_mxfp8", "router_topk_from_logits", "router_gather_shared_add",
            "router_gather_shared_add_table", "router_expert_gemm1_table",
            "router_set_exchange_timeout_us", "router_strerror")
 
@@ -68,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_fwd_route_table.restype = i32
     lib.router_fwd_mxfp4.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
     lib.router_fwd_mxfp4.restype = i32
+    lib.router_fwd_mxfp8.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.router_fwd_mxfp8.restype = i32
     lib.router_gather_shared_add.argtypes = [P, i64, P, P, P, i64, i32, i32, P, P]
     lib.router_gather_shared_add.restype = i32
     lib.router_gather_shared_add_table.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P]
@@ -200,6 +202,36 @@ def router_fwd_mxfp4(x: torch.Tensor, w_fp4: torch.Tensor, w_scale: torch.Tensor
                                      int(k), int(scoring), int(bool(renorm)), _ptr(inds), _ptr(wts),
                                      _ptr(logits), _stream(x.device))
     _check(rc, "router_fwd_mxfp4")
+    return (inds, wts, logits) if logits is not None else (inds, wts)
+
+
+def router_fwd_mxfp8(x: torch.Tensor, w_fp8: torch.Tensor, w_scale: torch.Tensor,
+                     bias: Optional[torch.Tensor], k: int, scoring: int = SOFTMAX,
+                     renorm: bool = True, *, return_logits: bool = False,
+                     out_inds=None, out_weights=None, logits_out=None):
+    """Fused router on an MXFP8 gate.  x: bf16 [M,H]; w_fp8: uint8 [E,H]
+    (E4M3 codes, none NaN); w_scale: uint8 [E,H/32] (E8M0 scales, each in
+    [10, 246]); bias: fp32 [E] or None.  H % 32 == 0, and H % 128 == 0 when
+    M > DECODE_MAX_M.
+
+    Returns what router_fwd returns.
+    """
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    _check_tensor(w_fp8, "w_fp8", torch.uint8, 2)
+    _check_tensor(w_scale, "w_scale", torch.uint8, 2)
+    M, H = x.shape
+    E = w_fp8.shape[0]
+    if H % 32 != 0:
+        raise ValueError("the MXFP8 gate needs H % 32 == 0")
+    if tuple(w_fp8.shape) != (E, H) or tuple(w_scale.shape) != (E, H // 32):
+        raise ValueError("w_fp8 must be [E, H] and w_scale [E, H/32]")
+    _check_bias(bias, E)
+    inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
+    with torch.cuda.device(x.device):
+        rc = load().router_fwd_mxfp8(_ptr(x), _ptr(w_fp8), _ptr(w_scale), _ptr(bias), M, H, E,
+                                     int(k), int(scoring), int(bool(renorm)), _ptr(inds), _ptr(wts),
+                                     _ptr(logits), _stream(x.device))
+    _check(rc, "router_fwd_mxfp8")
     return (inds, wts, logits) if logits is not None else (inds, wts)
 
 

@@ -258,7 +258,7 @@ def quantise_mxfp4(w: np.ndarray):
 @dataclasses.dataclass
 class MxCase:
     x: np.ndarray        # bf16 bits [M, H]
-    elems: np.ndarray    # uint8 [E, H/2]
+    elems: np.ndarray    # uint8 [E, H/2] (MXFP4) or [E, H] (MXFP8)
     scales: np.ndarray   # uint8 [E, H/32]
     bias: Optional[np.ndarray]
     k: int

@@ -177,6 +177,28 @@ int router_fwd_mxfp4(const void* x, const uint8_t* w_fp4, const uint8_t* w_scale
                      int32_t* out_inds, float* out_weights, float* opt_out_logits,
                      hipStream_t stream);
 
+/* router_fwd with a block-scaled FP8 gate: the same low-precision gate
+ * projection (dense_router_decode commit notes, block-scaled gate GEMM with
+ * the router epilogue) in the OCP MXFP8 encoding, 8-bit elements with the
+ * same E8M0 block scale per 32 elements:
+ *   w_fp8    uint8 [E, H]: FP8 E4M3 codes (bias 7, no infinities, NaN only
+ *            at S.1111.111, largest magnitude 448), one per byte
+ *            (16-byte aligned);
+ *   w_scale  uint8 [E, H/32]: E8M0 scales; element i of row e is
+ *            e4m3(code) * 2^(w_scale[e, i/32] - 127) (4-byte aligned when
+ *            M > ROUTER_DECODE_MAX_M, else ROUTER_ERR_MISALIGNED).
+ * Scales must lie in [10, 246] and codes must not be NaN, so that every
+ * dequantised weight is zero or a normal bf16 value; other inputs give
+ * unspecified (but finite-time and in-bounds) results.  The logits are sums
+ * of exact bf16 products accumulated in fp32, in this kernel's own order,
+ * and everything after them is router_fwd's device routine.
+ * Limits as router_fwd_mxfp4: H % 32 == 0, and H % 128 == 0 when
+ * M > ROUTER_DECODE_MAX_M, else ROUTER_ERR_UNSUPPORTED. */
+int router_fwd_mxfp8(const void* x, const uint8_t* w_fp8, const uint8_t* w_scale,
+                     const float* bias, int64_t M, int H, int E, int k, int scoring, int renorm,
+                     int32_t* out_inds, float* out_weights, float* opt_out_logits,
+                     hipStream_t stream);
+
 /* The step after the router: routed gather fused with the shared-expert
  * add (b70 lab MTP1 M=2 note, "Outcome"), with the note's rounding chain
  * ("Exact arithmetic": FP32 routed accumulation -> BF16 -> add shared BF16

@@ -157,18 +157,20 @@ def test_topk_rejects(lib, kw, code):
     (dict(x=FAKE_ODD), R.ERR_MISALIGNED),
     (dict(w=FAKE_ODD), R.ERR_MISALIGNED),
 ])
-def test_mxfp4_rejects(lib, kw, code):
+@pytest.mark.parametrize("entry", ["router_fwd_mxfp4", "router_fwd_mxfp8"])
+def test_block_scaled_rejects(lib, entry, kw, code):
     a = dict(x=FAKE, w=FAKE, scale=FAKE_ODD, M=4, H=4096, E=256, k=8, scoring=0, renorm=1,
              inds=FAKE, weights=FAKE)
     a.update(kw)
-    rc = lib.router_fwd_mxfp4(a["x"], a["w"], a["scale"], None, a["M"], a["H"], a["E"], a["k"],
-                              a["scoring"], a["renorm"], a["inds"], a["weights"], None, None)
-    assert rc == code, (kw, rc)
+    rc = getattr(lib, entry)(a["x"], a["w"], a["scale"], None, a["M"], a["H"], a["E"], a["k"],
+                             a["scoring"], a["renorm"], a["inds"], a["weights"], None, None)
+    assert rc == code, (entry, kw, rc)
 
 
-def test_mxfp4_empty_batch_is_ok_without_pointers(lib):
-    assert lib.router_fwd_mxfp4(None, None, None, None, 0, 4096, 256, 8, 0, 1, None, None, None,
-                                None) == R.OK
+@pytest.mark.parametrize("entry", ["router_fwd_mxfp4", "router_fwd_mxfp8"])
+def test_block_scaled_empty_batch_is_ok_without_pointers(lib, entry):
+    assert getattr(lib, entry)(None, None, None, None, 0, 4096, 256, 8, 0, 1, None, None, None,
+                               None) == R.OK
 
 
 @pytest.mark.parametrize("kw,code", [
