@@ -111,7 +111,15 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     const int wave = tid / kWave;
     const int B = (a.E + kDecodeTile - 1) / kDecodeTile;
 
+    // Block-scaled gates: the hardware deals consecutive workgroup ids to the
+    // 8 XCDs in turn; renumber so that each XCD holds a contiguous range of
+    // logical ids (whole expert blocks with all their splits), whose shared
+    // scale lines its L2 then fetches once (measured: 14 % less fabric
+    // traffic and a slightly shorter launch at M=1; the bf16 gate shares no
+    // lines between splits but the token row, and measured slower this way).
     int bid = blockIdx.x;
+    if constexpr (kFmt != kGateBf16)
+        if (gridDim.x % 8u == 0u) bid = (bid % 8) * (int)(gridDim.x / 8u) + bid / 8;
     const int s = bid % a.S;
     bid /= a.S;
     const int b = bid % B;
