@@ -82,6 +82,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // the swizzle c ^ ((R ^ R/8) mod 8) took 1.7x as long.
 __device__ __forceinline__ int slot_swizzle(int R) { return R & 7; }
 
+// The block-scaled gates read X with the k order of their B fragments (lane
+// group g takes k = 16 g + 8 kk + 0..7 in MFMA step kk, so that its codes for
+// both steps are contiguous): A chunk 2 g + kk instead of 4 kk + g.  For that
+// pattern c ^ ((R ^ R/8) mod 8) is the conflict-free slot (measured, as above).
+template <int kFmt>
+__device__ __forceinline__ int x_swizzle(int R) { return kFmt == kGateBf16 ? slot_swizzle(R) : (R ^ (R >> 3)) & 7; }
+
 constexpr int kOutOfRange = 0x7ffffff0;  // past every descriptor limit: loads read zeros
 
 // Lane i of a 1 KiB block b fills row R = 8b + i/8, slot i%8, so it fetches
@@ -99,10 +106,17 @@ struct DmaPlan {
 };
 
 // Code rows hold 16-byte chunks: MXFP4 two (one 32-block each), MXFP8 four
-// (16 k each).  Chunk c of row R sits in physical chunk c ^ sw(R), so the 16
-// rows of a fragment read at one k spread over all banks.
+// (16 k each).  Chunk c of row R sits in physical chunk c ^ sw(R); the swizzles
+// are the ones measured fastest for the fragment reads below (one ds_read_b64
+// of 16 MXFP4 codes, one ds_read_b128 of 16 MXFP8 codes, per expert row and
+// stage): 7.1 and 3.9 clocks per read per CU.
 __device__ __forceinline__ int half_swizzle(int R) { return (R >> 3) & 1; }     // MXFP4, 32-byte rows
-__device__ __forceinline__ int quarter_swizzle(int R) { return (R >> 2) & 3; }  // MXFP8, 64-byte rows
+__device__ __forceinline__ int quarter_swizzle(int R) { return (R >> 1) & 3; }  // MXFP8, 64-byte rows
+
+// A lane's block-scaled codes for one stage: MXFP4 16 codes in two dwords,
+// MXFP8 16 codes in four (unused for bf16).
+template <int kFmt> struct BStage { using type = u32x4; };
+template <> struct BStage<kGateMxfp4> { using type = u32x2; };
 
 // One 1 KiB direct-to-LDS load (lane i's 16 bytes to lds + 16 i).  Written as
 // inline asm so that the compiler does not track it: its waitcnt pass would
@@ -477,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
 #pragma unroll
         for (int j = 0; j < kDmaA; ++j) {
             const int R = (wave * kDmaA + j) * 8 + li;
-            d.a_k[j] = (ls ^ slot_swizzle(R)) * 8;
+            d.a_k[j] = (ls ^ x_swizzle<kFmt>(R)) * 8;
             d.a_off[j] = (R * p.H + d.a_k[j]) * 2;
         }
 #pragma unroll
@@ -531,41 +545,41 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
         issue_iteration(ks);
         const unsigned char* xs = xring + (ks % kXSlots) * kXStageBytes;
         const unsigned char* ws = wring + (ks % kWSlots) * kWStage;
-        // block-scaled: the scale pair of expert R is bytes sb0, sb0 + 1 of its dword
+        // block-scaled: the stage's two block scales of expert R are bytes sb0,
+        // sb0 + 1 of its dword; lane group g's k (16 g + 0..15) lie in block g / 2
         const unsigned char* ss = sring + (ks % kWSlots) * kSStageBytes + (((k_begin + ks * kBK) >> 5) & 3);
-        uint32_t spair[4];
+        // block-scaled: each lane's 16 codes of the stage (both MFMA steps) at once
+        typename BStage<kFmt>::type braw[4];
+        float bscale[4];
         if constexpr (kMx) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) spair[j] = *reinterpret_cast<const uint16_t*>(ss + b_row[j] * 4);
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (kFmt == kGateMxfp4)  // bytes 8 g .. 8 g + 7: half g / 2, offset 8 (g mod 2)
+                    braw[j] = *reinterpret_cast<const u32x2*>(ws + b_row[j] * (kBK / 2) +
+                                                              (((g >> 1) ^ half_swizzle(b_row[j])) << 4) + 8 * (g & 1));
+                else  // bytes 16 g .. 16 g + 15: chunk g
+                    braw[j] = *reinterpret_cast<const u32x4*>(ws + b_row[j] * kBK + ((g ^ quarter_swizzle(b_row[j])) << 4));
+                bscale[j] = __uint_as_float((uint32_t)ss[b_row[j] * 4 + (g >> 1)] << 23);
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < kBK / 32; ++kk) {
-            const int c = kk * 4 + g;
+            // k of lane group g in step kk: bf16 32 kk + 8 g + 0..7, block-scaled 16 g + 8 kk + 0..7
+            const int c = kMx ? 2 * g + kk : kk * 4 + g;
             bf16x8 af[4], bfr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 af[i] = *reinterpret_cast<const bf16x8*>(xs + a_row[i] * kRowBytes +
-                                                          ((c ^ slot_swizzle(a_row[i])) << 4));
+                                                          ((c ^ x_swizzle<kFmt>(a_row[i])) << 4));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if constexpr (kFmt == kGateMxfp4) {
-                    // codes k = 32 kk + 8 g .. +7 of expert b_row[j]: dword g of half kk
-                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(
-                        ws + b_row[j] * (kBK / 2) + ((kk ^ half_swizzle(b_row[j])) << 4) + 4 * g);
-                    const uint32_t sbyte = (spair[j] >> (8 * kk)) & 0xffu;
-                    bfr[j] = fp4x8_to_bf16x8(codes, __uint_as_float(sbyte << 23));
-                } else if constexpr (kFmt == kGateMxfp8) {
-                    // codes k = 32 kk + 8 g .. +7 of expert b_row[j]: half g & 1 of
-                    // 16-byte chunk 2 kk + g / 2
-                    const u32x2 codes = *reinterpret_cast<const u32x2*>(
-                        ws + b_row[j] * kBK + (((2 * kk + (g >> 1)) ^ quarter_swizzle(b_row[j])) << 4) +
-                        8 * (g & 1));
-                    const uint32_t sbyte = (spair[j] >> (8 * kk)) & 0xffu;
-                    bfr[j] = fp8x8_to_bf16x8(codes[0], codes[1], __uint_as_float(sbyte << 23));
-                } else {
+                if constexpr (kFmt == kGateMxfp4)
+                    bfr[j] = fp4x8_to_bf16x8(braw[j][kk], bscale[j]);
+                else if constexpr (kFmt == kGateMxfp8)
+                    bfr[j] = fp8x8_to_bf16x8(braw[j][2 * kk], braw[j][2 * kk + 1], bscale[j]);
+                else
                     bfr[j] = *reinterpret_cast<const bf16x8*>(ws + b_row[j] * kRowBytes +
                                                                ((c ^ slot_swizzle(b_row[j])) << 4));
-                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
