@@ -19,7 +19,8 @@
  *     a per-expert bias, unbiased winners' scores renormalised; the BF16 GEMM
  *     with FP32 accumulation and the row-level top-k epilogue;
  *   - dense_router_decode commit notes, the fused NVFP4 router: the gate
- *     projection on block-scaled FP4 weights (here OCP MXFP4);
+ *     projection on block-scaled low-precision weights (here OCP MXFP4, and
+ *     MXFP8 with FP8 E4M3 elements);
  *   - b70 lab MTP1 M=2 note, "Outcome" and "Exact arithmetic": the routed
  *     gather fused with the shared-expert BF16 add that follows the router;
  *   - b70 lab MTP1 M=2 note, "Why literal source-direct GEMM1 is not
@@ -41,8 +42,9 @@
  *   inds[t,:]   = the first k experts in (key descending, index ascending)
  *                 order, in that order;
  *   weights     = renorm: u_j / sum_{winners} u, with u = exp(l - max l)
- *                 (softmax) or s (sqrt-softplus), sum in rank order, in double,
- *                 rounded once to fp32;
+ *                 (softmax) or s (sqrt-softplus), in double (the sum over
+ *                 the winners in a fixed pairwise order), rounded once to
+ *                 fp32;
  *                 no renorm: the full-row probability p_j (softmax) or s_j;
  *                 the bias never enters a weight.
  *
