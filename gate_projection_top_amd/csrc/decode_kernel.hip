@@ -56,8 +56,9 @@ __device__ __forceinline__ float not_sentinel(float v)
 __device__ __forceinline__ bool published(f32x4 v)
 {
     // bitwise, not short-circuit: one compare per value, no branches
-    return (__float_as_uint(v[0]) != kPartialSentinel) & (__float_as_uint(v[1]) != kPartialSentinel) &
-           (__float_as_uint(v[2]) != kPartialSentinel) & (__float_as_uint(v[3]) != kPartialSentinel);
+    const int p0 = __float_as_uint(v[0]) != kPartialSentinel, p1 = __float_as_uint(v[1]) != kPartialSentinel;
+    const int p2 = __float_as_uint(v[2]) != kPartialSentinel, p3 = __float_as_uint(v[3]) != kPartialSentinel;
+    return (p0 & p1 & p2 & p3) != 0;
 }
 
 // One poll: every split's slot of this lane's four experts.  Splits q >= S
