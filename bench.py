@@ -16,7 +16,9 @@ Also reported (same JSON line):
                 timed replays, divided by the launch count), vs 8 TB/s; traffic
                 from the committed rocprofv3 counter summary when the kernel
                 sources still match it, else null;
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload, one
+                thread (extras.cpu_baseline_all_threads: the same calls on up to
+                16 threads at once, as throughput);
   extras        cache-hot cycle, verify widths M=2/8 at H=4096, the biased M=2
                 table on/off delta, the MXFP4 and MXFP8 gates at M=1 and M=8
                 (H=7168, 585 / 606 MB pools) and at the 8192-token prefill, the
@@ -216,6 +218,7 @@ def main():
         out["extras"].update(prefill_extras(torch, R, W, dev, args))
     if args.section == "all" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+        out["extras"]["cpu_baseline_all_threads"] = cpu_baseline_threads(W, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
@@ -551,6 +554,42 @@ def cpu_baseline(W, seconds):
     return {"value": round(el * 1e6 / n, 1), "unit": "µs/call", "cores": 1, "kind": "oracle",
             "sample": f"{n} single-token router calls (H=7168, E=256, k=8, softmax, renorm) "
                       f"through the C oracle, one thread"}
+
+
+def cpu_baseline_threads(W, seconds):
+    """The same oracle calls on every host core this process may use (at most
+    16 threads): independent calls in parallel threads (the C oracle runs
+    without the interpreter lock), reported as µs per call of throughput."""
+    import threading
+    import oracle
+
+    orc = oracle.get()
+    case = W.metric_case(0)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, avail))
+    counts = [0] * threads
+    t0 = time.perf_counter()
+    deadline = t0 + seconds
+
+    def work(i):
+        while time.perf_counter() < deadline:
+            orc.router(case.x, case.w, case.bias, case.k, case.scoring, case.renorm)
+            counts[i] += 1
+
+    pool = [threading.Thread(target=work, args=(i,)) for i in range(threads)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
+    el = time.perf_counter() - t0
+    n = sum(counts)
+    log(f"cpu baseline ({threads} threads): {n} oracle calls in {el:.1f}s")
+    return {"value": round(el * 1e6 / max(n, 1), 2), "unit": "µs/call", "cores": threads, "kind": "oracle",
+            "sample": f"{n} single-token router calls (H=7168, E=256, k=8, softmax, renorm), "
+                      f"independent calls on {threads} threads"}
 
 
 if __name__ == "__main__":
