@@ -9,14 +9,16 @@
 // would re-read the whole gate matrix from L2 for every 32 tokens; 128-row
 // tiles cut that traffic 4x.  To still occupy every CU, the K (= H) range of
 // a tile is split S ways (S = 4 for <= 64 tiles): S workgroups of 8 waves
-// each compute the tile's 128 x 256 partial over their K slice.  Each wave
-// owns a 64 x 64 block as 4 x 4 MFMA 16x16x32 accumulators.  K is staged
-// through LDS rings in 64-wide steps by direct-to-LDS buffer loads (no
-// staging registers; 8 consecutive lanes read one row's 128 contiguous
-// bytes): X, streamed from HBM, three steps ahead; W, which every tile
-// re-reads and L2 mostly holds, two steps ahead.  The MFMA operands are read
-// back from LDS through an XOR slot swizzle that keeps fragment reads free of
-// bank conflicts.
+// each compute the tile's 128 x 256 partial over their K slice.  The waves
+// split the work by role: four producers issue every load of the LDS rings,
+// so that only they ever queue on the memory pipeline, and four compute
+// waves, each owning a 64 x 128 block as 4 x 8 MFMA 16x16x32 accumulators,
+// only read fragments and multiply.  K is staged through the rings in
+// 64-wide steps by direct-to-LDS buffer loads (no staging registers; 8
+// consecutive lanes read one row's 128 contiguous bytes): X, streamed from
+// HBM, three steps ahead; W, which every tile re-reads and L2 mostly holds,
+// two steps ahead.  The MFMA operands are read back from LDS through XOR
+// slot swizzles, measured free of bank conflicts for these reads.
 //
 // Split exchange.  Split s owns rows [s*128/S, (s+1)*128/S) for the
 // epilogue.  It publishes the rows it does not own (device-coherent stores),
@@ -52,8 +54,6 @@ constexpr int kRowBytes = kBK * 2;
 constexpr int kXStageBytes = kBM * kRowBytes;             // 16 KiB
 constexpr int kWStageBytes = kBN * kRowBytes;             // 32 KiB
 constexpr int kWRingOffset = kXSlots * kXStageBytes;      // 64 KiB
-constexpr int kDmaA = kBM / 8 / kWaves;                   // 1 KiB DMA blocks per wave: 2
-constexpr int kDmaB = kBN / 8 / kWaves;                   // 4
 constexpr int kTileStride = kBN + 4;        // fp32 per row of the epilogue tile
 constexpr int kTileBytes = kBM * kTileStride * 4;
 constexpr int kRingBytes = kWRingOffset + kWSlots * kWStageBytes;
@@ -91,20 +91,6 @@ __device__ __forceinline__ int x_swizzle(int R) { return kFmt == kGateBf16 ? slo
 
 constexpr int kOutOfRange = 0x7ffffff0;  // past every descriptor limit: loads read zeros
 
-// Lane i of a 1 KiB block b fills row R = 8b + i/8, slot i%8, so it fetches
-// chunk (i%8) ^ sw(R) of that row.  Chunks at or past H take the
-// out-of-range offset and land as zeros; so do rows at or past M (X limit)
-// and E (W limit).
-struct DmaPlan {
-    __amdgpu_buffer_rsrc_t x;  // this tile's rows of X
-    __amdgpu_buffer_rsrc_t w;  // all of W (bf16), or all the block-scaled codes
-    __amdgpu_buffer_rsrc_t sc; // block scales
-    int a_off[kDmaA], a_k[kDmaA];
-    int b_off[kDmaB], b_k[kDmaB];
-    int m_off[2], m_k[2];      // codes: this lane's 16 bytes of a stage, per code load
-    int s_off;                 // scales: this lane's expert row (lanes < 32)
-};
-
 // Code rows hold 16-byte chunks: MXFP4 two (one 32-block each), MXFP8 four
 // (16 k each).  Chunk c of row R sits in physical chunk c ^ sw(R); the swizzles
 // are the ones measured fastest for the fragment reads below (one ds_read_b64
@@ -118,6 +104,12 @@ __device__ __forceinline__ int quarter_swizzle(int R) { return (R >> 1) & 3; }  
 template <int kFmt> struct BStage { using type = u32x4; };
 template <> struct BStage<kGateMxfp4> { using type = u32x2; };
 
+// A 1 KiB direct-to-LDS block b of a bf16 stage fills row R = 8b + i/8 with
+// lane i, at slot i%8, so lane i fetches chunk (i%8) ^ sw(R) of that row;
+// code blocks hold 32 (MXFP4) or 16 (MXFP8) rows the same way.  Chunks at or
+// past H take the out-of-range offset and land as zeros; so do rows at or past
+// M (X limit) and E (W limit).
+//
 // One 1 KiB direct-to-LDS load (lane i's 16 bytes to lds + 16 i).  Written as
 // inline asm so that the compiler does not track it: its waitcnt pass would
 // otherwise wait for every such load in flight before any LDS read, since it
@@ -134,42 +126,6 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, int byte_off, uns
 {
     const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)lds);
     asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(byte_off), "s"(r), "{m0}"(m0) : "memory");
-}
-
-__device__ __forceinline__ void issue_x(const DmaPlan& d, unsigned char* slot, int k0, int H, int wave)
-{
-#pragma unroll
-    for (int j = 0; j < kDmaA; ++j) {
-        const int off = (k0 + d.a_k[j] < H) ? d.a_off[j] + k0 * 2 : kOutOfRange;
-        dma16(d.x, off, slot + (wave * kDmaA + j) * 1024);
-    }
-}
-
-__device__ __forceinline__ void issue_w(const DmaPlan& d, unsigned char* slot, int k0, int H, int wave)
-{
-#pragma unroll
-    for (int j = 0; j < kDmaB; ++j) {
-        const int off = (k0 + d.b_k[j] < H) ? d.b_off[j] + k0 * 2 : kOutOfRange;
-        dma16(d.w, off, slot + (wave * kDmaB + j) * 1024);
-    }
-}
-
-// Block-scaled stage: every wave loads the codes of 32 rows (1 KiB of
-// MXFP4, 2 KiB of MXFP8) and, with its first 32 lanes, the scale dwords of
-// 32 experts.  Per wave and stage: kLoads + 1 loads, whatever the lane mask.
-template <int kFmt>
-__device__ __forceinline__ void issue_w_mx(const DmaPlan& d, unsigned char* wslot, unsigned char* sslot, int k0,
-                                           int H, int wave, int lane)
-{
-    constexpr int kLoads = kCodeRowBytes<kFmt> / 32;  // 1 KiB code loads per wave
-    constexpr int kRowDiv = kFmt == kGateMxfp8 ? 1 : 2;
-#pragma unroll
-    for (int b = 0; b < kLoads; ++b) {
-        const int off = (k0 + d.m_k[b] < H) ? d.m_off[b] + k0 / kRowDiv : kOutOfRange;
-        dma16(d.w, off, wslot + (wave * kLoads + b) * 1024);
-    }
-    // the stage's two scales (k0 / 32 is even) lie in the aligned dword at k0 / 32 & ~3
-    if (lane < 32) dma4(d.sc, d.s_off + ((k0 >> 5) & ~3), sslot + wave * 128);
 }
 
 // Workgroup barrier for the LDS ring.  Each wave has already waited (vmcnt)
@@ -420,26 +376,27 @@ __device__ __forceinline__ void exchange_and_route(const PrefillLaunch& p, float
     }
 }
 
+// Role-split GEMM: waves 4..7 only issue the ring's direct-to-LDS loads (and
+// wait for them), so that only they ever queue on the memory pipeline; waves
+// 0..3 only read fragments and multiply, each a 64 x 128 block (4 x 8 MFMA
+// 16x16 accumulators).  The epilogue is the one above.
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch p)
 {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-    int& flag = *reinterpret_cast<int*>(lds + kFlagOffset);  // used only after the GEMM
-
+    int& flag = *reinterpret_cast<int*>(lds + kFlagOffset);
     float* tile_f = reinterpret_cast<float*>(lds);
 
+    constexpr bool kMx = kFmt != kGateBf16;
+    constexpr int kWStage = kWStageBytesOf<kFmt>;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int wm = wave >> 2;  // 0..1: 64-row half of the tile
-    const int wn = wave & 3;   // 0..3: 64-expert quarter
+    const bool producer = wave >= 4;
+    const int cw = wave & 3;
+    const int wm = cw >> 1;  // compute: 64-row half
+    const int wn = cw & 1;   // compute: 128-expert half
 
-    // Workgroup -> (tile, split): consecutive workgroup ids are dealt to the
-    // XCDs in turn, so ids b, b+8, b+16, ... share an XCD (and its L2).  The
-    // splits of one tile take ids 8 apart: their exchange then stays inside
-    // one XCD, where freshly written partials are re-read about 3x faster
-    // than across XCDs.  (Only speed depends on that placement.)  The grid
-    // is padded to a multiple of 8 tiles; padding workgroups exit at once.
     const int xcd = blockIdx.x % kXcds;
     const int q8 = blockIdx.x / kXcds;
     const int s = q8 % p.S;
@@ -451,155 +408,187 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
     const int k_end = min(p.H, k_begin + p.k_per_split);
     const int nstages = k_end > k_begin ? (k_end - k_begin + kBK - 1) / kBK : 0;
 
-    // ---- GEMM over this split's K range
-    f32x4 acc[4][4];  // wave tile 64 x 64: 4 x 4 MFMA 16x16 blocks
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int fr = lane & 15;  // fragment row / column
-    const int g = lane >> 4;   // this lane's 16-byte chunk inside a 32-wide k step
-
-    DmaPlan d;
-    {
-        const int64_t rows_here = min((int64_t)kBM, p.M - row0);
-        d.x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + row0 * p.H), 0,
-                                                (int)(rows_here * p.H * 2), 0x00020000);
-        if constexpr (kFmt == kGateMxfp4) {
-            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_codes), 0, p.E * (p.H / 2), 0x00020000);
-            const int R = wave * 32 + (lane >> 1);
-            d.m_k[0] = ((lane & 1) ^ half_swizzle(R)) * 32;
-            d.m_off[0] = R * (p.H / 2) + d.m_k[0] / 2;
-        } else if constexpr (kFmt == kGateMxfp8) {
-            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_codes), 0, p.E * p.H, 0x00020000);
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int R = wave * 32 + b * 16 + (lane >> 2);
-                d.m_k[b] = ((lane & 3) ^ quarter_swizzle(R)) * 16;
-                d.m_off[b] = R * p.H + d.m_k[b];
-            }
-        }
-        if constexpr (kFmt != kGateBf16) {
-            d.sc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_scale), 0, p.E * (p.H / 32),
-                                                     0x00020000);
-            d.s_off = (wave * 32 + (lane & 31)) * (p.H / 32);
-        } else {
-            d.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), 0, p.E * p.H * 2, 0x00020000);
-        }
-        const int li = lane >> 3, ls = lane & 7;
-#pragma unroll
-        for (int j = 0; j < kDmaA; ++j) {
-            const int R = (wave * kDmaA + j) * 8 + li;
-            d.a_k[j] = (ls ^ x_swizzle<kFmt>(R)) * 8;
-            d.a_off[j] = (R * p.H + d.a_k[j]) * 2;
-        }
-#pragma unroll
-        for (int j = 0; j < kDmaB; ++j) {
-            const int R = (wave * kDmaB + j) * 8 + li;
-            d.b_k[j] = (ls ^ slot_swizzle(R)) * 8;
-            d.b_off[j] = (R * p.H + d.b_k[j]) * 2;
-        }
-    }
-    // Fragment read addresses: row R, chunk c -> R * 128 + (c ^ sw(R)) * 16.
-    int a_row[4], b_row[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a_row[i] = wm * 64 + i * 16 + fr;
-        b_row[i] = wn * 64 + i * 16 + fr;
-    }
-
-    // Loads are issued in "iterations": iteration j issues X[j+3] then
-    // W[j+2]; iterations -3..-1 form the prologue.  At the top of iteration
-    // ks, X[ks] and W[ks] have landed once at most the loads of iteration
-    // ks-1 are outstanding (they were all issued after W[ks]).
     unsigned char* const xring = lds;
     unsigned char* const wring = lds + kWRingOffset;
     unsigned char* const sring = lds + kSRingOffset;
-    constexpr bool kMx = kFmt != kGateBf16;
-    constexpr int kWStage = kWStageBytesOf<kFmt>;
-    constexpr int kWLoads = kMx ? kCodeRowBytes<kFmt> / 32 + 1 : kDmaB;  // W loads per wave and stage
-    constexpr int kIterLoads = kDmaA + kWLoads;       // loads per wave and iteration
-    auto issue_iteration = [&](int j) {
-        if (j + 3 >= 0 && j + 3 < nstages)
-            issue_x(d, xring + ((j + 3) % kXSlots) * kXStageBytes, k_begin + (j + 3) * kBK, p.H, wave);
-        if (j + 2 >= 0 && j + 2 < nstages) {
-            if constexpr (kMx)
-                issue_w_mx<kFmt>(d, wring + ((j + 2) % kWSlots) * kWStage,
-                           sring + ((j + 2) % kWSlots) * kSStageBytes, k_begin + (j + 2) * kBK, p.H, wave, lane);
-            else
-                issue_w(d, wring + ((j + 2) % kWSlots) * kWStageBytes, k_begin + (j + 2) * kBK, p.H, wave);
-        }
-    };
-    issue_iteration(-3);
-    issue_iteration(-2);
-    issue_iteration(-1);
-    for (int ks = 0; ks < nstages; ++ks) {
-        if (ks + 2 < nstages)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | kIterLoads);  // iteration ks-1's loads may be in flight
-        else if (ks + 1 < nstages)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | kWLoads);     // only W[ks+1] after W[ks]
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
-        ring_barrier();
-        issue_iteration(ks);
-        const unsigned char* xs = xring + (ks % kXSlots) * kXStageBytes;
-        const unsigned char* ws = wring + (ks % kWSlots) * kWStage;
-        // block-scaled: the stage's two block scales of expert R are bytes sb0,
-        // sb0 + 1 of its dword; lane group g's k (16 g + 0..15) lie in block g / 2
-        const unsigned char* ss = sring + (ks % kWSlots) * kSStageBytes + (((k_begin + ks * kBK) >> 5) & 3);
-        // block-scaled: each lane's 16 codes of the stage (both MFMA steps) at once
-        typename BStage<kFmt>::type braw[4];
-        float bscale[4];
-        if constexpr (kMx) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (kFmt == kGateMxfp4)  // bytes 8 g .. 8 g + 7: half g / 2, offset 8 (g mod 2)
-                    braw[j] = *reinterpret_cast<const u32x2*>(ws + b_row[j] * (kBK / 2) +
-                                                              (((g >> 1) ^ half_swizzle(b_row[j])) << 4) + 8 * (g & 1));
-                else  // bytes 16 g .. 16 g + 15: chunk g
-                    braw[j] = *reinterpret_cast<const u32x4*>(ws + b_row[j] * kBK + ((g ^ quarter_swizzle(b_row[j])) << 4));
-                bscale[j] = __uint_as_float((uint32_t)ss[b_row[j] * 4 + (g >> 1)] << 23);
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < kBK / 32; ++kk) {
-            // k of lane group g in step kk: bf16 32 kk + 8 g + 0..7, block-scaled 16 g + 8 kk + 0..7
-            const int c = kMx ? 2 * g + kk : kk * 4 + g;
-            bf16x8 af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(xs + a_row[i] * kRowBytes +
-                                                          ((c ^ x_swizzle<kFmt>(a_row[i])) << 4));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (kFmt == kGateMxfp4)
-                    bfr[j] = fp4x8_to_bf16x8(braw[j][kk], bscale[j]);
-                else if constexpr (kFmt == kGateMxfp8)
-                    bfr[j] = fp8x8_to_bf16x8(braw[j][2 * kk], braw[j][2 * kk + 1], bscale[j]);
-                else
-                    bfr[j] = *reinterpret_cast<const bf16x8*>(ws + b_row[j] * kRowBytes +
-                                                               ((c ^ slot_swizzle(b_row[j])) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no ring load still in flight
-    __syncthreads();  // every wave is done with the ring before it becomes the row tile
+    const int fr = lane & 15;
+    const int g = lane >> 4;
 
-    // ---- accumulators -> fp32 row tile in LDS (reuses the ring)
-    // MFMA 16x16 layout: lane holds rows 4*(lane/16)+q of the tile, column lane%16.
+    f32x4 acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (producer) {
+        // Producer pi fills 1 KiB blocks pi*4 .. pi*4+3 of an X stage and a
+        // quarter of each W stage: bf16 blocks pi*8 .. +7; codes blocks
+        // pi*2 .. +1 (MXFP4: 32 rows each) or pi*4 .. +3 (MXFP8: 16 rows
+        // each), plus the scale dwords of experts 64 pi .. 64 pi + 63.
+        constexpr int kPA = 4;
+        constexpr int kPB = kFmt == kGateBf16 ? 8 : (kFmt == kGateMxfp4 ? 2 : 4);
+        constexpr int kPW = kPB + (kMx ? 1 : 0);  // W-side loads per stage
+        constexpr int kPLoads = kPA + kPW;
+        const int pi = wave - 4;
+        const int64_t rows_here = min((int64_t)kBM, p.M - row0);
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(p.x + row0 * p.H), 0, (int)(rows_here * p.H * 2), 0x00020000);
+        __amdgpu_buffer_rsrc_t wr, sr;
+        if constexpr (kFmt == kGateBf16)
+            wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), 0, p.E * p.H * 2, 0x00020000);
+        else
+            wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_codes), 0,
+                                                   p.E * (kFmt == kGateMxfp8 ? p.H : p.H / 2), 0x00020000);
+        if constexpr (kMx)
+            sr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_scale), 0, p.E * (p.H / 32), 0x00020000);
+        const int li = lane >> 3, ls = lane & 7;
+        int a_off[kPA], a_k[kPA], b_off[kPB], b_k[kPB];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                tile_f[(wm * 64 + i * 16 + 4 * g + q) * kTileStride + wn * 64 + j * 16 + fr] = acc[i][j][q];
+        for (int j = 0; j < kPA; ++j) {
+            const int R = (pi * kPA + j) * 8 + li;
+            a_k[j] = (ls ^ x_swizzle<kFmt>(R)) * 8;
+            a_off[j] = (R * p.H + a_k[j]) * 2;
+        }
+#pragma unroll
+        for (int j = 0; j < kPB; ++j) {
+            const int blk = pi * kPB + j;
+            if constexpr (kFmt == kGateBf16) {
+                const int R = blk * 8 + li;
+                b_k[j] = (ls ^ slot_swizzle(R)) * 8;
+                b_off[j] = (R * p.H + b_k[j]) * 2;
+            } else if constexpr (kFmt == kGateMxfp4) {
+                const int R = blk * 32 + (lane >> 1);
+                b_k[j] = ((lane & 1) ^ half_swizzle(R)) * 32;
+                b_off[j] = R * (p.H / 2) + b_k[j] / 2;
+            } else {
+                const int R = blk * 16 + (lane >> 2);
+                b_k[j] = ((lane & 3) ^ quarter_swizzle(R)) * 16;
+                b_off[j] = R * p.H + b_k[j];
+            }
+        }
+        const int s_off = (pi * 64 + lane) * (p.H / 32);
+        auto issue = [&](int j) {
+            if (j + 3 >= 0 && j + 3 < nstages) {
+                const int k0 = k_begin + (j + 3) * kBK;
+                unsigned char* slot = xring + ((j + 3) % kXSlots) * kXStageBytes;
+#pragma unroll
+                for (int q = 0; q < kPA; ++q)
+                    dma16(xr, (k0 + a_k[q] < p.H) ? a_off[q] + k0 * 2 : kOutOfRange, slot + (pi * kPA + q) * 1024);
+            }
+            if (j + 2 >= 0 && j + 2 < nstages) {
+                const int k0 = k_begin + (j + 2) * kBK;
+                unsigned char* slot = wring + ((j + 2) % kWSlots) * kWStage;
+                constexpr int kDiv = kFmt == kGateBf16 ? 0 : (kFmt == kGateMxfp4 ? 2 : 1);
+#pragma unroll
+                for (int q = 0; q < kPB; ++q) {
+                    int off;
+                    if constexpr (kFmt == kGateBf16)
+                        off = (k0 + b_k[q] < p.H) ? b_off[q] + k0 * 2 : kOutOfRange;
+                    else
+                        off = (k0 + b_k[q] < p.H) ? b_off[q] + k0 / kDiv : kOutOfRange;
+                    dma16(wr, off, slot + (pi * kPB + q) * 1024);
+                }
+                if constexpr (kMx)  // the stage's two scales lie in the aligned dword at k0 / 32 & ~3
+                    dma4(sr, s_off + ((k0 >> 5) & ~3), sring + ((j + 2) % kWSlots) * kSStageBytes + pi * 256);
+            }
+        };
+        issue(-3);
+        issue(-2);
+        issue(-1);
+        for (int ks = 0; ks < nstages; ++ks) {
+            if (ks + 2 < nstages)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | kPLoads);  // iteration ks-1's loads may be in flight
+            else if (ks + 1 < nstages)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | kPW);      // only W[ks+1] after W[ks]
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+            ring_barrier();
+            issue(ks);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+        int a_row[4], b_row[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a_row[i] = wm * 64 + i * 16 + fr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b_row[j] = wn * 128 + j * 16 + fr;
+        for (int ks = 0; ks < nstages; ++ks) {
+            ring_barrier();
+            const unsigned char* xs = xring + (ks % kXSlots) * kXStageBytes;
+            const unsigned char* ws = wring + (ks % kWSlots) * kWStage;
+            if constexpr (!kMx) {
+                bf16x8 af[2][4], bf[2][8];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int c = kk * 4 + g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        af[kk][i] = *reinterpret_cast<const bf16x8*>(xs + a_row[i] * kRowBytes +
+                                                                     ((c ^ slot_swizzle(a_row[i])) << 4));
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        bf[kk][j] = *reinterpret_cast<const bf16x8*>(ws + b_row[j] * kRowBytes +
+                                                                     ((c ^ slot_swizzle(b_row[j])) << 4));
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
+            } else {
+                // block-scaled: k of lane group g in step kk is 16 g + 8 kk + 0..7
+                // (both operands); a row's 16 codes of the stage are read once
+                const unsigned char* ss =
+                    sring + (ks % kWSlots) * kSStageBytes + (((k_begin + ks * kBK) >> 5) & 3);
+                typename BStage<kFmt>::type braw[8];
+                float bscale[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if constexpr (kFmt == kGateMxfp4)
+                        braw[j] = *reinterpret_cast<const u32x2*>(ws + b_row[j] * (kBK / 2) +
+                                                                  (((g >> 1) ^ half_swizzle(b_row[j])) << 4) + 8 * (g & 1));
+                    else
+                        braw[j] = *reinterpret_cast<const u32x4*>(ws + b_row[j] * kBK +
+                                                                  ((g ^ quarter_swizzle(b_row[j])) << 4));
+                    bscale[j] = __uint_as_float((uint32_t)ss[b_row[j] * 4 + (g >> 1)] << 23);
+                }
+                bf16x8 af[2][4];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        af[kk][i] = *reinterpret_cast<const bf16x8*>(xs + a_row[i] * kRowBytes +
+                                                                     (((2 * g + kk) ^ x_swizzle<kFmt>(a_row[i])) << 4));
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        bf16x8 b;
+                        if constexpr (kFmt == kGateMxfp4)
+                            b = fp4x8_to_bf16x8(braw[j][kk], bscale[j]);
+                        else
+                            b = fp8x8_to_bf16x8(braw[j][2 * kk], braw[j][2 * kk + 1], bscale[j]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kk][i], b, acc[i][j], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();  // every wave is done with the ring before it becomes the row tile
+
+    if (!producer) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    tile_f[(wm * 64 + i * 16 + 4 * g + q) * kTileStride + wn * 128 + j * 16 + fr] = acc[i][j][q];
+    }
     __syncthreads();
 
     float bv[kPerLane] = {0.f, 0.f, 0.f, 0.f};
@@ -610,12 +599,10 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
             if (e < p.E) bv[j] = p.bias[e];
         }
     }
-
     if (p.S == 1) {
         route_tile_rows(p, tile_f, row0, 0, kBM, wave, lane, bv);
         return;
     }
-
     if (p.S == 4)
         exchange_and_route<4>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
     else
