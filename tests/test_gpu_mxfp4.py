@@ -103,6 +103,13 @@ def test_prefill_two_and_one_splits(orc, M, H):
     check_mx(orc, W.mxfp4_case(M, H=H, seed=M, with_bias=True))
 
 
+@pytest.mark.parametrize("M,H", [(100, 128), (1000, 128), (130, 256)])
+def test_prefill_splits_without_stages(orc, M, H):
+    """Four K splits over one or two 64-wide stages: some splits have no stage
+    and contribute zero partials, but still take part in the exchange."""
+    check_mx(orc, W.mxfp4_case(M, H=H, seed=M + H, with_bias=True))
+
+
 @pytest.mark.parametrize("E,k,scoring", [(100, 6, W.SQRT_SOFTPLUS), (16, 16, W.SOFTMAX)])
 def test_prefill_experts(orc, E, k, scoring):
     check_mx(orc, W.mxfp4_case(300, H=512, seed=E, E=E, k=k, scoring=scoring, with_bias=True))
