@@ -65,7 +65,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "mxfp8", "gather", "gemm1", "prefill", "topk"],
+    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "mxfp8", "gather", "gemm1", "prefill", "topk",
+                                          "floor"],
                     default="all",
                     help="restrict to one workload (for counter-collection runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -205,6 +206,8 @@ def main():
         decode_headline(torch, R, W, dev, args, out)
     if args.section in ("all",):
         out["extras"].update(decode_extras(torch, R, W, dev, args))
+    if args.section in ("all", "floor"):
+        out["extras"].update(floor_extras(torch, W, dev, args))
     for fmt in ("mxfp4", "mxfp8"):
         if args.section in ("all", fmt):
             out["extras"].update(block_scaled_extras(torch, R, W, dev, args, fmt))
@@ -533,6 +536,79 @@ def prefill_extras(torch, R, W, dev, args):
     except RuntimeError as exc:  # library GEMM not capturable
         log(f"torch.mm context skipped: {exc}")
     log("prefill done")
+    return ex
+
+
+def floor_extras(torch, W, dev, args):
+    """Launch-floor probes on the single-token decode router's grid (256
+    workgroups, one per expert at E=256): each adds one ingredient of the
+    router's launch to the one before (libfloorprobes.so, measurement only).
+    Timed like the headline: 40 launches per step in a HIP graph, each on its
+    own gate-sized matrix from a 160-matrix (587 MB) pool."""
+    import ctypes
+    ex = {}
+    lib = ctypes.CDLL(os.path.join(ROOT, "gate_projection_top_amd", "libfloorprobes.so"))
+    P, ci = ctypes.c_void_p, ctypes.c_int
+    lib.floor_empty.argtypes = [ci, ci, P]
+    lib.floor_read.argtypes = [P, ci, ci, P, P]
+    lib.floor_ticket.argtypes = [P, ci, ci, P, P, P, P, ci, P]
+    lib.floor_latency.argtypes = [P, P, ci, P, P]
+    E, H = 256, 7168
+    n16 = H * 2 // 16
+    pool = torch.randn((POOL, E, H), device=dev, dtype=torch.bfloat16)
+    out = torch.zeros(E + 1, dtype=torch.float32, device=dev)
+    ctr = torch.zeros(16 * 17, dtype=torch.int32, device=dev)
+    slots = torch.zeros(E * 2, dtype=torch.int32, device=dev)
+    epoch = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"floor probe failed: {rc}")
+
+    probes = {
+        "empty": lambda m: check(lib.floor_empty(E, 256, stream())),
+        "empty_1x64": lambda m: check(lib.floor_empty(1, 64, stream())),
+        "empty_256x64": lambda m: check(lib.floor_empty(E, 64, stream())),
+        "empty_256x320": lambda m: check(lib.floor_empty(E, 320, stream())),
+        "empty_512x256": lambda m: check(lib.floor_empty(2 * E, 256, stream())),
+        "read": lambda m: check(lib.floor_read(ctypes.c_void_p(pool[m].data_ptr()), n16, E,
+                                               ctypes.c_void_p(out.data_ptr()), stream())),
+        "ticket": lambda m: check(lib.floor_ticket(ctypes.c_void_p(pool[m].data_ptr()), n16, E,
+                                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ctr.data_ptr()),
+                                                   ctypes.c_void_p(slots.data_ptr()),
+                                                   ctypes.c_void_p(epoch.data_ptr()), 0, stream())),
+        "handoff": lambda m: check(lib.floor_ticket(ctypes.c_void_p(pool[m].data_ptr()), n16, E,
+                                                    ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ctr.data_ptr()),
+                                                    ctypes.c_void_p(slots.data_ptr()),
+                                                    ctypes.c_void_p(epoch.data_ptr()), 1, stream())),
+    }
+    groups = POOL // LAYERS
+    for name, fn in probes.items():
+        graphs = [GraphTimer(torch, [(lambda l=l, g=g: fn(g * LAYERS + l)) for l in range(LAYERS)])
+                  for g in range(groups)]
+        _, ev_ms = timed_replays(torch, graphs, args.steps, args.warmup)
+        ex[f"floor_{name}_us_per_launch"] = round(ev_ms * 1e3 / (args.steps * LAYERS), 3)
+        del graphs
+    # dependent round trips, in-kernel clock (100 MHz): atomic, coherent load, cold load
+    lat = torch.zeros(4, dtype=torch.float32, device=dev)
+    scratch = torch.zeros(1024, dtype=torch.int32, device=dev)
+    acc = [0.0, 0.0, 0.0]
+    runs = 8
+    for r in range(runs):
+        check(lib.floor_latency(ctypes.c_void_p(scratch.data_ptr()), ctypes.c_void_p(pool[97 + r].data_ptr()), 64,
+                                ctypes.c_void_p(lat.data_ptr()), stream()))
+        torch.cuda.synchronize()
+        v = lat.tolist()
+        for i in range(3):
+            acc[i] += v[i] / runs
+    ex["floor_atomic_rtt_us"] = round(acc[0] / 100.0, 3)
+    ex["floor_coherent_load_rtt_us"] = round(acc[1] / 100.0, 3)
+    ex["floor_cold_load_rtt_us"] = round(acc[2] / 100.0, 3)
+    del pool
+    log("floor probes done")
     return ex
 
 

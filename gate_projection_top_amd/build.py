@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "librouter.so")
 
-SOURCES = ["router_api.cpp", "topk_kernel.hip", "decode_kernel.hip", "prefill_kernel.hip",
-           "gather_kernel.hip", "gemm1_kernel.hip"]
+SOURCES = ["router_api.cpp", "topk_kernel.hip", "decode_kernel.hip", "decode_expert_kernel.hip",
+           "prefill_kernel.hip", "gather_kernel.hip", "gemm1_kernel.hip"]
 HEADERS = ["route_common.hpp", "launch.hpp", "coherent.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,9 +41,18 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB_PATH, verbose: bool = False) -> str:
+PROBE_SOURCES = ["floor_probes.hip"]
+PROBE_LIB_PATH = os.path.join(PKG, "libfloorprobes.so")
+
+
+def build_probes(out: str = PROBE_LIB_PATH, verbose: bool = False) -> str:
+    """Compile the launch-floor probes the benchmark times (not part of the router)."""
+    return build(out, verbose, sources=PROBE_SOURCES)
+
+
+def build(out: str = LIB_PATH, verbose: bool = False, sources=None) -> str:
     """Compile every source into one shared library (always rebuilds)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    srcs = [os.path.join(CSRC, s) for s in (sources or SOURCES)]
     tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
     if verbose:
@@ -62,3 +71,4 @@ def build(out: str = LIB_PATH, verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probes(verbose=True))

@@ -42,6 +42,11 @@ struct DecodeLaunch {
     int S;                  // H splits
     int ks_per_split;       // k units per split: 32-wide k-steps (bf16 gate), 128-wide blocks (MX)
     int load_waves;         // geometry: kDecodeNarrow.load_waves or kDecodeWide.load_waves
+    // one-expert-per-workgroup kernel (M <= kExpertMaxRows)
+    uint32_t* xslots;       // workspace [kExpertMaxRows][256] (logit bits, tag) pairs, tag 0 between calls
+    uint64_t* xcounters;    // workspace, kExpertCounterWords words: group words (epoch << 8 | count)
+    uint32_t* status;       // workspace: sticky status bits (kStatus*)
+    uint32_t wait_ticks;    // bound on the finisher's wait (100 MHz realtime ticks)
 };
 
 struct PrefillLaunch {
@@ -94,6 +99,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 hipError_t launch_gemm1(const Gemm1Launch& a, hipStream_t stream);
 hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+hipError_t launch_decode_expert(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 int prefill_splits(int64_t M);
 
@@ -114,6 +120,20 @@ constexpr uint32_t kPartialSentinel = 0x7f800001u;
 // Guard on the finisher's wait for published partials (100 MHz realtime
 // clock): 100 ms, orders of magnitude above any real wait.
 constexpr uint64_t kDecodePollLimitTicks = 10000000u;
+
+// One-expert-per-workgroup decode kernel: token counts up to kExpertMaxRows;
+// arrival counters for groups of kExpertGroup workgroups, one 64-byte line
+// (kExpertCounterStride 8-byte words) apart, then the group counter.
+constexpr int kExpertMaxRows = 4;
+constexpr int kExpertWaves = 4;
+constexpr int kExpertGroup = 16;
+constexpr int kExpertGroups = 256 / kExpertGroup;
+constexpr int kExpertCounterStride = 8;
+constexpr int kExpertCounterWords = kExpertCounterStride * (kExpertGroups + 1);
+// Sticky status bits (workspace word, read and cleared by router_status).
+constexpr uint32_t kStatusWaitLimit = 1u;  // a finisher stopped waiting at the time limit
+// Default bound on a decode finisher's wait: 100 ms (100 MHz realtime clock).
+constexpr uint32_t kDecodeWaitTicksDefault = 10000000u;
 
 // Two decode geometries.  A row block with at most kDecodeNarrowMaxRows
 // tokens takes about 256 workgroups of 3 load waves: more CUs pull W (each

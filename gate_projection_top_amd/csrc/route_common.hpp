@@ -220,7 +220,10 @@ __device__ __forceinline__ double rank_sum(double u)
 //   kRoundsScalar: the maximum and the winning lane pass through scalar
 //     registers (readlane, find-first-set).  Fewer vector instructions per
 //     round: for routing waves that share a SIMD.
-enum RoundStyle : int { kRoundsLane = 0, kRoundsScalar = 1 };
+//   kFilter: no rounds where a threshold leaves between k and kFilterCap
+//     candidates (select_filter above): they are ranked by counting; the
+//     lane rounds otherwise.  Needs kFilterCap 8-byte LDS entries per row.
+enum RoundStyle : int { kRoundsLane = 0, kRoundsScalar = 1, kFilter = 2 };
 
 template <RoundStyle kStyle>
 __device__ __forceinline__ uint32_t max_code(uint32_t v)
@@ -231,6 +234,100 @@ __device__ __forceinline__ uint32_t max_code(uint32_t v)
         return wave_max_u32(v);
 }
 
+// Filtered selection of one row (the lane's four codes sorted in selection
+// order, their slots in `order`, two bits each, head lowest).
+//
+// A threshold T below the row maximum is chosen so that at least k and at
+// most kFilterCap codes reach it: T = max - D in code space (codes are
+// monotone in the key), D moved by doubling, halving and bisection, each try
+// costing one ballot and population count per code slot.  Every winner is at
+// or above T (at least k codes are), so the winners are the first k of the
+// candidates under the contract's precedence.  Each candidate goes to LDS as
+// one 64-bit word, code above (0xFFFF - expert) below, so that one unsigned
+// comparison is that precedence (larger key first, equal keys by lower
+// index); a candidate's rank is the number of candidate words above its own,
+// and the first k are re-read in rank order.  Lane j < k ends with the index
+// and the code of rank j.  Rows where no such T exists within the try budget
+// (many equal or nearly equal codes near the top) return false and leave the
+// outputs untouched; the caller runs the rounds instead.
+// `lds`: kFilterCap entries owned by this wave.
+constexpr int kFilterCap = 32;
+constexpr int kFilterTries = 6;
+
+__device__ __forceinline__ int count_at_least(const uint32_t (&c)[kPerLane], uint32_t T)
+{
+    return __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[0] >= T)) +
+           __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[1] >= T)) +
+           __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[2] >= T)) +
+           __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[3] >= T));
+}
+
+__device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uint32_t order, int k,
+                                              uint64_t* lds, int& my_idx, uint32_t& my_code)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t top = wave_max_u32(c[0]);
+    // distances in code space: dlo gave fewer than k codes, dhi more than the cap
+    uint32_t D = 3u << 21, dlo = 0u, dhi = 0u, T = 1u;
+    int n = 0;
+    bool found = false;
+    for (int t = 0; t < kFilterTries; ++t) {
+        T = top > D ? top - D : 1u;  // valid codes are >= 1; absent entries are 0
+        n = count_at_least(c, T);
+        if (n >= k && n <= kFilterCap) {
+            found = true;
+            break;
+        }
+        if (n < k) {
+            if (T == 1u) break;  // fewer than k valid codes cannot happen; stop
+            dlo = D;
+            D = dhi ? dlo + ((dhi - dlo) >> 1) : (D > 0x7fffffffu ? 0xffffffffu : 2u * D);
+        } else {
+            dhi = D;
+            D = dlo + ((dhi - dlo) >> 1);
+        }
+        if (dhi && dhi - dlo <= 1u) break;  // no threshold separates k..cap codes
+    }
+    if (!found) return false;
+    // compaction: candidates of lower lanes first, then this lane's in its order
+    uint32_t at = 0u;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(c[j] >= T);
+        at += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    }
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        if (c[j] >= T) {
+            const uint32_t idx = (uint32_t)(lane * kPerLane) + ((order >> (2 * j)) & 3u);
+            lds[at] = ((uint64_t)c[j] << 32) | (0xFFFFu - idx);
+            at += 1u;
+        }
+    }
+    const int n8 = (n + 7) & ~7;
+    if (lane >= n && lane < n8) lds[lane] = 0ull;  // below every candidate word
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    const uint64_t mine = lane < n ? lds[lane] : 0ull;
+    int rank = 0;
+    for (int j = 0; j < n8; j += 8) {
+        uint64_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = lds[j + i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rank += q[i] > mine ? 1 : 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    if (lane < n && rank < k) lds[rank] = mine;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    const uint64_t got = lane < k ? lds[lane] : 0ull;
+    my_code = (uint32_t)(got >> 32);
+    my_idx = lane < k ? (int)(0xFFFFu - (uint32_t)got) : 0;
+    return true;
+}
+
 // k rounds over N rows: the wave-wide largest head wins; among equal heads
 // the lowest lane, whose head is its lowest-slot entry of that code, i.e. the
 // lowest expert index.  The winning lane pops its head.  c[n]: the lane's
@@ -238,10 +335,16 @@ __device__ __forceinline__ uint32_t max_code(uint32_t v)
 // in the low bits.  Lane j < k ends with the index and code of rank j.
 template <int N, RoundStyle kStyle>
 __device__ __forceinline__ void select_rounds(uint32_t (&c)[N][kPerLane], const uint32_t (&order)[N],
-                                              int k, int (&my_idx)[N], uint32_t (&my_code)[N])
+                                              int k, int (&my_idx)[N], uint32_t (&my_code)[N],
+                                              uint64_t* lds)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    if constexpr (kStyle == kRoundsLane) {
+    if constexpr (kStyle == kFilter) {
+        bool done = true;
+#pragma unroll
+        for (int n = 0; n < N; ++n) done &= select_filter(c[n], order[n], k, lds + n * kFilterCap, my_idx[n], my_code[n]);
+        if (!done) select_rounds<N, kRoundsLane>(c, order, k, my_idx, my_code, lds);
+    } else if constexpr (kStyle == kRoundsLane) {
         // lane `it` keeps round it's mask; each lane lists the ranks it won
         uint64_t my_mask[N];
         uint32_t wins[N], wshift[N];
@@ -316,7 +419,7 @@ __device__ __forceinline__ void select_rounds(uint32_t (&c)[N][kPerLane], const 
 template <int N, bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
                                                 const float (&bv)[kPerLane], const RowSpec& s,
-                                                RowResult (&out)[N])
+                                                RowResult (&out)[N], uint64_t* lds)
 {
     const int lane = threadIdx.x & (kWave - 1);
     bool valid[kPerLane];
@@ -405,7 +508,7 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
 
     int my_idx[N];
     uint32_t my_code[N];
-    select_rounds<N, kStyle>(c, slots, s.k, my_idx, my_code);
+    select_rounds<N, kStyle>(c, slots, s.k, my_idx, my_code, lds);
 
     // The winners' unbiased scores.  When every score was computed above,
     // fetch the winner's from the lane that holds it; otherwise compute it
@@ -450,15 +553,16 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
 }
 
 // N rows in lockstep (same spec); rows n carry logits v[n] and get out[n].
+// lds: N * kFilterCap entries owned by this wave (kFilter only).
 template <int N, RoundStyle kStyle = kRoundsScalar>
 __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const float (&bv)[kPerLane],
-                                           const RowSpec& s, RowResult (&out)[N])
+                                           const RowSpec& s, RowResult (&out)[N], uint64_t* lds = nullptr)
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
     if (need_all)
-        route_rows_impl<N, true, kStyle>(v, bv, s, out);
+        route_rows_impl<N, true, kStyle>(v, bv, s, out, lds);
     else
-        route_rows_impl<N, false, kStyle>(v, bv, s, out);
+        route_rows_impl<N, false, kStyle>(v, bv, s, out, lds);
 }
 
 // One row: the same steps as route_rows, written for a single row (the
@@ -466,7 +570,8 @@ __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const 
 // two give bit-identical results on identical inputs.
 template <bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
-                                                    const float (&bv)[kPerLane], const RowSpec& s)
+                                                    const float (&bv)[kPerLane], const RowSpec& s,
+                                                    uint64_t* lds)
 {
     const int lane = threadIdx.x & (kWave - 1);
     bool valid[kPerLane];
@@ -532,7 +637,7 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     const uint32_t ord[1] = {slots};
     int idx1[1];
     uint32_t code1[1];
-    select_rounds<1, kStyle>(cc, ord, s.k, idx1, code1);
+    select_rounds<1, kStyle>(cc, ord, s.k, idx1, code1, lds);
     const int my_idx = idx1[0];
     const uint32_t my_code = code1[0];
 
@@ -570,12 +675,14 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     return RowResult{my_idx, w};
 }
 
+// lds: kFilterCap entries owned by this wave (kFilter only).
 template <RoundStyle kStyle = kRoundsLane>
 __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
-                                               const float (&bv)[kPerLane], const RowSpec& s)
+                                               const float (&bv)[kPerLane], const RowSpec& s,
+                                               uint64_t* lds = nullptr)
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
-    return need_all ? route_row_impl<true, kStyle>(v, bv, s) : route_row_impl<false, kStyle>(v, bv, s);
+    return need_all ? route_row_impl<true, kStyle>(v, bv, s, lds) : route_row_impl<false, kStyle>(v, bv, s, lds);
 }
 
 // ---------------------------------------------------------------------------

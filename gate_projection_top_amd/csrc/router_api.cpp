@@ -13,6 +13,9 @@ namespace {
 struct DeviceWorkspace {
     float* partials = nullptr;          // decode H-split partial logits [S][M][256], sentinel-filled
     uint32_t* counters = nullptr;       // decode arrival counters (two levels)
+    uint32_t* xslots = nullptr;         // one-expert decode: tagged logit slots, zero-filled
+    uint64_t* xcounters = nullptr;      // one-expert decode: epoch/arrival words, zero-filled
+    uint32_t* status = nullptr;         // sticky status bits
     float* pf_partials = nullptr;       // prefill split partials [tile][S][128][256]
     uint32_t* pf_counters = nullptr;    // prefill per-tile counters
 };
@@ -24,9 +27,11 @@ constexpr int kCounters = gpt::kDecodeCounters;
 constexpr size_t kPfPartialFloats =
     (size_t)gpt::kPrefillMaxPairs * gpt::kPrefillTileRows * ROUTER_MAX_E;  // 32 MiB
 constexpr size_t kPfCounters = (size_t)gpt::kPrefillMaxSplitTiles * gpt::kPrefillCountersPerTile;
+constexpr size_t kXSlotWords = (size_t)gpt::kExpertMaxRows * ROUTER_MAX_E * 2;  // (logit, tag) pairs
 
 DeviceWorkspace g_ws[kMaxDevices];
 std::atomic<uint32_t> g_spin_ticks{20000};  // 200 us at the 100 MHz realtime clock
+std::atomic<uint32_t> g_decode_wait_ticks{gpt::kDecodeWaitTicksDefault};
 std::mutex g_ws_mutex;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -46,6 +51,12 @@ int init_device(int dev)
     if (e == hipSuccess) e = hipMalloc((void**)&ws.counters, kCounters * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_partials, kPfPartialFloats * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_counters, kPfCounters * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMalloc((void**)&ws.xslots, kXSlotWords * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMalloc((void**)&ws.xcounters, gpt::kExpertCounterWords * sizeof(uint64_t));
+    if (e == hipSuccess) e = hipMalloc((void**)&ws.status, sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ws.xslots, 0, kXSlotWords * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ws.xcounters, 0, gpt::kExpertCounterWords * sizeof(uint64_t));
+    if (e == hipSuccess) e = hipMemset(ws.status, 0, sizeof(uint32_t));
     if (e == hipSuccess)
         e = hipMemsetD32((hipDeviceptr_t)ws.partials, (int)gpt::kPartialSentinel, kPartialFloats);
     if (e == hipSuccess) e = hipMemset(ws.counters, 0, kCounters * sizeof(uint32_t));
@@ -59,6 +70,9 @@ int init_device(int dev)
         if (ws.counters) (void)hipFree(ws.counters);
         if (ws.pf_partials) (void)hipFree(ws.pf_partials);
         if (ws.pf_counters) (void)hipFree(ws.pf_counters);
+        if (ws.xslots) (void)hipFree(ws.xslots);
+        if (ws.xcounters) (void)hipFree(ws.xcounters);
+        if (ws.status) (void)hipFree(ws.status);
         return ROUTER_ERR_NO_WORKSPACE;
     }
     g_ws[dev] = ws;
@@ -151,9 +165,17 @@ int run_fused(const void* x, const void* w, int format, const uint8_t* w_codes, 
         a.table_count = t_count;
         a.partials = ws.partials;
         a.counters = ws.counters;
-        const int units = format != gpt::kGateBf16 ? (H + 127) / 128 : (H + 31) / 32;
-        decode_splits((int)M, units, E, &a.S, &a.ks_per_split, &a.load_waves);
-        e = gpt::launch_decode(a, stream);
+        a.xslots = ws.xslots;
+        a.xcounters = ws.xcounters;
+        a.status = ws.status;
+        a.wait_ticks = g_decode_wait_ticks.load(std::memory_order_relaxed);
+        if (M <= gpt::kExpertMaxRows) {
+            e = gpt::launch_decode_expert(a, stream);
+        } else {
+            const int units = format != gpt::kGateBf16 ? (H + 127) / 128 : (H + 31) / 32;
+            decode_splits((int)M, units, E, &a.S, &a.ks_per_split, &a.load_waves);
+            e = gpt::launch_decode(a, stream);
+        }
     } else {
         gpt::PrefillLaunch a{};
         a.x = static_cast<const uint16_t*>(x);
@@ -394,6 +416,41 @@ int router_set_exchange_timeout_us(int microseconds)
     const uint64_t ticks = (uint64_t)microseconds * 100u;
     g_spin_ticks.store(ticks > 0xffffffffu ? 0xffffffffu : (uint32_t)ticks, std::memory_order_relaxed);
     return ROUTER_OK;
+}
+
+int router_set_decode_wait_limit_us(int microseconds)
+{
+    if (microseconds < 0) return ROUTER_ERR_INVALID_ARGUMENT;
+    const uint64_t ticks = (uint64_t)microseconds * 100u;
+    g_decode_wait_ticks.store(ticks > 0xffffffffu ? 0xffffffffu : (uint32_t)ticks, std::memory_order_relaxed);
+    return ROUTER_OK;
+}
+
+int router_status(int device, int clear, uint32_t* out_flags)
+{
+    if (!out_flags) return ROUTER_ERR_INVALID_ARGUMENT;
+    if (device < 0) {
+        if (hipGetDevice(&device) != hipSuccess) return ROUTER_ERR_HIP;
+    }
+    if (device >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
+    uint32_t* st = nullptr;
+    {
+        std::lock_guard<std::mutex> guard(g_ws_mutex);
+        st = g_ws[device].status;
+    }
+    if (!st) {
+        *out_flags = 0;
+        return ROUTER_OK;
+    }
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return ROUTER_ERR_HIP;
+    if (prev != device && hipSetDevice(device) != hipSuccess) return ROUTER_ERR_HIP;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(out_flags, st, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) e = hipMemset(st, 0, sizeof(uint32_t));
+    if (e == hipSuccess && clear) e = hipDeviceSynchronize();
+    if (prev != device) (void)hipSetDevice(prev);
+    return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
 const char* router_strerror(int code)

@@ -282,6 +282,29 @@ int router_topk_from_logits(const float* logits, const float* bias, int64_t M, i
  * are rejected with ROUTER_ERR_INVALID_ARGUMENT. */
 int router_set_exchange_timeout_us(int microseconds);
 
+/* Bound, in microseconds, on how long a decode finisher (the workgroup that
+ * routes the rows) waits for the other workgroups' published logits before
+ * it gives a row up (default 100000 = 100 ms; every real wait ends in
+ * microseconds).  A row given up comes out as index -1 with a NaN weight in
+ * each of its k places, and ROUTER_STATUS_WAIT_LIMIT is set in the device's
+ * sticky status word (router_status).  The workspace stays valid: values
+ * published after the finisher stopped waiting carry an older launch's tag
+ * and are never taken for a later launch's.  0 gives every row up unless its
+ * logits are already in place at the first look (used by the tests to
+ * exercise that path from the host).  Process-wide; applies to calls
+ * enqueued after it returns.  Negative values: ROUTER_ERR_INVALID_ARGUMENT. */
+int router_set_decode_wait_limit_us(int microseconds);
+
+/* Sticky status bits of a device's workspace. */
+#define ROUTER_STATUS_WAIT_LIMIT 1u /* a decode finisher gave a row up */
+
+/* Waits for the device to finish all enqueued work (hipDeviceSynchronize),
+ * then reads the device's sticky status bits into *out_flags (0 when the
+ * workspace was never allocated); clear != 0 also resets them to 0.
+ * device < 0 means the current device.  Synchronising: not for use inside
+ * graph capture. */
+int router_status(int device, int clear, uint32_t* out_flags);
+
 /* Static, human-readable name of a return code. */
 const char* router_strerror(int code);
 
