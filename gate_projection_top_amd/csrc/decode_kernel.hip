@@ -106,6 +106,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     __shared__ int32_t tab_first[kMaxE + 1], tab_mask[kMaxE + 1];
     __shared__ int polled[kDecodeTile];  // finisher: 1 = row's partials read, 2 = row gave up
     __shared__ int fin_index;  // this workgroup's finisher index, -1: not a finisher
+    __shared__ uint64_t sel[kWaves][kFilterCap];  // selection scratch, one per routing wave
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -418,7 +419,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         }
         // a routing wave has a SIMD to itself in the narrow geometry; the
         // wide one puts two or three waves on each SIMD
-        const RowResult res = route_row<kLoadWaves + 1 <= 4 ? kRoundsLane : kRoundsScalar>(v, bv, spec);
+        const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave]);
         if (!real) {
             asm volatile("; dummy row %0 %1" :: "v"(res.idx), "v"(res.w));  // keep the pass
             continue;

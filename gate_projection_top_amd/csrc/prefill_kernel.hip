@@ -59,6 +59,8 @@ constexpr int kTileBytes = kBM * kTileStride * 4;
 constexpr int kRingBytes = kWRingOffset + kWSlots * kWStageBytes;
 constexpr int kLdsBytes = kRingBytes;
 constexpr int kFlagOffset = kLdsBytes - 16;  // one int after the ring's last use
+// epilogue: each wave's selection scratch (route_rows' filter), past the row tile
+constexpr int kSelOffset = ((kBM * (kBN + 4) * 4) + 255) & ~255;
 // Block-scaled gate: a W stage holds 256 rows of 64 k codes (32 bytes of
 // MXFP4, 64 of MXFP8) and a scale stage one dword per expert (the aligned
 // dword holding the stage's two block scales); the X ring is unchanged.
@@ -68,6 +70,7 @@ constexpr int kSStageBytes = kBN * 4;                            // 1 KiB
 constexpr int kSRingOffset = kWRingOffset + kWSlots * kWStageBytesOf<kGateMxfp8>;
 static_assert(kSRingOffset + kWSlots * kSStageBytes <= kRingBytes, "block-scaled rings fit the LDS ring");
 static_assert(kTileBytes <= kFlagOffset, "row tile and flag overlap");
+static_assert(kSelOffset + kWaves * 4 * kFilterCap * 8 <= kFlagOffset, "selection scratch and flag overlap");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -152,7 +155,13 @@ constexpr int kRowGroup = 4;  // rows a wave routes in lockstep (route_rows)
 
 // Route rows [r_begin, r_end) of the LDS tile (local row indices): wave w
 // takes rows w, w+8, ... in groups of kRowGroup routed together.
-__device__ __forceinline__ void route_tile_rows(const PrefillLaunch& p, const float* tile,
+__device__ __forceinline__ uint64_t* wave_sel(float* tile_f, int wave)
+{
+    return reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(tile_f) + kSelOffset) +
+           wave * kRowGroup * kFilterCap;
+}
+
+__device__ __forceinline__ void route_tile_rows(const PrefillLaunch& p, float* tile,
                                                 int64_t row0, int r_begin, int r_end, int wave,
                                                 int lane, const float (&bv)[kPerLane])
 {
@@ -168,7 +177,7 @@ __device__ __forceinline__ void route_tile_rows(const PrefillLaunch& p, const fl
                 v[g][j] = (t < r_end && col + j < p.E) ? tile[t * kTileStride + col + j] : 0.f;
         }
         RowResult res[kRowGroup];
-        route_rows<kRowGroup>(v, bv, spec, res);
+        route_rows<kRowGroup, kFilter>(v, bv, spec, res, wave_sel(tile, wave));
 #pragma unroll
         for (int g = 0; g < kRowGroup; ++g) {
             const int t = t0 + g * kWaves;
@@ -218,7 +227,7 @@ __device__ __forceinline__ void pf_gather_rows(const PrefillLaunch& p, float* ti
 // Every split's partials are complete (each waited for its stores before
 // counting itself in).
 template <int S>
-__device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, const float* tile_f, int tile,
+__device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, float* tile_f, int tile,
                                                   int s, int64_t row0, int r0, int rows, int wave,
                                                   int lane, const float (&bv)[kPerLane])
 {
@@ -262,7 +271,8 @@ __device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, const 
             }
         }
         RowResult res[G];
-        route_rows<G>(v, bv, spec, res);
+        static_assert(G == kRowGroup, "selection scratch holds kRowGroup rows per wave");
+        route_rows<G, kFilter>(v, bv, spec, res, wave_sel(tile_f, wave));
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int t = t0 + g * kWaves;

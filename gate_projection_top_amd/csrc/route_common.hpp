@@ -339,12 +339,8 @@ __device__ __forceinline__ void select_rounds(uint32_t (&c)[N][kPerLane], const 
                                               uint64_t* lds)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    if constexpr (kStyle == kFilter) {
-        bool done = true;
-#pragma unroll
-        for (int n = 0; n < N; ++n) done &= select_filter(c[n], order[n], k, lds + n * kFilterCap, my_idx[n], my_code[n]);
-        if (!done) select_rounds<N, kRoundsLane>(c, order, k, my_idx, my_code, lds);
-    } else if constexpr (kStyle == kRoundsLane) {
+    static_assert(kStyle != kFilter, "the filter is tried by the callers; select_rounds runs the rounds");
+    if constexpr (kStyle == kRoundsLane) {
         // lane `it` keeps round it's mask; each lane lists the ranks it won
         uint64_t my_mask[N];
         uint32_t wins[N], wshift[N];
@@ -481,12 +477,11 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
         }
     }
 
-    // Selection codes, then each lane's four entries in selection order.
+    // Selection codes (lane-local order: the filter needs none, the rounds
+    // sort each lane's four entries first).
     uint32_t c[N][kPerLane];
-    uint32_t slots[N];  // the four slots in selection order, two bits each, head lowest
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        int slot[kPerLane];
 #pragma unroll
         for (int j = 0; j < kPerLane; ++j) {
             float key = v[n][j];
@@ -495,20 +490,33 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
                 key = s32 + bv[j];
             }
             c[n][j] = valid[j] ? order_code(key) : 0u;
-            slot[j] = j;
         }
-        order_pair(c[n][0], slot[0], c[n][1], slot[1]);
-        order_pair(c[n][2], slot[2], c[n][3], slot[3]);
-        order_pair(c[n][0], slot[0], c[n][2], slot[2]);
-        order_pair(c[n][1], slot[1], c[n][3], slot[3]);
-        order_pair(c[n][1], slot[1], c[n][2], slot[2]);
-        slots[n] = (uint32_t)slot[0] | ((uint32_t)slot[1] << 2) | ((uint32_t)slot[2] << 4) |
-                   ((uint32_t)slot[3] << 6);
     }
-
     int my_idx[N];
     uint32_t my_code[N];
-    select_rounds<N, kStyle>(c, slots, s.k, my_idx, my_code, lds);
+    bool selected = false;
+    if constexpr (kStyle == kFilter) {
+        selected = true;
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            selected &= select_filter(c[n], 0xE4u, s.k, lds + n * kFilterCap, my_idx[n], my_code[n]);
+    }
+    if (!selected) {
+        uint32_t slots[N];  // the four slots in selection order, two bits each, head lowest
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            int slot[kPerLane] = {0, 1, 2, 3};
+            order_pair(c[n][0], slot[0], c[n][1], slot[1]);
+            order_pair(c[n][2], slot[2], c[n][3], slot[3]);
+            order_pair(c[n][0], slot[0], c[n][2], slot[2]);
+            order_pair(c[n][1], slot[1], c[n][3], slot[3]);
+            order_pair(c[n][1], slot[1], c[n][2], slot[2]);
+            slots[n] = (uint32_t)slot[0] | ((uint32_t)slot[1] << 2) | ((uint32_t)slot[2] << 4) |
+                       ((uint32_t)slot[3] << 6);
+        }
+        constexpr RoundStyle kRounds = kStyle == kFilter ? kRoundsScalar : kStyle;
+        select_rounds<N, kRounds>(c, slots, s.k, my_idx, my_code, lds);
+    }
 
     // The winners' unbiased scores.  When every score was computed above,
     // fetch the winner's from the lane that holds it; otherwise compute it
@@ -568,10 +576,18 @@ __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const 
 // One row: the same steps as route_rows, written for a single row (the
 // generic form costs the single-row decode path ~0.3 us of latency).  The
 // two give bit-identical results on identical inputs.
+//
+// ext_u (optional, only where no score is needed before the selection, i.e.
+// !kNeedAll): the row's unbiased scores by expert, written by another wave
+// with row_unbiased_scores() below; this wave waits until *ext_ready reaches
+// ext_want and then reads its winner's score from there instead of
+// computing it.  The scores are the same function of the same logits, so the
+// result is bit-identical either way.
 template <bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
                                                     const float (&bv)[kPerLane], const RowSpec& s,
-                                                    uint64_t* lds)
+                                                    uint64_t* lds, const double* ext_u = nullptr,
+                                                    int* ext_ready = nullptr, int ext_want = 0)
 {
     const int lane = threadIdx.x & (kWave - 1);
     bool valid[kPerLane];
@@ -624,22 +640,30 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
         c[j] = valid[j] ? order_code(key) : 0u;
         slot[j] = j;
     }
-    order_pair(c[0], slot[0], c[1], slot[1]);
-    order_pair(c[2], slot[2], c[3], slot[3]);
-    order_pair(c[0], slot[0], c[2], slot[2]);
-    order_pair(c[1], slot[1], c[3], slot[3]);
-    order_pair(c[1], slot[1], c[2], slot[2]);
-    // the four slots in selection order, two bits each, head in the low bits
-    uint32_t slots = (uint32_t)slot[0] | ((uint32_t)slot[1] << 2) | ((uint32_t)slot[2] << 4) |
-                     ((uint32_t)slot[3] << 6);
-
-    uint32_t cc[1][kPerLane] = {{c[0], c[1], c[2], c[3]}};
-    const uint32_t ord[1] = {slots};
-    int idx1[1];
-    uint32_t code1[1];
-    select_rounds<1, kStyle>(cc, ord, s.k, idx1, code1, lds);
-    const int my_idx = idx1[0];
-    const uint32_t my_code = code1[0];
+    int my_idx = 0;
+    uint32_t my_code = 0u;
+    // the filter needs no order inside a lane (its words carry the index);
+    // the lane's entries are sorted only for the rounds
+    bool selected = false;
+    if constexpr (kStyle == kFilter) selected = select_filter(c, 0xE4u, s.k, lds, my_idx, my_code);
+    if (!selected) {
+        order_pair(c[0], slot[0], c[1], slot[1]);
+        order_pair(c[2], slot[2], c[3], slot[3]);
+        order_pair(c[0], slot[0], c[2], slot[2]);
+        order_pair(c[1], slot[1], c[3], slot[3]);
+        order_pair(c[1], slot[1], c[2], slot[2]);
+        // the four slots in selection order, two bits each, head in the low bits
+        uint32_t slots = (uint32_t)slot[0] | ((uint32_t)slot[1] << 2) | ((uint32_t)slot[2] << 4) |
+                         ((uint32_t)slot[3] << 6);
+        uint32_t cc[1][kPerLane] = {{c[0], c[1], c[2], c[3]}};
+        const uint32_t ord[1] = {slots};
+        int idx1[1];
+        uint32_t code1[1];
+        constexpr RoundStyle kRounds = kStyle == kFilter ? kRoundsLane : kStyle;
+        select_rounds<1, kRounds>(cc, ord, s.k, idx1, code1, lds);
+        my_idx = idx1[0];
+        my_code = code1[0];
+    }
 
     // The winners' unbiased scores.  When every score was computed above,
     // fetch the winner's from the lane that holds it; otherwise compute it
@@ -658,6 +682,10 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
         }
         u = j == 0 ? got[0] : (j == 1 ? got[1] : (j == 2 ? got[2] : got[3]));
         if (lane >= s.k) u = 0.0;
+    } else if (ext_u) {
+        while (__hip_atomic_load(ext_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < ext_want)
+            __builtin_amdgcn_s_sleep(1);
+        if (lane < s.k) u = ext_u[my_idx];
     } else {
         if (softmax) mx = order_value(readlane_u32(my_code, 0));  // rank 0 holds the max
         if (lane < s.k) {
@@ -675,14 +703,51 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     return RowResult{my_idx, w};
 }
 
-// lds: kFilterCap entries owned by this wave (kFilter only).
+// Every expert's unbiased score of one row (lane L: experts 4L..4L+3) into
+// u[e], for a row whose selection needs no score (no bias, and renorm on or
+// sqrt-softplus scoring): exp(l - max l) or sqrt(softplus(l)), in double,
+// as route_row_impl computes them for its winners.  Then *ready is raised
+// to `mark` (workgroup scope, after the stores).
+__device__ __forceinline__ void row_unbiased_scores(const float (&v)[kPerLane], const RowSpec& s, double* u,
+                                                    int* ready, int mark)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool softmax = s.scoring == kSoftmax;
+    float mx = 0.0f;
+    if (softmax) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j)
+            if (lane * kPerLane + j < s.E) m = max(m, order_code(v[j]));
+        mx = order_value(wave_max_u32(m));
+    }
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const double x = softmax ? exp((double)v[j] - (double)mx) : sqrt_softplus(v[j]);
+        if (lane * kPerLane + j < s.E) u[lane * kPerLane + j] = x;
+    }
+    __hip_atomic_store(ready, mark, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// lds: kFilterCap entries owned by this wave (kFilter only).  ext_u,
+// ext_ready, ext_want: see route_row_impl (used only when the row needs no
+// score before its selection; ignored otherwise).
 template <RoundStyle kStyle = kRoundsLane>
 __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
                                                const float (&bv)[kPerLane], const RowSpec& s,
-                                               uint64_t* lds = nullptr)
+                                               uint64_t* lds = nullptr, const double* ext_u = nullptr,
+                                               int* ext_ready = nullptr, int ext_want = 0)
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
-    return need_all ? route_row_impl<true, kStyle>(v, bv, s, lds) : route_row_impl<false, kStyle>(v, bv, s, lds);
+    return need_all ? route_row_impl<true, kStyle>(v, bv, s, lds)
+                    : route_row_impl<false, kStyle>(v, bv, s, lds, ext_u, ext_ready, ext_want);
+}
+
+// Whether a row of this spec can take its winners' scores from
+// row_unbiased_scores() (no score is needed before the selection).
+__device__ __forceinline__ bool row_scores_after_selection(const RowSpec& s)
+{
+    return !(s.has_bias || (s.scoring == kSoftmax && !s.renorm));
 }
 
 // ---------------------------------------------------------------------------

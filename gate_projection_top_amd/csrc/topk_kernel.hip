@@ -15,6 +15,7 @@ constexpr int kTopkWaves = 4;
 
 __global__ __launch_bounds__(kTopkWaves * kWave) void topk_from_logits_kernel(TopkLaunch a)
 {
+    __shared__ uint64_t sel[kTopkWaves][kFilterCap];  // selection scratch, one per wave
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_from_logits_kernel(To
                 if (e < a.E) v[j] = r[e];
             }
         }
-        const RowResult res = route_row<kRoundsScalar>(v, bv, spec);  // several waves per SIMD
+        const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave]);
         if (lane < a.k) {
             a.inds[row * a.k + lane] = res.idx;
             a.weights[row * a.k + lane] = res.w;
