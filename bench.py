@@ -65,8 +65,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--section", choices=["all", "decode", "mxfp4", "mxfp8", "gather", "gemm1", "prefill", "topk",
-                                          "floor"],
+    ap.add_argument("--section", choices=["all", "decode", "widths", "mxfp4", "mxfp8", "gather", "gemm1", "prefill",
+                                          "topk", "floor"],
                     default="all",
                     help="restrict to one workload (for counter-collection runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -204,7 +204,7 @@ def main():
 
     if args.section in ("all", "decode"):
         decode_headline(torch, R, W, dev, args, out)
-    if args.section in ("all",):
+    if args.section in ("all", "widths"):
         out["extras"].update(decode_extras(torch, R, W, dev, args))
     if args.section in ("all", "floor"):
         out["extras"].update(floor_extras(torch, W, dev, args))

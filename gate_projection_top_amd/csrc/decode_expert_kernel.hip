@@ -11,7 +11,8 @@
 // (one 8-byte slot per token and expert, 1 KiB + tags per row) rather than
 // partial sums.
 //
-//   grid = E workgroups of kExpertWaves load waves + one control wave.
+//   grid = E workgroups of four load waves (eight above four tokens), one
+//   control wave and one warm-up wave.
 //   Control wave: draws the arrival ticket at kernel start, in two levels
 //     (groups of 16 workgroups, then the groups), so no counter sees more
 //     than 16 arrivals.  A group's counter word also carries the epoch of
@@ -49,8 +50,10 @@ namespace gpt {
 
 namespace {
 
-constexpr int kExpertThreads = kExpertWaves * kWave;
-constexpr int kExpertBatch = 4;  // 16-byte gate loads per thread issued together
+// Load waves per workgroup: four for up to four tokens, eight (one routing
+// wave per token) for more; 16-byte gate loads per thread issued together.
+template <int kRows> constexpr int kLoadWavesOf = kRows <= 4 ? 4 : 8;
+template <int kRows> constexpr int kBatchOf = kRows <= 4 ? 4 : 2;
 constexpr int kPollsInFlight = 3;
 constexpr int kPollGap = 2;       // s_sleep units (64 clocks) between polls
 
@@ -103,11 +106,9 @@ __device__ __forceinline__ u32x4v load16(const void* p) { return *reinterpret_ca
 // A launch's tag: odd, so never the cleared value 0.
 __device__ __forceinline__ uint32_t tag_of(uint64_t epoch) { return ((uint32_t)epoch << 1) | 1u; }
 
-// Waves of a workgroup: kExpertWaves load waves, then the control wave, then
-// the warm-up wave.
-constexpr int kControlWave = kExpertWaves;
-constexpr int kWarmWave = kExpertWaves + 1;
-constexpr int kExpertBlock = (kExpertWaves + 2) * kWave;
+// Waves of a workgroup: the load waves, then the control wave, then the
+// warm-up wave.
+template <int kRows> constexpr int kBlockOf = (kLoadWavesOf<kRows> + 2) * kWave;
 
 // Waits (sleeping) until the workgroup-shared word reaches `want`.
 __device__ __forceinline__ void wait_lds_at_least(int* w, int want)
@@ -116,9 +117,14 @@ __device__ __forceinline__ void wait_lds_at_least(int* w, int want)
 }
 
 template <int kRows, int kFmt>
-__global__ __launch_bounds__(kExpertBlock) void decode_expert_kernel(DecodeLaunch a)
+__global__ __launch_bounds__(kBlockOf<kRows>) void decode_expert_kernel(DecodeLaunch a)
 {
-    __shared__ float red[kExpertWaves][kRows];
+    constexpr int kLoadWaves = kLoadWavesOf<kRows>;
+    constexpr int kThreads = kLoadWaves * kWave;
+    constexpr int kBatch = kBatchOf<kRows>;
+    constexpr int kControlWave = kLoadWaves;
+    constexpr int kWarmWave = kLoadWaves + 1;
+    __shared__ float red[kLoadWaves][kRows];
     __shared__ uint64_t sel[kWarmWave + 1][kFilterCap];  // selection scratch, one per routing wave
     __shared__ int32_t slots[kWave];                      // route table: M*k <= 64 slots
     __shared__ int32_t tab_first[kMaxE + 1], tab_mask[kMaxE + 1];
@@ -197,12 +203,12 @@ __global__ __launch_bounds__(kExpertBlock) void decode_expert_kernel(DecodeLaunc
         if constexpr (kFmt == kGateBf16) {
             const int nu = a.H >> 3;  // 16-byte units per row
             const uint16_t* wrow = a.w + (int64_t)e * a.H;
-            for (int base = 0; base < nu; base += kExpertThreads * kExpertBatch) {
-                u32x4v wv[kExpertBatch];
-                u32x4v xv[kExpertBatch][kRows];
+            for (int base = 0; base < nu; base += kThreads * kBatch) {
+                u32x4v wv[kBatch];
+                u32x4v xv[kBatch][kRows];
 #pragma unroll
-                for (int i = 0; i < kExpertBatch; ++i) {
-                    const int u = base + i * kExpertThreads + tid;
+                for (int i = 0; i < kBatch; ++i) {
+                    const int u = base + i * kThreads + tid;
                     const bool in = u < nu;
                     wv[i] = in ? load16(wrow + 8 * u) : u32x4v{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(kExpertBlock) void decode_expert_kernel(DecodeLaunc
                         xv[i][t] = (in && t < M) ? load16(a.x + (int64_t)t * a.H + 8 * u) : u32x4v{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
-                for (int i = 0; i < kExpertBatch; ++i)
+                for (int i = 0; i < kBatch; ++i)
 #pragma unroll
                     for (int t = 0; t < kRows; ++t) acc[t] = dot8(xv[i][t], wv[i], acc[t]);
             }
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(kExpertBlock) void decode_expert_kernel(DecodeLaunc
             constexpr int kRowDiv = kFmt == kGateMxfp8 ? 1 : 2;
             const uint8_t* crow = a.w_codes + (int64_t)e * (a.H / kRowDiv);
             const uint8_t* srow = a.w_scale + (int64_t)e * (a.H / 32);
-            for (int base = 0; base < nu; base += kExpertThreads) {
+            for (int base = 0; base < nu; base += kThreads) {
                 const int u = base + tid;
                 const bool in = u < nu;
                 const int uc = in ? u : 0;  // a lane past the row reads unit 0 (in bounds) and adds nothing
@@ -276,13 +282,13 @@ __global__ __launch_bounds__(kExpertBlock) void decode_expert_kernel(DecodeLaunc
     const __amdgpu_buffer_rsrc_t srs =
         __builtin_amdgcn_make_buffer_rsrc(a.xslots, 0, M * kMaxE * 8, 0x00020000);
     if (wave == 0) {
-        wait_lds_at_least(&s_loaded, kExpertWaves);
+        wait_lds_at_least(&s_loaded, kLoadWaves);
         wait_lds_at_least(&s_ctl, 1);
         const uint32_t tag0 = s_tag;
         if (lane < M) {
             float l = red[0][lane];
 #pragma unroll
-            for (int w = 1; w < kExpertWaves; ++w) l += red[w][lane];
+            for (int w = 1; w < kLoadWaves; ++w) l += red[w][lane];
             const u32x2 v = {__float_as_uint(l), tag0};
             __builtin_amdgcn_raw_buffer_store_b64(v, srs, (lane * kMaxE + e) * 8, 0, kCoherent);
         }
@@ -395,9 +401,9 @@ __global__ __launch_bounds__(kExpertBlock) void decode_expert_kernel(DecodeLaunc
 hipError_t launch_decode_expert(const DecodeLaunch& a, hipStream_t stream)
 {
     if (a.M < 1 || a.M > kExpertMaxRows || a.E < 1 || a.E > kMaxE) return hipErrorInvalidValue;
-    const dim3 grid(a.E), block(kExpertBlock);
+    const dim3 grid(a.E);
 #define GPT_EXPERT_LAUNCH(ROWS, FMT) \
-    hipLaunchKernelGGL((decode_expert_kernel<ROWS, FMT>), grid, block, 0, stream, a)
+    hipLaunchKernelGGL((decode_expert_kernel<ROWS, FMT>), grid, dim3(kBlockOf<ROWS>), 0, stream, a)
 #define GPT_EXPERT_FORMATS(ROWS)                                                \
     if (a.w_format == kGateBf16) GPT_EXPERT_LAUNCH(ROWS, kGateBf16);            \
     else if (a.w_format == kGateMxfp4) GPT_EXPERT_LAUNCH(ROWS, kGateMxfp4);     \
@@ -407,8 +413,10 @@ hipError_t launch_decode_expert(const DecodeLaunch& a, hipStream_t stream)
         GPT_EXPERT_FORMATS(1)
     } else if (a.M == 2) {
         GPT_EXPERT_FORMATS(2)
-    } else {
+    } else if (a.M <= 4) {
         GPT_EXPERT_FORMATS(4)
+    } else {
+        GPT_EXPERT_FORMATS(8)
     }
 #undef GPT_EXPERT_FORMATS
 #undef GPT_EXPERT_LAUNCH

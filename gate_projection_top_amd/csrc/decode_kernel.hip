@@ -9,27 +9,40 @@
 // fast enough on its own.
 //
 //   grid = R row blocks x B expert blocks x S H-splits; each workgroup has
-//   kDecodeWaves load waves and one control wave.
-//   Start: the control wave draws an arrival ticket on the row block's
-//     counter.  The workgroups that draw the last F tickets are the row
-//     block's finishers (F > 1 when the block has more rows than a
-//     workgroup has waves to spare, each finisher taking every F-th row).
-//     No workgroup but a finisher ever waits, and the grid (at most 256
-//     workgroups) is resident at once, so the finishers' waits below always
-//     end.  The ticket's round trip overlaps the loads of phase 1.
+//   kLoadWaves load waves and one control wave.  (Up to kExpertMaxRows
+//   tokens take the one-expert-per-workgroup kernel instead.)
+//   Start: the control wave draws an arrival ticket, in two levels: on its
+//     expert block's word (S arrivals), then, for the last of those, on the
+//     row block's word (B arrivals).  The workgroups that draw the last F row
+//     tickets are the row block's finishers (F > 1 when the block has more
+//     rows than a workgroup has waves to spare, each finisher taking every
+//     F-th row).  An expert block's word also carries the row block's epoch
+//     in its upper bits: every workgroup learns it from its own ticket and
+//     tags the partials it publishes with it; the last arrival on a block
+//     word moves its epoch on while clearing its count, and the last finisher
+//     moves on the words of blocks this launch does not use, so all of a row
+//     block's words keep one epoch.  The ticket's round trip overlaps the
+//     loads of phase 1.
 //   Phase 1 (every workgroup): the 16x16 (tokens x experts) partial dot
 //     products over its H-split, one bf16 MFMA 16x16x32 per 32-wide k-step,
 //     every wave's loads issued before its first MFMA; the waves' partials
-//     summed in LDS in wave order and published with device-coherent 16-byte
-//     stores.  Non-finishers are then done: no wait for the stores.
-//   Phase 2 (finisher): every partial slot holds a signalling-NaN sentinel
-//     between launches, and arithmetic never produces that bit pattern, so
-//     a slot holding anything else has been published.  Each wave takes rows
-//     of the block; lane L polls the S partials of experts 4L..4L+3 (the
-//     routing layout itself) until none is the sentinel, resets those slots
-//     to the sentinel, adds the partials in split order and routes the row
-//     with route_row(); the unique-route table, when asked for, follows.  The finisher
-//     also resets the counter, so the kernel replays inside a HIP graph.
+//     summed in LDS in wave order and published as (value, tag) pairs with
+//     device-coherent stores.  Non-finishers are then done.
+//   Phase 2 (finisher): each wave takes rows of the block; lane L polls the
+//     S partials of experts 4L..4L+3 (the routing layout itself) until all
+//     carry this launch's tag, adds them in split order and routes the row
+//     with route_row(); a helper wave clears the slots' tags afterwards (tag
+//     0, which no launch uses); the unique-route table, when asked for,
+//     follows.  Counters return to zero and epochs move on, so the kernel
+//     replays inside a HIP graph.
+//   The last finisher's wait always ends (every workgroup of its row block
+//     has drawn a ticket, so all have started, and none waits).  A finisher
+//     that is not the last waits for workgroups that may not have started
+//     yet; they start as soon as any CU frees a slot, since no workgroup of
+//     this kernel but the finishers ever waits.  Every wait is bounded all
+//     the same (wait_ticks): a row given up comes out as index -1 with a NaN
+//     weight and sets kStatusWaitLimit, and the slots it leaves behind carry
+//     an older tag, so no later launch takes them for its own.
 //
 // Every logit is accumulated in the same order regardless of its expert
 // index, so two experts with identical gate rows get bitwise-equal logits and
@@ -43,54 +56,51 @@ namespace gpt {
 namespace {
 
 constexpr int kChunk = 8;      // k-steps whose loads a wave issues before its MFMAs
-constexpr int kPollGap = 16;   // s_sleep units (64 clocks) between the two polls in flight
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float not_sentinel(float v)
-{
-    // a quiet NaN stands in for the (never produced) sentinel pattern
-    return __float_as_uint(v) == kPartialSentinel ? __uint_as_float(0x7fc00000u) : v;
-}
+// A launch's tag: odd, so never the cleared value 0.
+__device__ __forceinline__ uint32_t partial_tag(uint64_t epoch) { return ((uint32_t)epoch << 1) | 1u; }
 
-__device__ __forceinline__ bool published(f32x4 v)
-{
-    // bitwise, not short-circuit: one compare per value, no branches
-    const int p0 = __float_as_uint(v[0]) != kPartialSentinel, p1 = __float_as_uint(v[1]) != kPartialSentinel;
-    const int p2 = __float_as_uint(v[2]) != kPartialSentinel, p3 = __float_as_uint(v[3]) != kPartialSentinel;
-    return (p0 & p1 & p2 & p3) != 0;
-}
-
-// One poll: every split's slot of this lane's four experts.  Splits q >= S
-// lie past the end of the buffer range, so their loads return zeros without
-// touching memory.  The empty asm keeps the loads from being hoisted out of
-// the polling loop.
+// One poll: every split's (value, tag) pairs of this lane's four experts, two
+// 16-byte loads per split.  Splits q >= S lie past the end of the buffer
+// range: their loads return zeros without touching memory.  The empty asm
+// keeps the loads from being hoisted out of the polling loop.
 template <int kMaxS>
-__device__ __forceinline__ void poll_issue(f32x4 (&p)[kMaxS], __amdgpu_buffer_rsrc_t prs, int off,
+__device__ __forceinline__ void poll_issue(u32x4 (&p)[kMaxS][2], __amdgpu_buffer_rsrc_t prs, int off,
                                            int qstride)
 {
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < kMaxS; ++q) p[q] = fetch4(prs, off + q * qstride);
+    for (int q = 0; q < kMaxS; ++q) {
+        p[q][0] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + q * qstride, 0, kCoherent);
+        p[q][1] = __builtin_amdgcn_raw_buffer_load_b128(prs, off + q * qstride + 16, 0, kCoherent);
+    }
 }
 
-// True when no lane that owns published slots still sees the sentinel.
+// True when every lane that owns published slots sees this launch's tag in
+// all of them (splits q < S).
 template <int kMaxS>
-__device__ __forceinline__ bool poll_ready(const f32x4 (&p)[kMaxS], bool mine)
+__device__ __forceinline__ bool poll_ready(const u32x4 (&p)[kMaxS][2], bool mine, int S, uint32_t tag)
 {
-    bool ok = true;
+    int ok = 1;  // bitwise, not short-circuit: no branch per slot
 #pragma unroll
-    for (int q = 0; q < kMaxS; ++q) ok &= published(p[q]);
-    return __builtin_amdgcn_ballot_w64(mine && !ok) == 0;
+    for (int q = 0; q < kMaxS; ++q)
+        ok &= (int)(q >= S) | ((int)(p[q][0][1] == tag) & (int)(p[q][0][3] == tag) & (int)(p[q][1][1] == tag) &
+                               (int)(p[q][1][3] == tag));
+    return __builtin_amdgcn_ballot_w64(mine && ok == 0) == 0;
 }
 
 // The logit: partials added in split order (zeros past S change nothing).
 template <int kMaxS>
-__device__ __forceinline__ f32x4 poll_sum(const f32x4 (&p)[kMaxS])
+__device__ __forceinline__ f32x4 poll_sum(const u32x4 (&p)[kMaxS][2])
 {
-    f32x4 sum = p[0];
+    f32x4 sum = {__uint_as_float(p[0][0][0]), __uint_as_float(p[0][0][2]), __uint_as_float(p[0][1][0]),
+                 __uint_as_float(p[0][1][2])};
 #pragma unroll
-    for (int q = 1; q < kMaxS; ++q) sum += p[q];
+    for (int q = 1; q < kMaxS; ++q)
+        sum += f32x4{__uint_as_float(p[q][0][0]), __uint_as_float(p[q][0][2]), __uint_as_float(p[q][1][0]),
+                     __uint_as_float(p[q][1][2])};
     return sum;
 }
 
@@ -106,6 +116,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     __shared__ int32_t tab_first[kMaxE + 1], tab_mask[kMaxE + 1];
     __shared__ int polled[kDecodeTile];  // finisher: 1 = row's partials read, 2 = row gave up
     __shared__ int fin_index;  // this workgroup's finisher index, -1: not a finisher
+    __shared__ uint32_t s_tag;  // this launch's tag (row block epoch)
     __shared__ uint64_t sel[kWaves][kFilterCap];  // selection scratch, one per routing wave
 
     const int tid = threadIdx.x;
@@ -133,7 +144,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     // rows in one workgroup: one finisher then.)
     const int t0 = r * kDecodeTile;
     const int rows_here = min(kDecodeTile, a.M - t0);
-    const int nfin = a.table_ids ? 1 : min(B, max(1, (rows_here + kWaves - 2) / (kWaves - 1)));
+    const int nfin = a.table_ids ? 1 : min(B, rows_here);
 
     if (tid < kDecodeTile) polled[tid] = 0;
     if (wave == kLoadWaves) {
@@ -144,16 +155,27 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         // load wave.  Each counter is reset by the workgroup that drew its
         // last ticket, when every ticket on it has been drawn.
         if (lane == 0) {
-            uint32_t* block_ctr = a.counters + kDecodeCounterStride * (r * kDecodeMaxBlocks + b);
-            uint32_t* row_ctr = a.counters + kDecodeCounterStride * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + r);
+            // 8-byte words, one 64-byte line apart: (epoch << 8 | count) per
+            // (row block, expert block), then a count per row block
+            uint64_t* words = reinterpret_cast<uint64_t*>(a.counters);
+            constexpr int kW = kDecodeCounterStride / 2;
+            uint64_t* block_w = words + kW * (r * kDecodeMaxBlocks + b);
+            uint64_t* row_w = words + kW * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + r);
             int fin = -1;
-            if (__hip_atomic_fetch_add(block_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)a.S - 1u) {
-                __hip_atomic_store(block_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t rt = __hip_atomic_fetch_add(row_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (rt == (uint32_t)B - 1u)
-                    __hip_atomic_store(row_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (rt >= (uint32_t)(B - nfin)) fin = (int)rt - (B - nfin);
+            const uint64_t old = __hip_atomic_fetch_add(block_w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_tag = partial_tag(old >> 8);
+            if ((int)(old & 0xffu) == a.S - 1) {
+                // last of the block: next epoch, count back to zero
+                __hip_atomic_fetch_add(block_w, (1ull << 8) - (uint64_t)a.S, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t rt = __hip_atomic_fetch_add(row_w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((int)rt == B - 1) {
+                    __hip_atomic_store(row_w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int u = B; u < kDecodeMaxBlocks; ++u)
+                        __hip_atomic_fetch_add(words + kW * (r * kDecodeMaxBlocks + u), 1ull << 8, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if ((int)rt >= B - nfin) fin = (int)rt - (B - nfin);
             }
             fin_index = fin;
         }
@@ -269,23 +291,30 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     __syncthreads();
 
     // ---- publish: wave 0 sums the load waves' partials (wave order) and
-    // stores them device-coherently (lane l: token row l/4, experts
-    // 4(l%4)..+3 of the block).  Layout [S][M][256] fp32.
-    const int qstride = a.M * kMaxE * 4;  // bytes per split
+    // stores them with the tag, device-coherently (lane l: token row l/4,
+    // experts 4(l%4)..+3 of the block).  Layout [S][M][256] (value, tag).
+    const int qstride = a.M * kMaxE * 8;  // bytes per split
     const __amdgpu_buffer_rsrc_t prs =
         __builtin_amdgcn_make_buffer_rsrc(a.partials, 0, a.S * qstride, 0x00020000);
+    const uint32_t tag = s_tag;  // written by the control wave before the barrier
     if (wave == 0) {
         const int rr = lane >> 2, cc = (lane & 3) * 4;
-        f32x4 sum;
+        float sum[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float v = red[0][rr][cc + j];
 #pragma unroll
             for (int w = 1; w < kLoadWaves; ++w) v += red[w][rr][cc + j];
-            sum[j] = not_sentinel(v);
+            sum[j] = v;
         }
         const int row = r * kDecodeTile + rr;
-        if (row < a.M) publish4(prs, s * qstride + (row * kMaxE + b * kDecodeTile + cc) * 4, sum);
+        if (row < a.M) {
+            const int off = s * qstride + (row * kMaxE + b * kDecodeTile + cc) * 8;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(sum[0]), tag, __float_as_uint(sum[1]), tag},
+                                                   prs, off, 0, kCoherent);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(sum[2]), tag, __float_as_uint(sum[3]), tag},
+                                                   prs, off + 16, 0, kCoherent);
+        }
     }
     const int f = fin_index;  // written by the control wave before the barrier
     if (f < 0) return;
@@ -295,8 +324,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     const int nrows = (rows_here - f + nfin - 1) / nfin;  // this finisher's rows
     const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};
     const bool mine = lane < 4 * B;  // the lane's expert group lies in a published block
-    const f32x4 sentinel4 = __builtin_bit_cast(f32x4, u32x4{kPartialSentinel, kPartialSentinel,
-                                                            kPartialSentinel, kPartialSentinel});
+    const u32x4 cleared = {0u, 0u, 0u, 0u};
     // bias beyond E reads as 0 (out-of-range buffer loads return zero)
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
@@ -308,9 +336,9 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     // to call, so its routing code is usually not in that CU's instruction
     // cache, and this wave, running ahead, fetches it while the row waves
     // are still polling.  (One wave only: dummy passes share SIMDs with the
-    // real rows.)  The next free wave, if there is one, puts the sentinel
-    // back into each row's slots once the row's wave has read them, so the
-    // row waves go straight from their poll to routing.
+    // real rows.)  The next free wave, if there is one, clears the tags of
+    // each row's slots once the row's wave has read them, so the row waves
+    // go straight from their poll to routing.
     const int slot_of_wave = (wave + kWaves - 1) % kWaves;  // row t goes to wave (t + 1) % kWaves
     const int my_rows = slot_of_wave < nrows ? (nrows - slot_of_wave + kWaves - 1) / kWaves : 0;
     const int passes = my_rows > 0 ? my_rows : (slot_of_wave == nrows ? 1 : 0);
@@ -322,12 +350,15 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
             // the row waves' own poll limit bounds this wait; the doubled
             // limit here is only a guard
             while ((st = __hip_atomic_load(&polled[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0 &&
-                   __builtin_amdgcn_s_memrealtime() - t_wait < 2 * kDecodePollLimitTicks)
+                   __builtin_amdgcn_s_memrealtime() - t_wait < 2ull * a.wait_ticks)
                 __builtin_amdgcn_s_sleep(1);
             if (st == 1 && mine) {
-                const int off = ((t0 + f + nfin * t) * kMaxE + lane * kPerLane) * 4;
+                const int off = ((t0 + f + nfin * t) * kMaxE + lane * kPerLane) * 8;
 #pragma unroll
-                for (int q = 0; q < kMaxS; ++q) publish4(prs, off + q * qstride, sentinel4);
+                for (int q = 0; q < kMaxS; ++q) {
+                    __builtin_amdgcn_raw_buffer_store_b128(cleared, prs, off + q * qstride, 0, kCoherent);
+                    __builtin_amdgcn_raw_buffer_store_b128(cleared, prs, off + q * qstride + 16, 0, kCoherent);
+                }
             }
         }
     }
@@ -338,55 +369,32 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         float v[kPerLane];
         float bv[kPerLane] = {0.f, 0.f, 0.f, 0.f};
         if (real) {
-            const int off = ((t0 + t) * kMaxE + lane * kPerLane) * 4;
+            const int off = ((t0 + t) * kMaxE + lane * kPerLane) * 8;
             // Splits q >= S lie past the end of the buffer range: their loads
-            // return zeros and their stores are dropped, so no branch on S.
-            // The wait ends once the publishers' stores land; the time limit is
-            // only a guard so that no wave can spin forever: a row that hits it
-            // is reported as index -1 with a NaN weight.
+            // return zeros (and are not examined) and their stores are
+            // dropped.  The wait ends once the publishers' stores land; the
+            // time limit only bounds it: a row that reaches it is reported as
+            // index -1 with a NaN weight.
             f32x4 sum;
             const uint64_t t_poll = __builtin_amdgcn_s_memrealtime();
             bool gave_up = false;
-            if constexpr (kMaxS <= 8) {
-                // Two polls stay in flight, half a round trip apart, so a
-                // partial that lands is seen about a quarter round trip
-                // sooner on average.  (At 16 splits the second poll's
-                // registers would spill.)
-                f32x4 p0[kMaxS], p1[kMaxS];
+            u32x4 p0[kMaxS][2];
+            for (;;) {
                 poll_issue<kMaxS>(p0, prs, off, qstride);
-                __builtin_amdgcn_s_sleep(kPollGap);
-                for (;;) {
-                    poll_issue<kMaxS>(p1, prs, off, qstride);
-                    if (poll_ready<kMaxS>(p0, mine)) {
-                        sum = poll_sum<kMaxS>(p0);
-                        break;
-                    }
-                    poll_issue<kMaxS>(p0, prs, off, qstride);
-                    if (poll_ready<kMaxS>(p1, mine)) {
-                        sum = poll_sum<kMaxS>(p1);
-                        break;
-                    }
-                    if (__builtin_amdgcn_s_memrealtime() - t_poll > kDecodePollLimitTicks) {
-                        gave_up = true;
-                        break;
-                    }
+                if (poll_ready<kMaxS>(p0, mine, a.S, tag)) {
+                    sum = poll_sum<kMaxS>(p0);
+                    break;
                 }
-            } else {
-                f32x4 p0[kMaxS];
-                for (;;) {
-                    poll_issue<kMaxS>(p0, prs, off, qstride);
-                    if (poll_ready<kMaxS>(p0, mine)) {
-                        sum = poll_sum<kMaxS>(p0);
-                        break;
-                    }
-                    if (__builtin_amdgcn_s_memrealtime() - t_poll > kDecodePollLimitTicks) {
-                        gave_up = true;
-                        break;
-                    }
+                if (__builtin_amdgcn_s_memrealtime() - t_poll > a.wait_ticks) {
+                    gave_up = true;
+                    break;
                 }
             }
             if (gave_up) {
-                if (lane == 0) __hip_atomic_store(&polled[i], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (lane == 0) {
+                    __hip_atomic_store(&polled[i], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_fetch_or(a.status, kStatusWaitLimit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                }
                 if (lane < a.k) {
                     const int64_t o = (int64_t)(t0 + t) * a.k + lane;
                     a.inds[o] = -1;
@@ -399,7 +407,10 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                 if (lane == 0) __hip_atomic_store(&polled[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             } else if (mine) {
 #pragma unroll
-                for (int q = 0; q < kMaxS; ++q) publish4(prs, off + q * qstride, sentinel4);
+                for (int q = 0; q < kMaxS; ++q) {
+                    __builtin_amdgcn_raw_buffer_store_b128(cleared, prs, off + q * qstride, 0, kCoherent);
+                    __builtin_amdgcn_raw_buffer_store_b128(cleared, prs, off + q * qstride + 16, 0, kCoherent);
+                }
             }
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
@@ -447,18 +458,15 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream)
     const int R = (a.M + kDecodeTile - 1) / kDecodeTile;
     const int B = (a.E + kDecodeTile - 1) / kDecodeTile;
     const int grid = R * B * a.S;
-    const bool narrow = a.load_waves == kDecodeNarrow.load_waves && a.S <= kDecodeNarrow.max_splits;
-    const bool wide = a.load_waves == kDecodeWide.load_waves && a.S <= kDecodeWide.max_splits;
-    const dim3 nb((kDecodeNarrow.load_waves + 1) * kWave), wb((kDecodeWide.load_waves + 1) * kWave);
-#define GPT_DECODE_LAUNCH(GEO, FMT, BLOCK)                                                           \
-    hipLaunchKernelGGL((decode_router_kernel<GEO.load_waves, GEO.max_splits, FMT>), dim3(grid), BLOCK, 0, \
-                       stream, a)
-    if (narrow && a.w_format == kGateBf16) GPT_DECODE_LAUNCH(kDecodeNarrow, kGateBf16, nb);
-    else if (narrow && a.w_format == kGateMxfp4) GPT_DECODE_LAUNCH(kDecodeNarrow, kGateMxfp4, nb);
-    else if (narrow && a.w_format == kGateMxfp8) GPT_DECODE_LAUNCH(kDecodeNarrow, kGateMxfp8, nb);
-    else if (wide && a.w_format == kGateBf16) GPT_DECODE_LAUNCH(kDecodeWide, kGateBf16, wb);
-    else if (wide && a.w_format == kGateMxfp4) GPT_DECODE_LAUNCH(kDecodeWide, kGateMxfp4, wb);
-    else if (wide && a.w_format == kGateMxfp8) GPT_DECODE_LAUNCH(kDecodeWide, kGateMxfp8, wb);
+    if (a.load_waves != kDecodeWide.load_waves || a.S > kDecodeWide.max_splits || a.S < 1)
+        return hipErrorInvalidValue;
+    const dim3 wb((kDecodeWide.load_waves + 1) * kWave);
+#define GPT_DECODE_LAUNCH(FMT)                                                                           \
+    hipLaunchKernelGGL((decode_router_kernel<kDecodeWide.load_waves, kDecodeWide.max_splits, FMT>), dim3(grid), \
+                       wb, 0, stream, a)
+    if (a.w_format == kGateBf16) GPT_DECODE_LAUNCH(kGateBf16);
+    else if (a.w_format == kGateMxfp4) GPT_DECODE_LAUNCH(kGateMxfp4);
+    else if (a.w_format == kGateMxfp8) GPT_DECODE_LAUNCH(kGateMxfp8);
     else return hipErrorInvalidValue;
 #undef GPT_DECODE_LAUNCH
     return hipGetLastError();

@@ -37,11 +37,12 @@ struct DecodeLaunch {
     int32_t* table_mask;
     int32_t* table_s2u;
     int32_t* table_count;
-    float* partials;        // workspace [S][M][256], every slot kPartialSentinel between calls
-    uint32_t* counters;     // workspace, kDecodeCounters words, zero between calls
+    float* partials;        // workspace [S][M][256] (value, tag) pairs, zero-filled at init
+    uint32_t* counters;     // workspace, kDecodeCounters words (8-byte words for the
+                            // split kernel: epoch << 8 | count), zero-filled at init
     int S;                  // H splits
     int ks_per_split;       // k units per split: 32-wide k-steps (bf16 gate), 128-wide blocks (MX)
-    int load_waves;         // geometry: kDecodeNarrow.load_waves or kDecodeWide.load_waves
+    int load_waves;         // geometry: kDecodeWide.load_waves
     // one-expert-per-workgroup kernel (M <= kExpertMaxRows)
     uint32_t* xslots;       // workspace [kExpertMaxRows][256] (logit bits, tag) pairs, tag 0 between calls
     uint64_t* xcounters;    // workspace, kExpertCounterWords words: group words (epoch << 8 | count)
@@ -105,27 +106,24 @@ int prefill_splits(int64_t M);
 
 // Decode geometry shared by the host (workspace sizing) and the launcher.
 constexpr int kDecodeTile = 16;        // rows per row block, experts per expert block
-constexpr int kDecodeMaxSplits = 16;   // H splits (either geometry)
+constexpr int kDecodeMaxSplits = 8;    // H splits
 constexpr int kDecodeMaxM = 64;
 constexpr int kDecodeMaxRowBlocks = kDecodeMaxM / kDecodeTile;
 constexpr int kDecodeMaxBlocks = 256 / kDecodeTile;  // expert blocks at E = 256
-// Arrival counters, one 64-byte line apart: per (row block, expert block),
-// then per row block.
+// Arrival counters, one 64-byte line (16 4-byte words) apart: per (row
+// block, expert block), then per row block.
 constexpr int kDecodeCounterStride = 16;
 constexpr int kDecodeCounters =
     kDecodeCounterStride * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + kDecodeMaxRowBlocks);
-// Empty decode partial slot: a signalling NaN, a pattern no arithmetic
-// result has (NaN results are quiet).
-constexpr uint32_t kPartialSentinel = 0x7f800001u;
-// Guard on the finisher's wait for published partials (100 MHz realtime
-// clock): 100 ms, orders of magnitude above any real wait.
-constexpr uint64_t kDecodePollLimitTicks = 10000000u;
 
 // One-expert-per-workgroup decode kernel: token counts up to kExpertMaxRows;
 // arrival counters for groups of kExpertGroup workgroups, one 64-byte line
 // (kExpertCounterStride 8-byte words) apart, then the group counter.
-constexpr int kExpertMaxRows = 4;
-constexpr int kExpertWaves = 4;
+constexpr int kExpertMaxRows = 8;
+// From this many tokens on, router_fwd without a table takes the H-split
+// kernel (measured: at 8 tokens it is 6.1 us against 7.5 us here, when each
+// of its rows gets a finisher of its own; the table needs one finisher).
+constexpr int kExpertSplitMinRows = 5;
 constexpr int kExpertGroup = 16;
 constexpr int kExpertGroups = 256 / kExpertGroup;
 constexpr int kExpertCounterStride = 8;
@@ -135,25 +133,16 @@ constexpr uint32_t kStatusWaitLimit = 1u;  // a finisher stopped waiting at the 
 // Default bound on a decode finisher's wait: 100 ms (100 MHz realtime clock).
 constexpr uint32_t kDecodeWaitTicksDefault = 10000000u;
 
-// Two decode geometries.  A row block with at most kDecodeNarrowMaxRows
-// tokens takes about 256 workgroups of 3 load waves: more CUs pull W (each
-// CU keeps only so many misses in flight), fewer waves to dispatch, and the
-// finisher has few rows to route.  More rows take about 128 workgroups of 8
-// load waves, so the finisher has enough waves to route 16 rows.  Each
-// workgroup also has one control wave (which routes a row too).  Sweeps of
-// 2/3/4 and 4/8/16 load waves and 64/128/256 workgroups chose these.
+// Split decode geometry (more than kExpertMaxRows tokens): about 128
+// workgroups of 8 load waves, so the finisher has enough waves to route 16
+// rows; each workgroup also has one control wave (which routes a row too).
+// Sweeps of 4/6/7/8/16 load waves and 64/128/256 workgroups chose these.
 struct DecodeGeometry {
     int load_waves;
     int target_workgroups;
     int max_splits;
 };
-constexpr DecodeGeometry kDecodeNarrow{3, 256, 16};
-constexpr DecodeGeometry kDecodeWide{8, 128, 8};
-constexpr int kDecodeNarrowMaxRows = 4;
-inline DecodeGeometry decode_geometry(int M)
-{
-    return M <= kDecodeNarrowMaxRows ? kDecodeNarrow : kDecodeWide;
-}
+constexpr DecodeGeometry kDecodeWide{8, 128, kDecodeMaxSplits};
 
 // Prefill geometry: 128-row tiles; K split S ways while tiles * S <= 256.
 constexpr int kPrefillTileRows = 128;

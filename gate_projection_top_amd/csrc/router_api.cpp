@@ -11,7 +11,7 @@
 namespace {
 
 struct DeviceWorkspace {
-    float* partials = nullptr;          // decode H-split partial logits [S][M][256], sentinel-filled
+    float* partials = nullptr;          // decode H-split partial logits [S][M][256] (value, tag), zero-filled
     uint32_t* counters = nullptr;       // decode arrival counters (two levels)
     uint32_t* xslots = nullptr;         // one-expert decode: tagged logit slots, zero-filled
     uint64_t* xcounters = nullptr;      // one-expert decode: epoch/arrival words, zero-filled
@@ -22,7 +22,7 @@ struct DeviceWorkspace {
 
 constexpr int kMaxDevices = 64;
 constexpr size_t kPartialFloats =
-    (size_t)gpt::kDecodeMaxSplits * gpt::kDecodeMaxM * ROUTER_MAX_E;  // 1 MiB
+    (size_t)gpt::kDecodeMaxSplits * gpt::kDecodeMaxM * ROUTER_MAX_E * 2;  // (value, tag) pairs: 1 MiB
 constexpr int kCounters = gpt::kDecodeCounters;
 constexpr size_t kPfPartialFloats =
     (size_t)gpt::kPrefillMaxPairs * gpt::kPrefillTileRows * ROUTER_MAX_E;  // 32 MiB
@@ -57,8 +57,7 @@ int init_device(int dev)
     if (e == hipSuccess) e = hipMemset(ws.xslots, 0, kXSlotWords * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(ws.xcounters, 0, gpt::kExpertCounterWords * sizeof(uint64_t));
     if (e == hipSuccess) e = hipMemset(ws.status, 0, sizeof(uint32_t));
-    if (e == hipSuccess)
-        e = hipMemsetD32((hipDeviceptr_t)ws.partials, (int)gpt::kPartialSentinel, kPartialFloats);
+    if (e == hipSuccess) e = hipMemset(ws.partials, 0, kPartialFloats * sizeof(float));
     if (e == hipSuccess) e = hipMemset(ws.counters, 0, kCounters * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(ws.pf_counters, 0, kPfCounters * sizeof(uint32_t));
     // The counters must read zero before any stream (blocking or not) runs a
@@ -118,7 +117,7 @@ int check_projection(const void* x, const void* w)
 // wave in every split.
 void decode_splits(int M, int KS, int E, int* S_out, int* ks_per_split_out, int* load_waves_out)
 {
-    const gpt::DecodeGeometry g = gpt::decode_geometry(M);
+    const gpt::DecodeGeometry g = gpt::kDecodeWide;
     const int R = (M + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int B = (E + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     int S = (g.target_workgroups + R * B - 1) / (R * B);
@@ -169,7 +168,10 @@ int run_fused(const void* x, const void* w, int format, const uint8_t* w_codes, 
         a.xcounters = ws.xcounters;
         a.status = ws.status;
         a.wait_ticks = g_decode_wait_ticks.load(std::memory_order_relaxed);
-        if (M <= gpt::kExpertMaxRows) {
+        // One gate row per workgroup up to kExpertSplitMinRows - 1 tokens, and
+        // for the route table up to kExpertMaxRows (its rows must meet in one
+        // finisher); the H-split kernel otherwise, one finisher per row.
+        if (M < gpt::kExpertSplitMinRows || (t_ids && M <= gpt::kExpertMaxRows)) {
             e = gpt::launch_decode_expert(a, stream);
         } else {
             const int units = format != gpt::kGateBf16 ? (H + 127) / 128 : (H + 31) / 32;

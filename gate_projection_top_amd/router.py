@@ -35,7 +35,9 @@ DECODE_MAX_M = 64
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
            "router_fwd_mxfp4", "router_fwd_mxfp8", "router_topk_from_logits", "router_gather_shared_add",
            "router_gather_shared_add_table", "router_expert_gemm1_table",
-           "router_set_exchange_timeout_us", "router_strerror")
+           "router_set_exchange_timeout_us", "router_set_decode_wait_limit_us", "router_status",
+           "router_strerror")
+STATUS_WAIT_LIMIT = 1  # ROUTER_STATUS_WAIT_LIMIT: a decode finisher gave a row up
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -80,6 +82,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_topk_from_logits.restype = i32
     lib.router_set_exchange_timeout_us.argtypes = [i32]
     lib.router_set_exchange_timeout_us.restype = i32
+    lib.router_set_decode_wait_limit_us.argtypes = [i32]
+    lib.router_set_decode_wait_limit_us.restype = i32
+    lib.router_status.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_uint32)]
+    lib.router_status.restype = i32
     lib.router_strerror.argtypes = [i32]
     lib.router_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -125,6 +131,20 @@ def init(device: Optional[int] = None):
 def set_exchange_timeout_us(microseconds: int):
     """Bounded wait of a prefill K split for its siblings (0 forces the hand-over path)."""
     _check(load().router_set_exchange_timeout_us(int(microseconds)), "router_set_exchange_timeout_us")
+
+
+def set_decode_wait_limit_us(microseconds: int):
+    """Bound on a decode finisher's wait for the published logits (0 gives
+    every row up unless its logits are already in place at the first look)."""
+    _check(load().router_set_decode_wait_limit_us(int(microseconds)), "router_set_decode_wait_limit_us")
+
+
+def status(device: Optional[int] = None, clear: bool = False) -> int:
+    """The device's sticky status bits (synchronises the device first)."""
+    dev = -1 if device is None else int(device)
+    flags = ctypes.c_uint32(0)
+    _check(load().router_status(dev, int(bool(clear)), ctypes.byref(flags)), "router_status")
+    return int(flags.value)
 
 
 def _outputs(M: int, k: int, E: int, device, out_inds, out_weights, want_logits, logits_out):

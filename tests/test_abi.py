@@ -79,6 +79,16 @@ def test_exchange_timeout_validation(lib):
     assert lib.router_set_exchange_timeout_us(200) == R.OK
 
 
+def test_decode_wait_limit_validation(lib):
+    assert lib.router_set_decode_wait_limit_us(-1) == R.ERR_INVALID_ARGUMENT
+    assert lib.router_set_decode_wait_limit_us(100000) == R.OK
+
+
+def test_status_needs_an_output_pointer(lib):
+    assert lib.router_status(0, 0, None) == R.ERR_INVALID_ARGUMENT
+    assert lib.router_status(1 << 20, 0, ctypes.byref(ctypes.c_uint32())) == R.ERR_INVALID_ARGUMENT
+
+
 def test_router_fwd_empty_batch_is_ok_without_pointers(lib):
     assert lib.router_fwd(None, None, None, 0, 4096, 256, 8, 0, 1, None, None, None, None) == R.OK
 
