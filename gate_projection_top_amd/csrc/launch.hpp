@@ -120,10 +120,11 @@ constexpr int kDecodeCounters =
 // arrival counters for groups of kExpertGroup workgroups, one 64-byte line
 // (kExpertCounterStride 8-byte words) apart, then the group counter.
 constexpr int kExpertMaxRows = 8;
-// From this many tokens on, router_fwd without a table takes the H-split
-// kernel (measured: at 8 tokens it is 6.1 us against 7.5 us here, when each
-// of its rows gets a finisher of its own; the table needs one finisher).
-constexpr int kExpertSplitMinRows = 5;
+// From this many tokens on, router_fwd takes the H-split kernel.  (At 8
+// tokens that kernel measured 6.1 us against 7.5 us here, with one finisher
+// per row; but the route table needs all rows in one finisher, and both
+// calls must give the same bytes, so both stay here up to kExpertMaxRows.)
+constexpr int kExpertSplitMinRows = kExpertMaxRows + 1;
 constexpr int kExpertGroup = 16;
 constexpr int kExpertGroups = 256 / kExpertGroup;
 constexpr int kExpertCounterStride = 8;

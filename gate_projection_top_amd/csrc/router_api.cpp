@@ -168,10 +168,10 @@ int run_fused(const void* x, const void* w, int format, const uint8_t* w_codes, 
         a.xcounters = ws.xcounters;
         a.status = ws.status;
         a.wait_ticks = g_decode_wait_ticks.load(std::memory_order_relaxed);
-        // One gate row per workgroup up to kExpertSplitMinRows - 1 tokens, and
-        // for the route table up to kExpertMaxRows (its rows must meet in one
-        // finisher); the H-split kernel otherwise, one finisher per row.
-        if (M < gpt::kExpertSplitMinRows || (t_ids && M <= gpt::kExpertMaxRows)) {
+        // One gate row per workgroup up to kExpertMaxRows tokens (with or
+        // without the route table, so both give the same bytes); the H-split
+        // kernel above, one finisher per row.
+        if (M < gpt::kExpertSplitMinRows) {
             e = gpt::launch_decode_expert(a, stream);
         } else {
             const int units = format != gpt::kGateBf16 ? (H + 127) / 128 : (H + 31) / 32;
