@@ -42,6 +42,8 @@
 // landed later) carries an older tag and is never taken for this launch's.
 // A finisher that reaches the limit writes index -1 and a NaN weight for the
 // row and sets kStatusWaitLimit in the workspace's sticky status word.
+#include <mutex>
+
 #include "coherent.hpp"
 #include "launch.hpp"
 #include "route_common.hpp"
@@ -421,6 +423,67 @@ hipError_t launch_decode_expert(const DecodeLaunch& a, hipStream_t stream)
 #undef GPT_EXPERT_FORMATS
 #undef GPT_EXPERT_LAUNCH
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free entry: the kernel's workspace in static device memory
+// ---------------------------------------------------------------------------
+// Tagged logit slots, arrival words and the status word of the one-expert
+// kernel for up to kNoAllocMaxRows tokens, in one array per device that the
+// code object defines (zero when the library loads, which is the kernel's
+// starting state: tag 0 is no launch's, every counter at zero).  Host code
+// never uses the array's name as an address: each device's copy is resolved
+// once with hipGetSymbolAddress (with that device current) and that pointer
+// is what the kernel gets.  The array persists until the process ends; every
+// call on a device shares it (overlapping calls on one device race).
+constexpr size_t kNoAllocSlotBytes = (size_t)kNoAllocMaxRows * kMaxE * 8;
+constexpr size_t kNoAllocCounterBytes = (size_t)kExpertCounterWords * 8;
+constexpr size_t kNoAllocBytes = kNoAllocSlotBytes + kNoAllocCounterBytes + 256;  // + the status word
+static_assert(kNoAllocSlotBytes % 256 == 0 && kNoAllocCounterBytes % 8 == 0, "scratch layout alignment");
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+constexpr int kNoAllocDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kNoAllocDevices] = {};
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return kNoAllocBytes; }
+
+hipError_t noalloc_scratch(int device, void** out)
+{
+    if (device < 0 || device >= kNoAllocDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(g_scratch_mutex);
+    if (!g_scratch_ptr[device]) {
+        int prev = -1;
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess) return e;
+        if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (prev != device) (void)hipSetDevice(prev);
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
+hipError_t launch_decode_expert_noalloc(DecodeLaunch a, hipStream_t stream)
+{
+    if (a.M < 1 || a.M > kNoAllocMaxRows || a.table_ids) return hipErrorInvalidValue;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    void* base = nullptr;
+    if ((e = noalloc_scratch(dev, &base)) != hipSuccess) return e;
+    unsigned char* b = static_cast<unsigned char*>(base);
+    a.xslots = reinterpret_cast<uint32_t*>(b);
+    a.xcounters = reinterpret_cast<uint64_t*>(b + kNoAllocSlotBytes);
+    a.status = reinterpret_cast<uint32_t*>(b + kNoAllocSlotBytes + kNoAllocCounterBytes);
+    return launch_decode_expert(a, stream);
 }
 
 }  // namespace gpt

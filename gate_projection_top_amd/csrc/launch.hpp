@@ -101,6 +101,11 @@ hipError_t launch_gemm1(const Gemm1Launch& a, hipStream_t stream);
 hipError_t launch_gather(const GatherLaunch& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_decode_expert(const DecodeLaunch& a, hipStream_t stream);
+// The allocation-free variant: the kernel's workspace in static device memory
+// (the launch's xslots, xcounters and status are ignored and replaced).
+hipError_t launch_decode_expert_noalloc(DecodeLaunch a, hipStream_t stream);
+hipError_t noalloc_scratch(int device, void** out);  // this device's copy of that memory
+size_t noalloc_scratch_bytes();
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 int prefill_splits(int64_t M);
 
@@ -125,6 +130,8 @@ constexpr int kExpertMaxRows = 8;
 // per row; but the route table needs all rows in one finisher, and both
 // calls must give the same bytes, so both stay here up to kExpertMaxRows.)
 constexpr int kExpertSplitMinRows = kExpertMaxRows + 1;
+// Allocation-free decode entry point: up to this many tokens.
+constexpr int kNoAllocMaxRows = 4;
 constexpr int kExpertGroup = 16;
 constexpr int kExpertGroups = 256 / kExpertGroup;
 constexpr int kExpertCounterStride = 8;

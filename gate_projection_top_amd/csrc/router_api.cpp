@@ -215,7 +215,11 @@ int router_init(int device)
     if (device < 0) {
         if (hipGetDevice(&device) != hipSuccess) return ROUTER_ERR_HIP;
     }
-    return init_device(device);
+    const int rc = init_device(device);
+    if (rc != ROUTER_OK) return rc;
+    // resolve this device's copy of the allocation-free entry's static scratch
+    void* scratch = nullptr;
+    return gpt::noalloc_scratch(device, &scratch) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
 int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
@@ -234,6 +238,37 @@ int router_fwd(const void* x, const void* w, const float* bias, int64_t M, int H
     if ((int64_t)H * 2 * 256 > 0x7fff0000LL) return ROUTER_ERR_UNSUPPORTED;
     return run_fused(x, w, gpt::kGateBf16, nullptr, nullptr, bias, M, H, E, k, scoring, renorm, out_inds,
                      out_weights, opt_out_logits, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+int router_fwd_noalloc(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
+                       int scoring, int renorm, int32_t* out_inds, float* out_weights, float* opt_out_logits,
+                       hipStream_t stream)
+{
+    int rc = check_common(M, E, k, scoring, renorm);
+    if (rc == ROUTER_OK) rc = check_hidden(H);
+    if (rc != ROUTER_OK) return rc;
+    if (M == 0) return ROUTER_OK;
+    if (M > ROUTER_NOALLOC_MAX_M) return ROUTER_ERR_UNSUPPORTED;
+    rc = check_projection(x, w);
+    if (rc != ROUTER_OK) return rc;
+    if (!out_inds || !out_weights) return ROUTER_ERR_INVALID_ARGUMENT;
+    if ((int64_t)H * 2 * 256 > 0x7fff0000LL) return ROUTER_ERR_UNSUPPORTED;
+    gpt::DecodeLaunch a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.w = static_cast<const uint16_t*>(w);
+    a.w_format = gpt::kGateBf16;
+    a.bias = bias;
+    a.M = (int)M;
+    a.H = H;
+    a.E = E;
+    a.k = k;
+    a.scoring = scoring;
+    a.renorm = renorm;
+    a.inds = out_inds;
+    a.weights = out_weights;
+    a.logits_out = opt_out_logits;
+    a.wait_ticks = g_decode_wait_ticks.load(std::memory_order_relaxed);
+    return gpt::launch_decode_expert_noalloc(a, stream) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
 // The table is built by the finisher of the single row block, in one wavefront.
@@ -435,21 +470,27 @@ int router_status(int device, int clear, uint32_t* out_flags)
         if (hipGetDevice(&device) != hipSuccess) return ROUTER_ERR_HIP;
     }
     if (device >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
-    uint32_t* st = nullptr;
+    uint32_t* words[2] = {nullptr, nullptr};  // the workspace's status word, the scratch's
     {
         std::lock_guard<std::mutex> guard(g_ws_mutex);
-        st = g_ws[device].status;
+        words[0] = g_ws[device].status;
     }
-    if (!st) {
-        *out_flags = 0;
-        return ROUTER_OK;
-    }
+    *out_flags = 0;
+    if (!words[0]) return ROUTER_OK;  // nothing has run on this device through this library
+    void* scratch = nullptr;
+    if (gpt::noalloc_scratch(device, &scratch) == hipSuccess)
+        words[1] = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(scratch) + gpt::noalloc_scratch_bytes() - 256);
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) return ROUTER_ERR_HIP;
     if (prev != device && hipSetDevice(device) != hipSuccess) return ROUTER_ERR_HIP;
     hipError_t e = hipDeviceSynchronize();
-    if (e == hipSuccess) e = hipMemcpy(out_flags, st, sizeof(uint32_t), hipMemcpyDeviceToHost);
-    if (e == hipSuccess && clear) e = hipMemset(st, 0, sizeof(uint32_t));
+    for (uint32_t* st : words) {
+        if (!st || e != hipSuccess) continue;
+        uint32_t f = 0;
+        e = hipMemcpy(&f, st, sizeof(uint32_t), hipMemcpyDeviceToHost);
+        *out_flags |= f;
+        if (e == hipSuccess && clear) e = hipMemset(st, 0, sizeof(uint32_t));
+    }
     if (e == hipSuccess && clear) e = hipDeviceSynchronize();
     if (prev != device) (void)hipSetDevice(prev);
     return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;

@@ -36,7 +36,8 @@ EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route
            "router_fwd_mxfp4", "router_fwd_mxfp8", "router_topk_from_logits", "router_gather_shared_add",
            "router_gather_shared_add_table", "router_expert_gemm1_table",
            "router_set_exchange_timeout_us", "router_set_decode_wait_limit_us", "router_status",
-           "router_strerror")
+           "router_fwd_noalloc", "router_strerror")
+NOALLOC_MAX_M = 4  # ROUTER_NOALLOC_MAX_M
 STATUS_WAIT_LIMIT = 1  # ROUTER_STATUS_WAIT_LIMIT: a decode finisher gave a row up
 
 _lib: Optional[ctypes.CDLL] = None
@@ -63,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_init.restype = i32
     lib.router_fwd.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
     lib.router_fwd.restype = i32
+    lib.router_fwd_noalloc.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.router_fwd_noalloc.restype = i32
     lib.router_fwd_m2_table.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
     lib.router_fwd_m2_table.restype = i32
     lib.router_fwd_route_table.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P,
@@ -192,6 +195,28 @@ def router_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k
                                int(bool(renorm)), _ptr(inds), _ptr(wts), _ptr(logits),
                                _stream(x.device))
     _check(rc, "router_fwd")
+    return (inds, wts, logits) if logits is not None else (inds, wts)
+
+
+def router_fwd_noalloc(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                       scoring: int = SOFTMAX, renorm: bool = True, *, return_logits: bool = False,
+                       out_inds=None, out_weights=None, logits_out=None):
+    """router_fwd through the allocation-free entry point (M <= NOALLOC_MAX_M):
+    the library allocates nothing for the call; pass preallocated outputs to
+    allocate nothing at all."""
+    _check_tensor(x, "x", torch.bfloat16, 2)
+    _check_tensor(w, "w", torch.bfloat16, 2)
+    M, H = x.shape
+    E = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("x and w disagree on H")
+    _check_bias(bias, E)
+    inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
+    with torch.cuda.device(x.device):
+        rc = load().router_fwd_noalloc(_ptr(x), _ptr(w), _ptr(bias), M, H, E, int(k), int(scoring),
+                                       int(bool(renorm)), _ptr(inds), _ptr(wts), _ptr(logits),
+                                       _stream(x.device))
+    _check(rc, "router_fwd_noalloc")
     return (inds, wts, logits) if logits is not None else (inds, wts)
 
 

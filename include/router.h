@@ -282,6 +282,24 @@ int router_topk_from_logits(const float* logits, const float* bias, int64_t M, i
  * are rejected with ROUTER_ERR_INVALID_ARGUMENT. */
 int router_set_exchange_timeout_us(int microseconds);
 
+/* router_fwd for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * one-gate-row-per-workgroup decode kernel, bit-identical results, with its
+ * workspace (tagged logit slots, arrival words, a status word: about 17 KiB)
+ * in a statically allocated device array that each GPU holds until the
+ * process ends, instead of router_init's workspace.  The call allocates
+ * nothing, on the host or the device; router_init (or the first call on a
+ * device) resolves that device's copy of the array once.  Every call on a
+ * GPU shares its copy: overlapping calls on one device race (order them on
+ * one stream).  Limits: 1 <= M <= ROUTER_NOALLOC_MAX_M (M == 0 is a no-op),
+ * else ROUTER_ERR_UNSUPPORTED, nothing launched; bf16 gate; the rest as
+ * router_fwd.  A row given up at the decode wait limit sets the status bit
+ * router_status reports. */
+#define ROUTER_NOALLOC_MAX_M 4
+int router_fwd_noalloc(const void* x, const void* w, const float* bias, int64_t M, int H, int E, int k,
+                       int scoring, int renorm, int32_t* out_inds, float* out_weights,
+                       float* opt_out_logits, hipStream_t stream);
+
 /* Bound, in microseconds, on how long a decode finisher (the workgroup that
  * routes the rows) waits for the other workgroups' published logits before
  * it gives a row up (default 100000 = 100 ms; every real wait ends in
