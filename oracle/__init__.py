@@ -299,8 +299,12 @@ _default: Optional[Oracle] = None
 
 
 def get() -> Oracle:
-    """The oracle built from oracle.c (built on first use if missing)."""
+    """The oracle built from oracle.c (built on first use if missing).
+
+    ``ORACLE_LIB`` in the environment names another build of the same source
+    (the sanitizer build the CPU tests make) to load instead.
+    """
     global _default
     if _default is None:
-        _default = Oracle()
+        _default = Oracle(os.environ.get("ORACLE_LIB") or LIB_PATH)
     return _default
