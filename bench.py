@@ -19,14 +19,19 @@ Also reported (same JSON line):
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, one
                 thread (extras.cpu_baseline_all_threads: the same calls on up to
                 16 threads at once, as throughput);
-  extras        cache-hot cycle, verify widths M=2/8 at H=4096, the biased M=2
-                table on/off delta, the MXFP4 and MXFP8 gates at M=1 and M=8
+  extras        the same calls launched eagerly, the cache-hot cycle, verify
+                widths M=1/2/8 at H=4096 (cache-hot, and cold from a 537 MB
+                pool), the fused-vs-unfused A/B at those widths (a library GEMM
+                writing logits + router_topk_from_logits), the biased M=2 table
+                on/off delta and M=16/64, the launch-floor probes
+                (libfloorprobes.so), the MXFP4 and MXFP8 gates at M=1 and M=8
                 (H=7168, 585 / 606 MB pools) and at the 8192-token prefill, the
                 routed gather + shared-expert add at M=2 (explicit rows, all
                 remote, table rows) and at M=4096, the expert GEMM1 on the
                 table at M=2 (F=4096, D=7168, 15 GB of expert weights), the
-                standalone top-k at M=4096, and the
-                8192-token prefill (tokens/s, fraction of bf16 MFMA and HBM peak).
+                standalone top-k at M=4096, and the 8192-token prefill
+                (tokens/s, fraction of bf16 MFMA and HBM peak, and a roofline
+                block of its own).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
 """
@@ -51,7 +56,9 @@ MX_TRAFFIC_SUMMARY = {f: os.path.join(ROOT, "profiles", f"decode_router_{f}_M1_H
                       for f in ("mxfp4", "mxfp8")}
 GATHER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gather_shared_add_M2_k6_D7168_traffic.txt")
 GEMM1_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_gemm1_M2_k6_F4096_D7168_traffic.txt")
-KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_kernel.hip", "launch.hpp", "router_api.cpp"]
+KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_expert_kernel.hip", "launch.hpp", "router_api.cpp"]
+PREFILL_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_router_M8192_H7168_traffic.txt")
+PREFILL_SOURCES = ["route_common.hpp", "coherent.hpp", "prefill_kernel.hip", "launch.hpp", "router_api.cpp"]
 GATHER_SOURCES = ["gather_kernel.hip", "route_common.hpp", "launch.hpp", "router_api.cpp"]
 GEMM1_SOURCES = ["gemm1_kernel.hip", "route_common.hpp", "coherent.hpp", "launch.hpp", "router_api.cpp"]
 
@@ -254,7 +261,7 @@ def decode_headline(torch, R, W, dev, args, out):
     traffic = committed_traffic()
     out["roofline"] = {
         "bound": "hbm",
-        "kernel": "decode_router_kernel",
+        "kernel": "decode_expert_kernel",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
@@ -266,6 +273,17 @@ def decode_headline(torch, R, W, dev, args, out):
         "launch_timing": "HIP event pair on the launching stream around the timed replays "
                          "(back-to-back launches) / launch count",
     }
+    # the same calls launched eagerly (host launch path included), cold pool
+    eager_calls = [c for grp in step_calls for c in grp]
+    for c in eager_calls[:LAYERS]:
+        c()
+    torch.cuda.synchronize()
+    n_eager = args.steps * LAYERS
+    t0 = time.perf_counter()
+    for i in range(n_eager):
+        eager_calls[i % len(eager_calls)]()
+    torch.cuda.synchronize()
+    out["extras"]["decode_M1_H7168_eager_us_per_call"] = round((time.perf_counter() - t0) * 1e6 / n_eager, 3)
     # cache-hot cycle: the same 40 gate matrices every step (Infinity-Cache resident)
     hot, _ = timed_replays(torch, clean[:1], args.steps, args.warmup)
     out["extras"]["decode_M1_H7168_hot_us_per_call"] = round(hot * 1e6 / (args.steps * LAYERS), 3)
@@ -285,7 +303,8 @@ def decode_extras(torch, R, W, dev, args):
                                                                out_inds=oi[l], out_weights=ow[l]))
                  for l in range(LAYERS)]
         ex[f"decode_M{M}_H4096_hot_us_per_call"] = round(graph_call_us(torch, calls, args.steps, args.warmup), 3)
-    log("verify widths done")
+    log("verify widths (hot) done")
+    ex.update(decode_widths_cold_and_unfused(torch, R, W, dev, args))
 
     # biased M=2 with and without the unique-route table (k=6)
     bias = W.torch_uniform_f32(E, -0.05, 0.05, seed=9, device=dev)
@@ -332,6 +351,62 @@ def decode_extras(torch, R, W, dev, args):
             for l in range(LAYERS)]
         ex[f"biased_M{M}_k6_us_per_call"] = round(graph_call_us(torch, calls, args.steps, args.warmup), 3)
     log("biased router done")
+    return ex
+
+
+def decode_widths_cold_and_unfused(torch, R, W, dev, args):
+    """Verify widths M in {1, 2, 8} at H=4096 with the gate matrices cold: 40
+    calls per step from a 256-matrix pool (537 MB, twice the Infinity Cache),
+    fused (router_fwd) and unfused (the projection as a library fp32 GEMM
+    writing fp32 logits to HBM, then router_topk_from_logits on them: the two
+    back-to-back launches of the pages' isolated A/B gate).  The unfused
+    path's GEMM reads fp32 copies of the gate (twice the bytes of bf16: the
+    library has no bf16 x bf16 -> fp32 GEMM through torch here), stated with
+    the numbers."""
+    ex = {}
+    H, E, k, pool = 4096, 256, 8, 256
+    groups = pool // LAYERS
+    wpool = W.torch_gaussian_bf16((pool, E, H), 1.0 / H ** 0.5, seed=70, device=dev)
+    for M in (1, 2, 8):
+        x = W.torch_rms_normalised_bf16((LAYERS, M, H), seed=71 + M, device=dev)
+        oi = torch.empty((LAYERS, M, k), dtype=torch.int32, device=dev)
+        ow = torch.empty((LAYERS, M, k), dtype=torch.float32, device=dev)
+        graphs = [GraphTimer(torch, [(lambda l=l, g=g: R.router_fwd(x[l], wpool[g * LAYERS + l], None, k, W.SOFTMAX,
+                                                                   True, out_inds=oi[l], out_weights=ow[l]))
+                                     for l in range(LAYERS)]) for g in range(groups)]
+        wall, ev_ms = timed_replays(torch, graphs, args.steps, args.warmup)
+        ex[f"decode_M{M}_H4096_cold_us_per_call"] = round(wall * 1e6 / (args.steps * LAYERS), 3)
+        del graphs
+    log("verify widths (cold) done")
+    # unfused A/B on a smaller cold pool of fp32 gates (40 x 4 MiB per step, 6 steps' worth)
+    upool = 240
+    wf = wpool[:upool].float().transpose(1, 2).contiguous()  # [pool, H, E] fp32: logits = x @ wf
+    del wpool
+    ugroups = upool // LAYERS
+    for M in (1, 2, 8):
+        x = W.torch_rms_normalised_bf16((LAYERS, M, H), seed=71 + M, device=dev).float()
+        lg = torch.empty((LAYERS, M, E), dtype=torch.float32, device=dev)
+        oi = torch.empty((LAYERS, M, k), dtype=torch.int32, device=dev)
+        ow = torch.empty((LAYERS, M, k), dtype=torch.float32, device=dev)
+
+        def unfused(l, widx, x=x, lg=lg, oi=oi, ow=ow):
+            def run():
+                torch.mm(x[l], wf[widx], out=lg[l])
+                R.router_topk_from_logits(lg[l], None, k, W.SOFTMAX, True, out_inds=oi[l], out_weights=ow[l])
+            return run
+
+        try:
+            graphs = [GraphTimer(torch, [unfused(l, g * LAYERS + l) for l in range(LAYERS)]) for g in range(ugroups)]
+        except RuntimeError as exc:  # library GEMM not capturable
+            log(f"unfused A/B skipped: {exc}")
+            break
+        wall, _ = timed_replays(torch, graphs, args.steps, args.warmup)
+        ex[f"decode_M{M}_H4096_unfused_gemm_plus_topk_cold_us_per_call"] = round(wall * 1e6 / (args.steps * LAYERS), 3)
+        del graphs
+    ex["decode_unfused_note"] = ("unfused = torch.mm fp32 GEMM (fp32 copy of the gate, 2x its bf16 bytes) "
+                                 "writing logits + router_topk_from_logits, two launches per call")
+    del wf
+    log("fused vs unfused A/B done")
     return ex
 
 
@@ -525,8 +600,21 @@ def prefill_extras(torch, R, W, dev, args):
     ex["prefill_M8192_tokens_per_s"] = round(M / (p_us * 1e-6), 0)
     ex["prefill_mfma_tflops"] = round(tflops, 1)
     ex["prefill_mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
-    ex["prefill_hbm_frac"] = round((M * H * 2 + E * H * 2 + E * 4 + M * 64) / (p_us * 1e-6) / 1e9
-                                   / HBM_PEAK_GBS, 4)
+    algo_bytes = M * H * 2 + E * H * 2 + E * 4 + M * 64
+    ex["prefill_hbm_frac"] = round(algo_bytes / (p_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    ex["prefill_roofline"] = {
+        "bound": "mfma",
+        "kernel": "prefill_router_kernel",
+        "achieved": round(tflops, 1),
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": committed_traffic(PREFILL_TRAFFIC_SUMMARY, PREFILL_SOURCES),
+        "flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "launch_us": round(p_us, 2),
+        "launch_timing": "HIP event pair on the launching stream around the timed graph replays / launch count",
+    }
     # context: the vendor GEMM (hipBLASLt through torch) on the same projection, logits only
     xf = xs[0]
     wpt = wp.t().contiguous()  # [H, E]: no transposed view reaches the library GEMM
@@ -612,6 +700,17 @@ def floor_extras(torch, W, dev, args):
     return ex
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(W, seconds):
     """The oracle (as written, single thread) on M=1 H=7168 router calls for ~`seconds`."""
     import oracle
@@ -628,6 +727,7 @@ def cpu_baseline(W, seconds):
             break
     log(f"cpu baseline: {n} oracle calls in {el:.1f}s")
     return {"value": round(el * 1e6 / n, 1), "unit": "µs/call", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{n} single-token router calls (H=7168, E=256, k=8, softmax, renorm) "
                       f"through the C oracle, one thread"}
 
@@ -664,6 +764,7 @@ def cpu_baseline_threads(W, seconds):
     n = sum(counts)
     log(f"cpu baseline ({threads} threads): {n} oracle calls in {el:.1f}s")
     return {"value": round(el * 1e6 / max(n, 1), 2), "unit": "µs/call", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{n} single-token router calls (H=7168, E=256, k=8, softmax, renorm), "
                       f"independent calls on {threads} threads"}
 
