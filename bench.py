@@ -51,8 +51,8 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 LAYERS = 40
 POOL = 160
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_router_M1_H7168_traffic.txt")
-MX_TRAFFIC_SUMMARY = {f: os.path.join(ROOT, "profiles", f"decode_router_{f}_M1_H7168_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_expert_M1_H7168_traffic.txt")
+MX_TRAFFIC_SUMMARY = {f: os.path.join(ROOT, "profiles", f"decode_expert_{f}_M1_H7168_traffic.txt")
                       for f in ("mxfp4", "mxfp8")}
 GATHER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gather_shared_add_M2_k6_D7168_traffic.txt")
 GEMM1_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_gemm1_M2_k6_F4096_D7168_traffic.txt")
