@@ -70,7 +70,6 @@ constexpr int kSStageBytes = kBN * 4;                            // 1 KiB
 constexpr int kSRingOffset = kWRingOffset + kWSlots * kWStageBytesOf<kGateMxfp8>;
 static_assert(kSRingOffset + kWSlots * kSStageBytes <= kRingBytes, "block-scaled rings fit the LDS ring");
 static_assert(kTileBytes <= kFlagOffset, "row tile and flag overlap");
-static_assert(kSelOffset + kWaves * 4 * kFilterCap * 8 <= kFlagOffset, "selection scratch and flag overlap");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -152,13 +151,14 @@ __device__ __forceinline__ int partial_off(const PrefillLaunch& p, int tile, int
 }
 
 constexpr int kRowGroup = 4;  // rows a wave routes in lockstep (route_rows)
+static_assert(kSelOffset + kWaves * kRowGroup * kFilterSlots * 8 <= kFlagOffset, "selection scratch and flag overlap");
 
 // Route rows [r_begin, r_end) of the LDS tile (local row indices): wave w
 // takes rows w, w+8, ... in groups of kRowGroup routed together.
 __device__ __forceinline__ uint64_t* wave_sel(float* tile_f, int wave)
 {
     return reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(tile_f) + kSelOffset) +
-           wave * kRowGroup * kFilterCap;
+           wave * kRowGroup * kFilterSlots;
 }
 
 __device__ __forceinline__ void route_tile_rows(const PrefillLaunch& p, float* tile,

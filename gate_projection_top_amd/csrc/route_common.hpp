@@ -222,7 +222,7 @@ __device__ __forceinline__ double rank_sum(double u)
 //     round: for routing waves that share a SIMD.
 //   kFilter: no rounds where a threshold leaves between k and kFilterCap
 //     candidates (select_filter above): they are ranked by counting; the
-//     lane rounds otherwise.  Needs kFilterCap 8-byte LDS entries per row.
+//     lane rounds otherwise.  Needs kFilterSlots 8-byte LDS entries per row.
 enum RoundStyle : int { kRoundsLane = 0, kRoundsScalar = 1, kFilter = 2 };
 
 template <RoundStyle kStyle>
@@ -234,24 +234,26 @@ __device__ __forceinline__ uint32_t max_code(uint32_t v)
         return wave_max_u32(v);
 }
 
-// Filtered selection of one row (the lane's four codes sorted in selection
-// order, their slots in `order`, two bits each, head lowest).
+// Filtered selection of one row (the lane's four codes in any order, their
+// slots in `order`, two bits each).
 //
 // A threshold T below the row maximum is chosen so that at least k and at
-// most kFilterCap codes reach it: T = max - D in code space (codes are
-// monotone in the key), D moved by doubling, halving and bisection, each try
-// costing one ballot and population count per code slot.  Every winner is at
-// or above T (at least k codes are), so the winners are the first k of the
-// candidates under the contract's precedence.  Each candidate goes to LDS as
-// one 64-bit word, code above (0xFFFF - expert) below, so that one unsigned
-// comparison is that precedence (larger key first, equal keys by lower
-// index); a candidate's rank is the number of candidate words above its own,
-// and the first k are re-read in rank order.  Lane j < k ends with the index
-// and the code of rank j.  Rows where no such T exists within the try budget
-// (many equal or nearly equal codes near the top) return false and leave the
-// outputs untouched; the caller runs the rounds instead.
-// `lds`: kFilterCap entries owned by this wave.
+// most kFilterCap codes reach it: T = top - D in code space (codes are
+// monotone in the key; top is the largest first-slot code, any reference
+// below the maximum works), D moved by doubling, halving and bisection, each
+// try costing one ballot and population count per code slot.  Every winner
+// is at or above T (at least k codes are), so the winners are the first k of
+// the candidates under the contract's precedence.  Each candidate goes to
+// LDS as one 64-bit word, code above (0xFFFF - expert) below, so that one
+// unsigned comparison is that precedence (larger key first, equal keys by
+// lower index); a candidate's rank is the number of candidate words above
+// its own, and the first k are re-read in rank order.  Lane j < k ends with
+// the index and the code of rank j.  Rows where no such T exists within the
+// try budget (many equal or nearly equal codes near the top) return false
+// and leave the outputs untouched; the caller runs the rounds instead.
+// `lds`: kFilterSlots entries owned by this wave.
 constexpr int kFilterCap = 32;
+constexpr int kFilterSlots = kFilterCap + 2;  // + a discard slot, rows kept 16-byte aligned
 constexpr int kFilterTries = 6;
 
 __device__ __forceinline__ int count_at_least(const uint32_t (&c)[kPerLane], uint32_t T)
@@ -289,33 +291,39 @@ __device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uin
         if (dhi && dhi - dlo <= 1u) break;  // no threshold separates k..cap codes
     }
     if (!found) return false;
-    // compaction: candidates of lower lanes first, then this lane's in its order
+    // compaction: lane L's candidates go to [at, ...), at counting the
+    // candidates of the lower lanes, in slot order; its other entries go to
+    // the discard slot, and lanes n .. cap-1 zero the unused tail, so that
+    // entries 0 .. cap-1 hold the n candidates and then zeros (below every
+    // candidate word).  No write needs a lane mask.
     uint32_t at = 0u;
+    bool take[kPerLane];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-        const uint64_t m = __builtin_amdgcn_ballot_w64(c[j] >= T);
+        take[j] = c[j] >= T;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(take[j]);
         at += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     }
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-        if (c[j] >= T) {
-            const uint32_t idx = (uint32_t)(lane * kPerLane) + ((order >> (2 * j)) & 3u);
-            lds[at] = ((uint64_t)c[j] << 32) | (0xFFFFu - idx);
-            at += 1u;
-        }
+        const uint32_t idx = (uint32_t)(lane * kPerLane) + ((order >> (2 * j)) & 3u);
+        lds[take[j] ? at : (uint32_t)kFilterCap] = ((uint64_t)c[j] << 32) | (0xFFFFu - idx);
+        at += take[j] ? 1u : 0u;
     }
-    const int n8 = (n + 7) & ~7;
-    if (lane >= n && lane < n8) lds[lane] = 0ull;  // below every candidate word
+    lds[(lane >= n && lane < kFilterCap) ? lane : kFilterCap] = 0ull;
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    const uint64_t mine = lane < n ? lds[lane] : 0ull;
+    // every lane reads the table (broadcast reads, half of it per batch to
+    // bound the registers) and ranks its own entry: the number above it
+    const uint64_t mine = lds[lane & (kFilterCap - 1)];
     int rank = 0;
-    for (int j = 0; j < n8; j += 8) {
-        uint64_t q[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = lds[j + i];
+    for (int h = 0; h < kFilterCap; h += kFilterCap / 2) {
+        uint64_t q[kFilterCap / 2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rank += q[i] > mine ? 1 : 0;
+        for (int i = 0; i < kFilterCap / 2; ++i) q[i] = lds[h + i];
+#pragma unroll
+        for (int i = 0; i < kFilterCap / 2; ++i) rank += q[i] > mine ? 1 : 0;
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
@@ -499,7 +507,7 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
         selected = true;
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            selected &= select_filter(c[n], 0xE4u, s.k, lds + n * kFilterCap, my_idx[n], my_code[n]);
+            selected &= select_filter(c[n], 0xE4u, s.k, lds + n * kFilterSlots, my_idx[n], my_code[n]);
     }
     if (!selected) {
         uint32_t slots[N];  // the four slots in selection order, two bits each, head lowest
@@ -561,7 +569,7 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
 }
 
 // N rows in lockstep (same spec); rows n carry logits v[n] and get out[n].
-// lds: N * kFilterCap entries owned by this wave (kFilter only).
+// lds: N * kFilterSlots entries owned by this wave (kFilter only).
 template <int N, RoundStyle kStyle = kRoundsScalar>
 __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const float (&bv)[kPerLane],
                                            const RowSpec& s, RowResult (&out)[N], uint64_t* lds = nullptr)
@@ -729,7 +737,7 @@ __device__ __forceinline__ void row_unbiased_scores(const float (&v)[kPerLane], 
     __hip_atomic_store(ready, mark, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// lds: kFilterCap entries owned by this wave (kFilter only).  ext_u,
+// lds: kFilterSlots entries owned by this wave (kFilter only).  ext_u,
 // ext_ready, ext_want: see route_row_impl (used only when the row needs no
 // score before its selection; ignored otherwise).
 template <RoundStyle kStyle = kRoundsLane>
