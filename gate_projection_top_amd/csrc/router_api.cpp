@@ -29,24 +29,36 @@ constexpr size_t kPfPartialFloats =
 constexpr size_t kPfCounters = (size_t)gpt::kPrefillMaxSplitTiles * gpt::kPrefillCountersPerTile;
 constexpr size_t kXSlotWords = (size_t)gpt::kExpertMaxRows * ROUTER_MAX_E * 2;  // (logit, tag) pairs
 
-DeviceWorkspace g_ws[kMaxDevices];
+// A device's workspaces: one per stream that has called a fused entry
+// point, up to ROUTER_MAX_STREAMS, all allocated by router_init.  A stream
+// keeps its slot until router_release_stream; calls on one stream are
+// ordered by the stream, so no two launches that can overlap share a slot.
+struct DevicePool {
+    bool ready = false;
+    DeviceWorkspace ws[ROUTER_MAX_STREAMS];
+    hipStream_t owner[ROUTER_MAX_STREAMS] = {};
+    bool taken[ROUTER_MAX_STREAMS] = {};
+};
+
+DevicePool g_pool[kMaxDevices];
 std::atomic<uint32_t> g_spin_ticks{20000};  // 200 us at the 100 MHz realtime clock
 std::atomic<uint32_t> g_decode_wait_ticks{gpt::kDecodeWaitTicksDefault};
 std::mutex g_ws_mutex;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int init_device(int dev)
+void free_workspace(DeviceWorkspace& ws)
 {
-    if (dev < 0 || dev >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
-    std::lock_guard<std::mutex> guard(g_ws_mutex);
-    if (g_ws[dev].partials) return ROUTER_OK;
+    void* bufs[] = {ws.partials, ws.counters, ws.xslots, ws.xcounters, ws.status, ws.pf_partials, ws.pf_counters};
+    for (void* b : bufs)
+        if (b) (void)hipFree(b);
+    ws = DeviceWorkspace{};
+}
 
-    int prev = -1;
-    if (hipGetDevice(&prev) != hipSuccess) return ROUTER_ERR_HIP;
-    if (prev != dev && hipSetDevice(dev) != hipSuccess) return ROUTER_ERR_HIP;
-
-    DeviceWorkspace ws;
+// Allocates one workspace and zeroes what must start at zero (on the null
+// stream; the caller synchronises the device before first use).
+hipError_t alloc_workspace(DeviceWorkspace& ws)
+{
     hipError_t e = hipMalloc((void**)&ws.partials, kPartialFloats * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&ws.counters, kCounters * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMalloc((void**)&ws.pf_partials, kPfPartialFloats * sizeof(float));
@@ -60,32 +72,69 @@ int init_device(int dev)
     if (e == hipSuccess) e = hipMemset(ws.partials, 0, kPartialFloats * sizeof(float));
     if (e == hipSuccess) e = hipMemset(ws.counters, 0, kCounters * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(ws.pf_counters, 0, kPfCounters * sizeof(uint32_t));
+    return e;
+}
+
+int init_device(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> guard(g_ws_mutex);
+    DevicePool& pool = g_pool[dev];
+    if (pool.ready) return ROUTER_OK;
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return ROUTER_ERR_HIP;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) return ROUTER_ERR_HIP;
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < ROUTER_MAX_STREAMS && e == hipSuccess; ++i) e = alloc_workspace(pool.ws[i]);
     // The counters must read zero before any stream (blocking or not) runs a
     // kernel; init is rare, so a device-wide wait is acceptable here.
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (prev != dev) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
-        if (ws.partials) (void)hipFree(ws.partials);
-        if (ws.counters) (void)hipFree(ws.counters);
-        if (ws.pf_partials) (void)hipFree(ws.pf_partials);
-        if (ws.pf_counters) (void)hipFree(ws.pf_counters);
-        if (ws.xslots) (void)hipFree(ws.xslots);
-        if (ws.xcounters) (void)hipFree(ws.xcounters);
-        if (ws.status) (void)hipFree(ws.status);
+        for (DeviceWorkspace& ws : pool.ws) free_workspace(ws);
         return ROUTER_ERR_NO_WORKSPACE;
     }
-    g_ws[dev] = ws;
+    pool.ready = true;
     return ROUTER_OK;
 }
 
-int current_workspace(DeviceWorkspace* out)
+// The workspace of `stream` on the current device: its slot, or a free slot
+// it now takes.  A device not yet initialised is initialised here, except
+// under stream capture (allocation and a device-wide wait cannot be
+// captured): then ROUTER_ERR_NOT_INITIALIZED.
+int current_workspace(hipStream_t stream, DeviceWorkspace* out)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return ROUTER_ERR_HIP;
-    const int rc = init_device(dev);
-    if (rc != ROUTER_OK) return rc;
-    *out = g_ws[dev];
-    return ROUTER_OK;
+    if (dev < 0 || dev >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        {
+            std::lock_guard<std::mutex> guard(g_ws_mutex);
+            DevicePool& pool = g_pool[dev];
+            if (pool.ready) {
+                int free_slot = -1;
+                for (int i = 0; i < ROUTER_MAX_STREAMS; ++i) {
+                    if (pool.taken[i] && pool.owner[i] == stream) {
+                        *out = pool.ws[i];
+                        return ROUTER_OK;
+                    }
+                    if (!pool.taken[i] && free_slot < 0) free_slot = i;
+                }
+                if (free_slot < 0) return ROUTER_ERR_BUSY;
+                pool.taken[free_slot] = true;
+                pool.owner[free_slot] = stream;
+                *out = pool.ws[free_slot];
+                return ROUTER_OK;
+            }
+        }
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return ROUTER_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return ROUTER_ERR_NOT_INITIALIZED;
+        const int rc = init_device(dev);
+        if (rc != ROUTER_OK) return rc;
+    }
+    return ROUTER_ERR_NO_WORKSPACE;
 }
 
 int check_common(int64_t M, int E, int k, int scoring, int renorm)
@@ -139,7 +188,7 @@ int run_fused(const void* x, const void* w, int format, const uint8_t* w_codes, 
 {
     hipError_t e;
     DeviceWorkspace ws;
-    const int rc = current_workspace(&ws);
+    const int rc = current_workspace(stream, &ws);
     if (rc != ROUTER_OK) return rc;
     if (M <= ROUTER_DECODE_MAX_M) {
         gpt::DecodeLaunch a{};
@@ -470,16 +519,18 @@ int router_status(int device, int clear, uint32_t* out_flags)
         if (hipGetDevice(&device) != hipSuccess) return ROUTER_ERR_HIP;
     }
     if (device >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
-    uint32_t* words[2] = {nullptr, nullptr};  // the workspace's status word, the scratch's
+    uint32_t* words[ROUTER_MAX_STREAMS + 1] = {};  // every workspace's status word, then the scratch's
     {
         std::lock_guard<std::mutex> guard(g_ws_mutex);
-        words[0] = g_ws[device].status;
+        if (g_pool[device].ready)
+            for (int i = 0; i < ROUTER_MAX_STREAMS; ++i) words[i] = g_pool[device].ws[i].status;
     }
     *out_flags = 0;
     if (!words[0]) return ROUTER_OK;  // nothing has run on this device through this library
     void* scratch = nullptr;
     if (gpt::noalloc_scratch(device, &scratch) == hipSuccess)
-        words[1] = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(scratch) + gpt::noalloc_scratch_bytes() - 256);
+        words[ROUTER_MAX_STREAMS] =
+            reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(scratch) + gpt::noalloc_scratch_bytes() - 256);
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) return ROUTER_ERR_HIP;
     if (prev != device && hipSetDevice(device) != hipSuccess) return ROUTER_ERR_HIP;
@@ -496,6 +547,18 @@ int router_status(int device, int clear, uint32_t* out_flags)
     return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
+int router_release_stream(hipStream_t stream)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ROUTER_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ROUTER_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> guard(g_ws_mutex);
+    DevicePool& pool = g_pool[dev];
+    for (int i = 0; i < ROUTER_MAX_STREAMS; ++i)
+        if (pool.taken[i] && pool.owner[i] == stream) pool.taken[i] = false;
+    return ROUTER_OK;
+}
+
 const char* router_strerror(int code)
 {
     switch (code) {
@@ -505,6 +568,8 @@ const char* router_strerror(int code)
     case ROUTER_ERR_MISALIGNED: return "x or the gate weights are not 16-byte aligned";
     case ROUTER_ERR_HIP: return "HIP runtime error";
     case ROUTER_ERR_NO_WORKSPACE: return "workspace allocation failed";
+    case ROUTER_ERR_BUSY: return "every workspace of the device is held by another stream (router_release_stream)";
+    case ROUTER_ERR_NOT_INITIALIZED: return "first call on the device under stream capture: call router_init first";
     default: return "unknown router error";
     }
 }

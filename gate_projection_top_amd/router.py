@@ -25,6 +25,9 @@ ERR_UNSUPPORTED = 2
 ERR_MISALIGNED = 3
 ERR_HIP = 4
 ERR_NO_WORKSPACE = 5
+ERR_BUSY = 6
+ERR_NOT_INITIALIZED = 7
+MAX_STREAMS = 8  # ROUTER_MAX_STREAMS
 
 # router_fwd_route_table limits (ROUTER_TABLE_MAX_M / ROUTER_TABLE_MAX_SLOTS)
 TABLE_MAX_M = 16
@@ -36,7 +39,7 @@ EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route
            "router_fwd_mxfp4", "router_fwd_mxfp8", "router_topk_from_logits", "router_gather_shared_add",
            "router_gather_shared_add_table", "router_expert_gemm1_table",
            "router_set_exchange_timeout_us", "router_set_decode_wait_limit_us", "router_status",
-           "router_fwd_noalloc", "router_strerror")
+           "router_fwd_noalloc", "router_release_stream", "router_strerror")
 NOALLOC_MAX_M = 4  # ROUTER_NOALLOC_MAX_M
 STATUS_WAIT_LIMIT = 1  # ROUTER_STATUS_WAIT_LIMIT: a decode finisher gave a row up
 
@@ -89,6 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.router_set_decode_wait_limit_us.restype = i32
     lib.router_status.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_uint32)]
     lib.router_status.restype = i32
+    lib.router_release_stream.argtypes = [P]
+    lib.router_release_stream.restype = i32
     lib.router_strerror.argtypes = [i32]
     lib.router_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -126,9 +131,16 @@ def _check_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int):
 
 
 def init(device: Optional[int] = None):
-    """Allocate the per-device workspace now (required before graph capture)."""
+    """Allocate the device's workspaces now (required before graph capture)."""
     dev = torch.cuda.current_device() if device is None else int(device)
     _check(load().router_init(dev), "router_init")
+
+
+def release_stream(stream=None):
+    """Give back the workspace the stream (default: the current one) holds on
+    the current device; only once the stream's router work has finished."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    _check(load().router_release_stream(ctypes.c_void_p(s.cuda_stream)), "router_release_stream")
 
 
 def set_exchange_timeout_us(microseconds: int):

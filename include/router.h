@@ -5,7 +5,8 @@
  * are owned by the caller and are never freed or retained by the library.
  * All calls are asynchronous on `stream`: they enqueue HIP kernels and
  * return without synchronising.  After router_init() on a device no call
- * allocates memory, so calls may be captured into a HIP graph.
+ * allocates memory, so calls may be captured into a HIP graph (router_status
+ * excepted, which synchronises).
  *
  * What is computed (pages on the fused MoE router):
  *   - qwisp issue #145 "Observation" and "Change": the gate matvec
@@ -63,10 +64,18 @@
  * on any error nothing is launched and no output byte changes.  The return
  * value is ROUTER_OK or one of the codes below; router_strerror() names it.
  *
- * Concurrency: the fused router entry points (router_fwd*) use a per-device
- * workspace (partial sums and arrival counters).  Calls on one device must be
- * ordered (same stream, or externally synchronised); overlapping calls on
- * one device race on that workspace.  router_topk_from_logits uses none.
+ * Concurrency: the fused router entry points (router_fwd*) need a
+ * workspace (partial sums, tagged logit slots, arrival counters, a status
+ * word).  router_init allocates ROUTER_MAX_STREAMS of them per device, and
+ * each stream that calls a fused entry point takes one for itself on its
+ * first call and keeps it (router_release_stream gives it back).  Calls on
+ * one stream are ordered by the stream, so calls on different streams may
+ * overlap freely.  A call from one more stream than that gets
+ * ROUTER_ERR_BUSY, nothing launched.  A captured graph keeps the workspace
+ * of the stream it was captured on: replays of it must not overlap each
+ * other or calls on that stream.  router_fwd_noalloc is the exception: its
+ * workspace is one static array per device, so its calls must be ordered
+ * with each other (see there).  The other entry points use no workspace.
  */
 #ifndef GATE_PROJECTION_TOP_ROUTER_H
 #define GATE_PROJECTION_TOP_ROUTER_H
@@ -80,8 +89,9 @@ extern "C" {
 
 #define ROUTER_MAX_E 256
 #define ROUTER_MAX_K 16
-/* router_fwd runs the split-H decode kernel up to this many tokens and the
- * MFMA GEMM-with-epilogue prefill kernel above it. */
+/* router_fwd runs a decode kernel up to this many tokens (one workgroup per
+ * gate row up to 8 tokens, row blocks x expert blocks x H-splits from 9) and
+ * the MFMA GEMM-with-epilogue prefill kernel above it. */
 #define ROUTER_DECODE_MAX_M 64
 /* router_fwd_route_table: at most this many tokens, and at most
  * ROUTER_TABLE_MAX_SLOTS = M*k slots (one wavefront builds the table). */
@@ -99,20 +109,36 @@ enum {
     ROUTER_ERR_UNSUPPORTED = 2,      /* shape outside the limits above */
     ROUTER_ERR_MISALIGNED = 3,       /* x or the gate weights not aligned as stated */
     ROUTER_ERR_HIP = 4,              /* a HIP runtime call failed */
-    ROUTER_ERR_NO_WORKSPACE = 5      /* workspace could not be allocated */
+    ROUTER_ERR_NO_WORKSPACE = 5,     /* workspace could not be allocated */
+    ROUTER_ERR_BUSY = 6,             /* every workspace of the device is held by other streams */
+    ROUTER_ERR_NOT_INITIALIZED = 7   /* first fused call on a device made under stream capture */
 };
 
-/* Allocates the per-device workspace for `device` (or the current device
- * when device < 0) and zeroes its counters.  Idempotent and thread-safe.
- * Call it before capturing router_fwd into a graph; router_fwd calls it
- * itself on first use otherwise.  The workspace lives until process exit. */
+/* Streams per device that can hold a fused-router workspace at once. */
+#define ROUTER_MAX_STREAMS 8
+
+/* Allocates the ROUTER_MAX_STREAMS workspaces of `device` (or of the
+ * current device when device < 0; about 34 MiB each) and zeroes what must
+ * start at zero, then waits for the device.  Idempotent and thread-safe.
+ * Call it before capturing a fused call into a graph: a first fused call on
+ * a device that is made under stream capture cannot allocate and returns
+ * ROUTER_ERR_NOT_INITIALIZED; otherwise the first fused call runs it.  The
+ * workspaces live until process exit. */
 int router_init(int device);
 
+/* Gives back the workspace that `stream` holds on the current device, if
+ * any, for another stream to take.  Call it only once the stream's router
+ * work has finished (e.g. after synchronising the stream): a later stream
+ * may otherwise race with it.  A released stream that calls again takes a
+ * workspace again.  Always ROUTER_OK unless the runtime fails. */
+int router_release_stream(hipStream_t stream);
+
 /* Fused router (gate projection + scoring + top-k + renorm in one launch).
- * Decode (M <= ROUTER_DECODE_MAX_M): experts and H are split across
- * workgroups; the last workgroup to arrive holds the E logits of each row in
- * LDS and runs the selection.  Prefill (larger M): one MFMA GEMM whose
- * epilogue does the selection from LDS.  Logits reach HBM only when
+ * Decode (M <= ROUTER_DECODE_MAX_M): the gate rows (and, from 9 tokens, H)
+ * are split across workgroups, which publish their logits as tagged slots;
+ * a finisher workgroup picked by an arrival ticket gathers a row's E logits
+ * and runs the selection.  Prefill (larger M): one MFMA GEMM whose epilogue
+ * does the selection from LDS.  Logits reach HBM only when
  * opt_out_logits is non-NULL, and writing them never changes inds/weights.
  *   x, w, bias, inds, weights, opt_out_logits: device pointers (see layouts);
  *   scoring: router_scoring_t; renorm: 0 or 1. */
@@ -313,7 +339,8 @@ int router_fwd_noalloc(const void* x, const void* w, const float* bias, int64_t 
  * enqueued after it returns.  Negative values: ROUTER_ERR_INVALID_ARGUMENT. */
 int router_set_decode_wait_limit_us(int microseconds);
 
-/* Sticky status bits of a device's workspace. */
+/* Sticky status bits of a device's workspaces (all streams' and the
+ * allocation-free entry point's, read together). */
 #define ROUTER_STATUS_WAIT_LIMIT 1u /* a decode finisher gave a row up */
 
 /* Waits for the device to finish all enqueued work (hipDeviceSynchronize),

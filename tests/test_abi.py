@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_strerror_names_every_code(lib):
-    for code in range(0, 6):
+    for code in range(0, 8):
         assert R.strerror(code) and "unknown" not in R.strerror(code)
     assert "unknown" in R.strerror(99)
 
