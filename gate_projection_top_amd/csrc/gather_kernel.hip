@@ -1,7 +1,9 @@
-// Routed gather + shared-expert add, the step after the router (b70 lab MTP1
-// M=2 note: "Outcome" fuses the generic routed gather with the following
-// shared-expert BF16 addition; "Exact arithmetic" fixes the rounding chain
-// FP32 routed accumulation -> BF16 -> add shared BF16 -> BF16).
+// Routed gather + shared-expert add, the step after the router.  One launch
+// does both the weighted gather of the routed experts' rows and the add of
+// the shared expert's row (b70 lab MTP1 M=2 note, "Outcome"), with the
+// rounding chain of that note's "Exact arithmetic" section: the routed sum
+// in FP32, rounded to BF16, then the BF16 shared row added and rounded to
+// BF16 again.
 //
 //   out[t, d] = bf16( bf16(acc) + shared[t, d] ),
 //   acc = fp32 sum over the slots j = 0..k-1 of token t, in order, of
