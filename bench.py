@@ -19,7 +19,8 @@ Also reported (same JSON line):
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, one
                 thread (extras.cpu_baseline_all_threads: the same calls on up to
                 16 threads at once, as throughput);
-  extras        the same calls launched eagerly, the cache-hot cycle, verify
+  extras        the same calls launched eagerly (through the Python binding,
+                and straight through the C ABI), the cache-hot cycle, verify
                 widths M=1/2/8 at H=4096 (cache-hot, and cold from a 537 MB
                 pool), the fused-vs-unfused A/B at those widths (a library GEMM
                 writing logits + router_topk_from_logits), the biased M=2 table
@@ -284,6 +285,22 @@ def decode_headline(torch, R, W, dev, args, out):
         eager_calls[i % len(eager_calls)]()
     torch.cuda.synchronize()
     out["extras"]["decode_M1_H7168_eager_us_per_call"] = round((time.perf_counter() - t0) * 1e6 / n_eager, 3)
+    # the same eager calls straight through the C ABI with their arguments
+    # marshalled beforehand: the library's own host path per call
+    lib = R.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    raw = [(xpool[i % LAYERS].data_ptr(), wpool[i % POOL].data_ptr(), inds[i % LAYERS].data_ptr(),
+            wts[i % LAYERS].data_ptr()) for i in range(POOL)]
+    for xp, wp, ip, op in raw[:LAYERS]:
+        lib.router_fwd(xp, wp, None, 1, H, E, k, W.SOFTMAX, 1, ip, op, None, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_eager):
+        xp, wp, ip, op = raw[i % POOL]
+        if lib.router_fwd(xp, wp, None, 1, H, E, k, W.SOFTMAX, 1, ip, op, None, stream) != 0:
+            raise RuntimeError("router_fwd failed")
+    torch.cuda.synchronize()
+    out["extras"]["decode_M1_H7168_eager_c_abi_us_per_call"] = round((time.perf_counter() - t0) * 1e6 / n_eager, 3)
     # cache-hot cycle: the same 40 gate matrices every step (Infinity-Cache resident)
     hot, _ = timed_replays(torch, clean[:1], args.steps, args.warmup)
     out["extras"]["decode_M1_H7168_hot_us_per_call"] = round(hot * 1e6 / (args.steps * LAYERS), 3)

@@ -8,6 +8,7 @@ is not built, loading raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -105,11 +106,28 @@ def strerror(code: int) -> str:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The device's current stream as a raw handle (the cheap accessor when
+    this torch has it)."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_SAME_DEVICE = contextlib.nullcontext()
+
+
+def _on(device: torch.device):
+    """Make `device` current for the call (no switch when it already is)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _SAME_DEVICE
+    return torch.cuda.device(device)
 
 
 def _check(rc: int, where: str):
@@ -118,6 +136,9 @@ def _check(rc: int, where: str):
 
 
 def _check_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int):
+    if (isinstance(t, torch.Tensor) and t.dtype == dtype and t.dim() == dim and t.is_cuda
+            and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -202,7 +223,7 @@ def router_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], k
         raise ValueError("x and w disagree on H")
     _check_bias(bias, E)
     inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = load().router_fwd(_ptr(x), _ptr(w), _ptr(bias), M, H, E, int(k), int(scoring),
                                int(bool(renorm)), _ptr(inds), _ptr(wts), _ptr(logits),
                                _stream(x.device))
@@ -224,7 +245,7 @@ def router_fwd_noalloc(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Te
         raise ValueError("x and w disagree on H")
     _check_bias(bias, E)
     inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = load().router_fwd_noalloc(_ptr(x), _ptr(w), _ptr(bias), M, H, E, int(k), int(scoring),
                                        int(bool(renorm)), _ptr(inds), _ptr(wts), _ptr(logits),
                                        _stream(x.device))
@@ -254,7 +275,7 @@ def router_fwd_mxfp4(x: torch.Tensor, w_fp4: torch.Tensor, w_scale: torch.Tensor
         raise ValueError("w_fp4 must be [E, H/2] and w_scale [E, H/32]")
     _check_bias(bias, E)
     inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = load().router_fwd_mxfp4(_ptr(x), _ptr(w_fp4), _ptr(w_scale), _ptr(bias), M, H, E,
                                      int(k), int(scoring), int(bool(renorm)), _ptr(inds), _ptr(wts),
                                      _ptr(logits), _stream(x.device))
@@ -284,7 +305,7 @@ def router_fwd_mxfp8(x: torch.Tensor, w_fp8: torch.Tensor, w_scale: torch.Tensor
         raise ValueError("w_fp8 must be [E, H] and w_scale [E, H/32]")
     _check_bias(bias, E)
     inds, wts, logits = _outputs(M, k, E, x.device, out_inds, out_weights, return_logits, logits_out)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = load().router_fwd_mxfp8(_ptr(x), _ptr(w_fp8), _ptr(w_scale), _ptr(bias), M, H, E,
                                      int(k), int(scoring), int(bool(renorm)), _ptr(inds), _ptr(wts),
                                      _ptr(logits), _stream(x.device))
@@ -325,7 +346,7 @@ def router_fwd_route_table(x: torch.Tensor, w: torch.Tensor, bias: Optional[torc
         if t.shape[0] != cnt:
             raise ValueError(f"{name} must have {cnt} entries")
         tab[name] = t
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = load().router_fwd_route_table(
             _ptr(x), _ptr(w), _ptr(bias), M, H, E, int(k), int(scoring), int(bool(renorm)),
             _ptr(inds), _ptr(wts), _ptr(logits), _ptr(tab["unique_ids"]), _ptr(tab["token_mask"]),
@@ -364,7 +385,7 @@ def router_fwd_m2_table(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.T
         if t.shape[0] != n:
             raise ValueError(f"{name} must have {n} entries")
         tab[name] = t
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = load().router_fwd_m2_table(
             _ptr(x), _ptr(w), _ptr(bias), H, E, int(k), int(scoring), int(bool(renorm)),
             _ptr(inds), _ptr(wts), _ptr(logits), _ptr(tab["unique_ids"]), _ptr(tab["token_mask"]),
@@ -384,7 +405,7 @@ def router_topk_from_logits(logits: torch.Tensor, bias: Optional[torch.Tensor], 
     M, E = logits.shape
     _check_bias(bias, E)
     inds, wts, _ = _outputs(M, k, E, logits.device, out_inds, out_weights, False, None)
-    with torch.cuda.device(logits.device):
+    with _on(logits.device):
         rc = load().router_topk_from_logits(_ptr(logits), _ptr(bias), M, E, int(k), int(scoring),
                                             int(bool(renorm)), _ptr(inds), _ptr(wts),
                                             _stream(logits.device))
@@ -410,7 +431,7 @@ def router_gather_shared_add(y: torch.Tensor, slot_rows: torch.Tensor, weights: 
     _check_tensor(out, "out", torch.bfloat16, 2)
     if tuple(out.shape) != (M, D):
         raise ValueError("out must be [M, D]")
-    with torch.cuda.device(y.device):
+    with _on(y.device):
         rc = load().router_gather_shared_add(_ptr(y), R, _ptr(slot_rows), _ptr(weights), _ptr(shared),
                                              M, k, D, _ptr(out), _stream(y.device))
     _check(rc, "router_gather_shared_add")
@@ -437,7 +458,7 @@ def router_gather_shared_add_table(y: torch.Tensor, table: dict, weights: torch.
     if out is None:
         out = torch.empty((M, D), dtype=torch.bfloat16, device=y.device)
     _check_tensor(out, "out", torch.bfloat16, 2)
-    with torch.cuda.device(y.device):
+    with _on(y.device):
         rc = load().router_gather_shared_add_table(_ptr(y), _ptr(mask), _ptr(s2u), _ptr(cnt),
                                                    _ptr(weights), _ptr(shared), M, k, D, _ptr(out),
                                                    _stream(y.device))
@@ -466,7 +487,7 @@ def router_expert_gemm1_table(x: torch.Tensor, w1: torch.Tensor, table: dict, k:
     _check_tensor(out, "out", torch.bfloat16, 2)
     if out.shape[0] < M * k or out.shape[1] != F:
         raise ValueError("out must be at least [M*k, F]")
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = load().router_expert_gemm1_table(_ptr(x), _ptr(w1), E, F, D, _ptr(ids), _ptr(mask),
                                               _ptr(cnt), M, int(k), _ptr(out), _stream(x.device))
     _check(rc, "router_expert_gemm1_table")
