@@ -17,7 +17,9 @@
 //                   its value as a tagged 8-byte slot with a device-coherent
 //                   store, and the last arrival polls all G slots (lane L:
 //                   slots 4L..4L+3) until every tag is this launch's, then
-//                   writes their sum.
+//                   writes their sum;
+//   floor_handoff_fixed  the same publish and poll with no ticket: workgroup
+//                   0 is the finisher whatever the arrival order.
 // floor_latency: one wave times dependent round trips with the 100 MHz
 // realtime clock: a device-scope atomic, a device-coherent load of a line
 // another XCD wrote, and a plain load of a line not yet in any cache.
@@ -95,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void floor_read_kernel(const u32x4* w, in
     if (threadIdx.x == 0) out[blockIdx.x] = s;
 }
 
-// mode 0: ticket only; mode 1: ticket + tagged publish + poll.
+// mode 0: ticket only; mode 1: ticket + tagged publish + poll; mode 2: the
+// tagged publish and poll with no ticket, workgroup 0 the fixed finisher.
 // ctr: 16 * 17 words, zero between launches; slots: G 8-byte slots;
 // epoch: one word, advanced by the last arrival (tags are epoch + 1, never 0).
 __global__ __launch_bounds__(kThreads + 64) void floor_ticket_kernel(const u32x4* w, int n16, float* out,
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kThreads + 64) void floor_ticket_kernel(const u32x4
         if (lane == 0) {
             const uint32_t tag = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
             s_tag = tag;  // read before the ticket: the last arrival advances it
-            s_last = last_arrival(ctr) ? 1 : 0;
+            s_last = mode == 2 ? (blockIdx.x == 0 ? 1 : 0) : (last_arrival(ctr) ? 1 : 0);
         }
     }
     // the read (the control wave takes part in the barrier only)
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kThreads + 64) void floor_ticket_kernel(const u32x4
     }
     const int G = (int)gridDim.x;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(slots, 0, G * 8, 0x00020000);
-    if (mode == 1 && threadIdx.x == 0) {
+    if (mode >= 1 && threadIdx.x == 0) {
         const u32x2 v = {__float_as_uint(s), s_tag};
         __builtin_amdgcn_raw_buffer_store_b64(v, rs, (int)blockIdx.x * 8, 0, kCoherent);
     }
@@ -230,7 +233,7 @@ int floor_ticket(const void* w, int n16, int grid, float* out, uint32_t* ctr, vo
                  int mode, hipStream_t stream)
 {
     if (grid < 1 || grid > 256 || n16 < 1 || n16 > kThreads * kMaxLoads || !w || !out || !ctr || !slots ||
-        !epoch || (mode != 0 && mode != 1))
+        !epoch || mode < 0 || mode > 2)
         return -1;
     hipLaunchKernelGGL(floor_ticket_kernel, dim3(grid), dim3(kThreads + 64), 0, stream,
                        static_cast<const u32x4*>(w), n16, out, ctr, static_cast<u32x2*>(slots), epoch, mode);
