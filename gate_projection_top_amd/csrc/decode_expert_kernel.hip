@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kBlockOf<kRows>) void decode_expert_kernel(DecodeLa
     constexpr int kControlWave = kLoadWaves;
     constexpr int kWarmWave = kLoadWaves + 1;
     __shared__ float red[kLoadWaves][kRows];
-    __shared__ uint64_t sel[kWarmWave + 1][kFilterSlots];  // selection scratch, one per routing wave
+    __shared__ uint64_t sel[kWarmWave + 1][kRefineSlots];  // selection scratch, one per routing wave
     __shared__ int32_t slots[kWave];                      // route table: M*k <= 64 slots
     __shared__ int32_t tab_first[kMaxE + 1], tab_mask[kMaxE + 1];
     __shared__ uint32_t s_tag;

@@ -117,7 +117,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     __shared__ int polled[kDecodeTile];  // finisher: 1 = row's partials read, 2 = row gave up
     __shared__ int fin_index;  // this workgroup's finisher index, -1: not a finisher
     __shared__ uint32_t s_tag;  // this launch's tag (row block epoch)
-    __shared__ uint64_t sel[kWaves][kFilterSlots];  // selection scratch, one per routing wave
+    __shared__ uint64_t sel[kWaves][kRefineSlots];  // selection scratch, one per routing wave
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);

@@ -264,22 +264,20 @@ __device__ __forceinline__ int count_at_least(const uint32_t (&c)[kPerLane], uin
            __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[3] >= T));
 }
 
-__device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uint32_t order, int k,
-                                              uint64_t* lds, int& my_idx, uint32_t& my_code)
+// The filter's threshold: T = top - D in code space with k <= n <= cap
+// codes at or above it (n returned), D moved by doubling, halving and
+// bisection; false when no try within the budget finds one.
+__device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], int k, uint32_t& T, int& n)
 {
-    const int lane = threadIdx.x & (kWave - 1);
     const uint32_t top = wave_max_u32(c[0]);
     // distances in code space: dlo gave fewer than k codes, dhi more than the cap
-    uint32_t D = 3u << 21, dlo = 0u, dhi = 0u, T = 1u;
-    int n = 0;
-    bool found = false;
+    uint32_t D = 3u << 21, dlo = 0u, dhi = 0u;
+    T = 1u;
+    n = 0;
     for (int t = 0; t < kFilterTries; ++t) {
         T = top > D ? top - D : 1u;  // valid codes are >= 1; absent entries are 0
         n = count_at_least(c, T);
-        if (n >= k && n <= kFilterCap) {
-            found = true;
-            break;
-        }
+        if (n >= k && n <= kFilterCap) return true;
         if (n < k) {
             if (T == 1u) break;  // fewer than k valid codes cannot happen; stop
             dlo = D;
@@ -290,6 +288,16 @@ __device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uin
         }
         if (dhi && dhi - dlo <= 1u) break;  // no threshold separates k..cap codes
     }
+    return false;
+}
+
+__device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uint32_t order, int k,
+                                              uint64_t* lds, int& my_idx, uint32_t& my_code)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t T = 1u;
+    int n = 0;
+    const bool found = filter_threshold(c, k, T, n);
     if (!found) return false;
     // compaction: lane L's candidates go to [at, ...), at counting the
     // candidates of the lower lanes, in slot order; its other entries go to
@@ -331,6 +339,109 @@ __device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uin
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
     const uint64_t got = lane < k ? lds[lane] : 0ull;
+    my_code = (uint32_t)(got >> 32);
+    my_idx = lane < k ? (int)(0xFFFFu - (uint32_t)got) : 0;
+    return true;
+}
+
+// Sqrt-softplus scores with a bias, decided with as little double precision
+// as the result allows.  Every key fl32(fl32(s) + b) is first bracketed from
+// an fp32 evaluation of s (hardware exp, log and square root; a series for
+// log1p of small arguments), whose relative error stays below 2^-17 for
+// |logit| <= 40, bracketed at 2^-13, plus one code of slack each way.  A
+// threshold T on the lower ends with at least k of them at or above it (the
+// filter's search) makes T a lower bound on the k-th largest exact key, so
+// only experts whose upper end reaches T can win.  Those candidates (at most
+// kFilterCap, one per lane after compaction) get their exact double score
+// and key, exactly as the all-double path computes them, and are ranked by
+// the filter's counting; lane j < k ends with the winner of rank j, its code
+// and its double score.  Results are bit-identical to the all-double path.
+// Returns false (outputs untouched) for rows with a logit beyond +-40 or too
+// many candidates; the caller then scores every expert in double.
+// `lds`: kRefineSlots 8-byte entries owned by this wave.
+constexpr int kRefineSlots = 3 * kFilterSlots + kMaxK;
+
+__device__ __forceinline__ bool select_refined_softplus(const float (&v)[kPerLane], const float (&bv)[kPerLane],
+                                                        const bool (&valid)[kPerLane], int k, uint64_t* lds,
+                                                        int& my_idx, uint32_t& my_code, double& my_u)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    bool far = false;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) far |= valid[j] && !(fabsf(v[j]) <= 40.0f);
+    if (__builtin_amdgcn_ballot_w64(far) != 0) return false;
+    uint32_t clo[kPerLane], chi[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const float l = v[j];
+        const float a = __expf(-fabsf(l));
+        // log1p(a): a - a^2/2 + a^3/3 - a^4/4 below 1/32 (truncation < a^5/5),
+        // log(1 + a) above
+        const float lp = a < 0.03125f ? a * (1.0f - a * (0.5f - a * (0.33333334f - a * 0.25f))) : __logf(1.0f + a);
+        const float sq = sqrtf(fmaxf(l, 0.0f) + lp);
+        const uint32_t lo = order_code(sq * (1.0f - 0x1p-13f) + bv[j]);
+        const uint32_t hi = order_code(sq * (1.0f + 0x1p-13f) + bv[j]);
+        clo[j] = valid[j] ? (lo > 1u ? lo - 1u : 1u) : 0u;
+        chi[j] = valid[j] ? hi + 1u : 0u;
+    }
+    uint32_t T = 1u;
+    int n = 0;
+    if (!filter_threshold(clo, k, T, n)) return false;
+    const int nc = count_at_least(chi, T);
+    if (nc > kFilterCap) return false;
+
+    uint64_t* cand = lds;                      // (logit bits, bias bits) of candidate i
+    uint64_t* cidx = lds + kFilterSlots;       // its expert index
+    uint64_t* table = lds + 2 * kFilterSlots;  // ranking words
+    double* urank = reinterpret_cast<double*>(lds + 3 * kFilterSlots);  // winners' scores by rank
+    uint32_t at = 0u;
+    bool take[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        take[j] = chi[j] >= T;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(take[j]);
+        at += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    }
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const uint32_t pos = take[j] ? at : (uint32_t)kFilterCap;
+        cand[pos] = ((uint64_t)__float_as_uint(v[j]) << 32) | __float_as_uint(bv[j]);
+        cidx[pos] = (uint64_t)(lane * kPerLane + j);
+        at += take[j] ? 1u : 0u;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    uint64_t word = 0ull;
+    double u = 0.0;
+    if (lane < nc) {
+        const uint64_t e = cand[lane];
+        const uint32_t id = (uint32_t)cidx[lane];
+        u = sqrt_softplus(__uint_as_float((uint32_t)(e >> 32)));
+        const float key = (float)u + __uint_as_float((uint32_t)e);
+        word = ((uint64_t)order_code(key) << 32) | (0xFFFFu - id);
+    }
+    table[(lane < kFilterCap) ? lane : kFilterCap] = word;  // zeros past the candidates
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    int rank = 0;
+#pragma unroll
+    for (int h = 0; h < kFilterCap; h += kFilterCap / 2) {
+        uint64_t q[kFilterCap / 2];
+#pragma unroll
+        for (int i = 0; i < kFilterCap / 2; ++i) q[i] = table[h + i];
+#pragma unroll
+        for (int i = 0; i < kFilterCap / 2; ++i) rank += q[i] > word ? 1 : 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    if (lane < nc && rank < k) {
+        cand[rank] = word;
+        urank[rank] = u;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    const uint64_t got = lane < k ? cand[lane] : 0ull;
+    my_u = lane < k ? urank[lane] : 0.0;
     my_code = (uint32_t)(got >> 32);
     my_idx = lane < k ? (int)(0xFFFFu - (uint32_t)got) : 0;
     return true;
@@ -605,6 +716,19 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     const bool softmax = s.scoring == kSoftmax;
     constexpr bool need_all = kNeedAll;
 
+    if constexpr (need_all && kStyle == kFilter) {
+        // sqrt-softplus with a bias: exact keys only where they can decide
+        if (!softmax) {
+            int ridx = 0;
+            uint32_t rcode = 0u;
+            double ru = 0.0;
+            if (select_refined_softplus(v, bv, valid, s.k, lds, ridx, rcode, ru)) {
+                const float w = s.renorm ? (float)(ru / rank_sum(ru)) : (float)ru;
+                return RowResult{ridx, w};
+            }
+        }
+    }
+
     float mx = 0.0f;  // softmax shift: the row's largest logit
     double Z = 1.0;
     double sc[kPerLane] = {0.0, 0.0, 0.0, 0.0};  // scores: the key's first term
@@ -737,7 +861,7 @@ __device__ __forceinline__ void row_unbiased_scores(const float (&v)[kPerLane], 
     __hip_atomic_store(ready, mark, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// lds: kFilterSlots entries owned by this wave (kFilter only).  ext_u,
+// lds: kRefineSlots entries owned by this wave (kFilter only).  ext_u,
 // ext_ready, ext_want: see route_row_impl (used only when the row needs no
 // score before its selection; ignored otherwise).
 template <RoundStyle kStyle = kRoundsLane>

@@ -15,7 +15,7 @@ constexpr int kTopkWaves = 4;
 
 __global__ __launch_bounds__(kTopkWaves * kWave) void topk_from_logits_kernel(TopkLaunch a)
 {
-    __shared__ uint64_t sel[kTopkWaves][kFilterSlots];  // selection scratch, one per wave
+    __shared__ uint64_t sel[kTopkWaves][kRefineSlots];  // selection scratch, one per wave
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};

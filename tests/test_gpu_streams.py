@@ -97,3 +97,43 @@ def test_stream_beyond_the_workspaces_is_refused_until_one_is_released(orc):
         torch.cuda.synchronize()
         for s in held:
             R.release_stream(s)
+
+
+def test_first_call_under_capture_is_refused_not_allocated():
+    """A fresh process whose first fused call is made under stream capture
+    gets ROUTER_ERR_NOT_INITIALIZED (no allocation inside the capture), and
+    after router_init the same capture succeeds and replays exactly."""
+    import os
+    import subprocess
+    import sys
+    code = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from gate_projection_top_amd import router as R
+x = torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda:0")
+w = torch.zeros((16, 256), dtype=torch.bfloat16, device="cuda:0")
+oi = torch.empty((1, 2), dtype=torch.int32, device="cuda:0")
+ow = torch.empty((1, 2), dtype=torch.float32, device="cuda:0")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+code = None
+try:
+    with torch.cuda.graph(g):
+        R.router_fwd(x, w, None, 2, out_inds=oi, out_weights=ow)
+except R.RouterError as exc:
+    code = exc.code
+print("first", code, flush=True)
+R.init()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    R.router_fwd(x, w, None, 2, out_inds=oi, out_weights=ow)
+g.replay()
+torch.cuda.synchronize()
+print("after", oi.cpu().tolist(), flush=True)
+"""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code, root], capture_output=True, text=True, timeout=240)
+    say(r.stdout.strip())
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert f"first {R.ERR_NOT_INITIALIZED}" in r.stdout, r.stdout
+    assert "after [[0, 1]]" in r.stdout, r.stdout

@@ -95,3 +95,47 @@ def test_permutation_and_no_duplicates():
     assert gi.min() >= 0 and gi.max() < 256
     for r in range(gi.shape[0]):
         assert len(set(gi[r].tolist())) == 16
+
+
+def _near_tie_softplus_rows(M, seed, E=256, k=8):
+    """Logits whose sqrt-softplus + bias keys crowd the cut after rank k: the
+    experts ranked k+1..k+4 get logits solved so that their keys land on the
+    k-th key, then nudged by 0..3 fp32 ulps either way, so the fp32 brackets
+    of the selection overlap and only the exact keys decide (ties included).
+    One row in eight carries a logit beyond 40 (the all-double path), and one
+    in eight gives the (k+1)-th expert the k-th expert's logit."""
+    rng = np.random.default_rng(seed)
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    logits = (rng.standard_normal((M, E)) * 2.0).astype(np.float32)
+
+    def keys(row):
+        s = np.sqrt(np.logaddexp(0.0, row.astype(np.float64))).astype(np.float32)
+        return (s + bias).astype(np.float32)
+
+    for t in range(M):
+        row = logits[t]
+        order = np.lexsort((np.arange(E), -keys(row).astype(np.float64)))
+        target = float(keys(row)[order[k - 1]])
+        for r, e in enumerate(order[k:k + 4]):
+            s_want = max(target - float(bias[e]), 1e-3)
+            l = np.float32(np.log(np.expm1(s_want * s_want)))
+            step = int(rng.integers(-3, 4))
+            row[e] = np.nextafter(l, np.float32(np.inf if step > 0 else -np.inf), dtype=np.float32) if step else l
+            for _ in range(abs(step) - 1):
+                row[e] = np.nextafter(row[e], np.float32(np.inf if step > 0 else -np.inf), dtype=np.float32)
+        if t % 8 == 3:
+            row[int(rng.integers(0, E))] = np.float32(rng.choice([-45.0, 41.5, 60.0]))
+        if t % 8 == 5:
+            row[order[k]] = row[order[k - 1]]  # the same logit at the cut, another bias
+    return logits, bias
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("k", [6, 8])
+def test_softplus_bias_near_ties(orc, renorm, k):
+    logits, bias = _near_tie_softplus_rows(512, seed=40 + k + int(renorm), k=k)
+    say(f"topk sqrt-softplus near ties k={k} renorm={renorm}")
+    gi, gw = R.router_topk_from_logits(f32_dev(logits), f32_dev(bias), k, W.SQRT_SOFTPLUS, renorm)
+    torch.cuda.synchronize()
+    ri, rw = orc.topk_from_logits(logits, bias, k, W.SQRT_SOFTPLUS, renorm)
+    check_topk(host(gi), host(gw), ri, rw, what=f"softplus near ties k={k} renorm={renorm}")
