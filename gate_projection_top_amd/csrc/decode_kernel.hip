@@ -140,11 +140,12 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
 
     // Finishers per row block: the last nfin workgroups to draw a ticket on
     // the block's row counter each route every nfin-th row, so that no wave
-    // of a finisher routes more than one row.  (The route table needs all
-    // rows in one workgroup: one finisher then.)
+    // of a finisher routes more than one row.  With the route table, every
+    // routing wave also publishes its row's indices as (index, tag) slots,
+    // and the last finisher collects them and builds the table.
     const int t0 = r * kDecodeTile;
     const int rows_here = min(kDecodeTile, a.M - t0);
-    const int nfin = a.table_ids ? 1 : min(B, rows_here);
+    const int nfin = min(B, rows_here);
 
     if (tid < kDecodeTile) polled[tid] = 0;
     if (wave == kLoadWaves) {
@@ -325,6 +326,9 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     const RowSpec spec{a.E, a.k, a.scoring, a.renorm, a.bias != nullptr};
     const bool mine = lane < 4 * B;  // the lane's expert group lies in a published block
     const u32x4 cleared = {0u, 0u, 0u, 0u};
+    // the table's (index, tag) slots (routed slot s = t*k + j of the block)
+    const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+        a.counters + kDecodeTableSlotWord, 0, a.table_ids ? 64 * 8 : 0, 0x00020000);
     // bias beyond E reads as 0 (out-of-range buffer loads return zero)
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
@@ -399,7 +403,10 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                     const int64_t o = (int64_t)(t0 + t) * a.k + lane;
                     a.inds[o] = -1;
                     a.weights[o] = __builtin_nanf("");
-                    if (a.table_ids) slots[t * a.k + lane] = -1;
+                    if (a.table_ids) {
+                        const u32x2 sv = {0xffffffffu, tag};
+                        __builtin_amdgcn_raw_buffer_store_b64(sv, trs, (t * a.k + lane) * 8, 0, kCoherent);
+                    }
                 }
                 continue;
             }
@@ -439,15 +446,43 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
             const int64_t o = (int64_t)(t0 + t) * a.k + lane;
             a.inds[o] = res.idx;
             a.weights[o] = res.w;
-            if (a.table_ids) slots[t * a.k + lane] = res.idx;  // table: M*k <= 64
+            if (a.table_ids) {
+                const u32x2 sv = {(uint32_t)res.idx, tag};
+                __builtin_amdgcn_raw_buffer_store_b64(sv, trs, (t * a.k + lane) * 8, 0, kCoherent);
+            }
         }
     }
 
-    if (a.table_ids) {  // table: M <= 16, so every row is in this row block
-        __syncthreads();
-        if (wave == 0)
-            emit_route_table(slots, a.M, a.k, tab_first, tab_mask, a.table_ids, a.table_mask,
-                             a.table_s2u, a.table_count);
+    if (a.table_ids && f == nfin - 1 && wave == 0) {
+        // Table (M <= 16: one row block): wave 0 of the last finisher (the
+        // last workgroup to draw a ticket, so every routing wave it waits on
+        // has started) waits until every routed slot carries this launch's
+        // tag (lane s: slot s), then builds the table.
+        const int nslots = a.M * a.k;
+        const uint64_t t_wait = __builtin_amdgcn_s_memrealtime();
+        int32_t id = -1;
+        for (;;) {
+            asm volatile("" ::: "memory");
+            const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(trs, lane * 8, 0, kCoherent);
+            const bool ok = lane >= nslots || sv[1] == tag;
+            if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+                id = (int32_t)sv[0];
+                break;
+            }
+            if (__builtin_amdgcn_s_memrealtime() - t_wait > a.wait_ticks) {
+                // a row never arrived: its slots read -1, as a given-up row's do
+                if (lane == 0)
+                    __hip_atomic_fetch_or(a.status, kStatusWaitLimit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                id = ok ? (int32_t)sv[0] : -1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        slots[lane] = id;
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        emit_route_table(slots, a.M, a.k, tab_first, tab_mask, a.table_ids, a.table_mask, a.table_s2u,
+                         a.table_count);
     }
 }
 

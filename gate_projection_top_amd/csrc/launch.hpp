@@ -118,18 +118,23 @@ constexpr int kDecodeMaxBlocks = 256 / kDecodeTile;  // expert blocks at E = 256
 // Arrival counters, one 64-byte line (16 4-byte words) apart: per (row
 // block, expert block), then per row block.
 constexpr int kDecodeCounterStride = 16;
-constexpr int kDecodeCounters =
+// ... then the unique-route table's (index, tag) slots, one per routed slot
+// t*k + j of the row block that builds it (M*k <= 64).
+constexpr int kDecodeTableSlotWord =
     kDecodeCounterStride * (kDecodeMaxRowBlocks * kDecodeMaxBlocks + kDecodeMaxRowBlocks);
+constexpr int kDecodeCounters = kDecodeTableSlotWord + 2 * 64;
 
 // One-expert-per-workgroup decode kernel: token counts up to kExpertMaxRows;
 // arrival counters for groups of kExpertGroup workgroups, one 64-byte line
 // (kExpertCounterStride 8-byte words) apart, then the group counter.
 constexpr int kExpertMaxRows = 8;
-// From this many tokens on, router_fwd takes the H-split kernel.  (At 8
-// tokens that kernel measured 6.1 us against 7.5 us here, with one finisher
-// per row; but the route table needs all rows in one finisher, and both
-// calls must give the same bytes, so both stay here up to kExpertMaxRows.)
-constexpr int kExpertSplitMinRows = kExpertMaxRows + 1;
+// From this many tokens on, router_fwd (and router_fwd_route_table, which
+// must give the same bytes) takes the H-split kernel: measured at H = 7168,
+// 5 to 8 tokens there take 6.5-6.6 us against 7.6-8.7 us here (one finisher
+// per row beats one workgroup routing every row); up to 4 tokens this kernel
+// is as fast or faster, and the allocation-free entry point (up to 4 tokens)
+// shares it.
+constexpr int kExpertSplitMinRows = 5;
 // Allocation-free decode entry point: up to this many tokens.
 constexpr int kNoAllocMaxRows = 4;
 constexpr int kExpertGroup = 16;

@@ -90,7 +90,7 @@ extern "C" {
 #define ROUTER_MAX_E 256
 #define ROUTER_MAX_K 16
 /* router_fwd runs a decode kernel up to this many tokens (one workgroup per
- * gate row up to 8 tokens, row blocks x expert blocks x H-splits from 9) and
+ * gate row up to 4 tokens, row blocks x expert blocks x H-splits from 5) and
  * the MFMA GEMM-with-epilogue prefill kernel above it. */
 #define ROUTER_DECODE_MAX_M 64
 /* router_fwd_route_table: at most this many tokens, and at most
@@ -134,7 +134,7 @@ int router_init(int device);
 int router_release_stream(hipStream_t stream);
 
 /* Fused router (gate projection + scoring + top-k + renorm in one launch).
- * Decode (M <= ROUTER_DECODE_MAX_M): the gate rows (and, from 9 tokens, H)
+ * Decode (M <= ROUTER_DECODE_MAX_M): the gate rows (and, from 5 tokens, H)
  * are split across workgroups, which publish their logits as tagged slots;
  * a finisher workgroup picked by an arrival ticket gathers a row's E logits
  * and runs the selection.  Prefill (larger M): one MFMA GEMM whose epilogue
