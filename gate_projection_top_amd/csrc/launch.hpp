@@ -112,7 +112,7 @@ int prefill_splits(int64_t M);
 // Decode geometry shared by the host (workspace sizing) and the launcher.
 constexpr int kDecodeTile = 16;        // rows per row block, experts per expert block
 constexpr int kDecodeMaxSplits = 8;    // H splits
-constexpr int kDecodeMaxM = 64;
+constexpr int kDecodeMaxM = 256;
 constexpr int kDecodeMaxRowBlocks = kDecodeMaxM / kDecodeTile;
 constexpr int kDecodeMaxBlocks = 256 / kDecodeTile;  // expert blocks at E = 256
 // Arrival counters, one 64-byte line (16 4-byte words) apart: per (row

@@ -22,7 +22,7 @@ struct DeviceWorkspace {
 
 constexpr int kMaxDevices = 64;
 constexpr size_t kPartialFloats =
-    (size_t)gpt::kDecodeMaxSplits * gpt::kDecodeMaxM * ROUTER_MAX_E * 2;  // (value, tag) pairs: 1 MiB
+    (size_t)gpt::kDecodeMaxSplits * gpt::kDecodeMaxM * ROUTER_MAX_E * 2;  // (value, tag) pairs: 4 MiB
 constexpr int kCounters = gpt::kDecodeCounters;
 constexpr size_t kPfPartialFloats =
     (size_t)gpt::kPrefillMaxPairs * gpt::kPrefillTileRows * ROUTER_MAX_E;  // 32 MiB
@@ -169,7 +169,11 @@ void decode_splits(int M, int KS, int E, int* S_out, int* ks_per_split_out, int*
     const gpt::DecodeGeometry g = gpt::kDecodeWide;
     const int R = (M + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int B = (E + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
-    int S = (g.target_workgroups + R * B - 1) / (R * B);
+    // Up to 4 row blocks: about the geometry's target workgroup count.  More
+    // row blocks: as many splits as keep one workgroup per CU (256), since a
+    // second workgroup on a CU shares its load path and doubles the launch
+    // (measured at 320 tokens: 36 us against 20 us at 256).
+    int S = R <= 4 ? (g.target_workgroups + R * B - 1) / (R * B) : 256 / (R * B);
     const int by_work = KS / g.load_waves > 1 ? KS / g.load_waves : 1;
     if (S > by_work) S = by_work;
     if (S > g.max_splits) S = g.max_splits;

@@ -34,7 +34,7 @@ MAX_STREAMS = 8  # ROUTER_MAX_STREAMS
 TABLE_MAX_M = 16
 TABLE_MAX_SLOTS = 64
 # router_fwd runs the decode kernel up to this many tokens (ROUTER_DECODE_MAX_M)
-DECODE_MAX_M = 64
+DECODE_MAX_M = 256
 
 EXPORTS = ("router_init", "router_fwd", "router_fwd_m2_table", "router_fwd_route_table",
            "router_fwd_mxfp4", "router_fwd_mxfp8", "router_topk_from_logits", "router_gather_shared_add",

@@ -92,7 +92,7 @@ extern "C" {
 /* router_fwd runs a decode kernel up to this many tokens (one workgroup per
  * gate row up to 4 tokens, row blocks x expert blocks x H-splits from 5) and
  * the MFMA GEMM-with-epilogue prefill kernel above it. */
-#define ROUTER_DECODE_MAX_M 64
+#define ROUTER_DECODE_MAX_M 256
 /* router_fwd_route_table: at most this many tokens, and at most
  * ROUTER_TABLE_MAX_SLOTS = M*k slots (one wavefront builds the table). */
 #define ROUTER_TABLE_MAX_M 16

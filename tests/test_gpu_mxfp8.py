@@ -7,7 +7,7 @@ fp32.  Workloads (seeded, synthetic): unit-RMS activations, W ~ N(0, 1/H)
 quantised to MXFP8; decode widths M in {1, 2, 4, 8, 16, 64}; H = 4096, 7168
 and ragged H (a last 128-block with one, two or three 32-blocks); E = 256,
 100 and 16; every finite E4M3 code (subnormals, both zeros, +-448) at
-ordinary and extreme scales; prefill sizes M in {65, 100, 333, 1000} (four
+ordinary and extreme scales; prefill sizes M in {257, 300, 333, 1000} (four
 K splits), 10000 (two) and 20000 (one), and M = 8192, H = 7168 on every
 row.
 """
@@ -94,7 +94,7 @@ def test_scoring_modes_and_experts(orc, scoring, with_bias, renorm, E, k):
                                    with_bias=with_bias, renorm=renorm))
 
 
-@pytest.mark.parametrize("M", [1, 3, 130])
+@pytest.mark.parametrize("M", [1, 3, 130, 390])
 def test_every_code(orc, M):
     # all finite codes, subnormals and -0 included, at 2^-14: the largest (448)
     # becomes 0.027 and the smallest (2^-9) 2^-23, so the weights have about the
@@ -121,7 +121,7 @@ def test_scale_extremes(orc):
     check_mx(orc, case)
 
 
-@pytest.mark.parametrize("M", [65, 100, 333, 1000])
+@pytest.mark.parametrize("M", [257, 300, 333, 1000])
 @pytest.mark.parametrize("scoring,with_bias", [(W.SOFTMAX, True), (W.SOFTMAX, False),
                                                (W.SQRT_SOFTPLUS, True)])
 def test_prefill_ragged(orc, M, scoring, with_bias):
@@ -134,7 +134,7 @@ def test_prefill_two_and_one_splits(orc, M, H):
     check_mx(orc, W.mxfp8_case(M, H=H, seed=M, with_bias=True))
 
 
-@pytest.mark.parametrize("M,H", [(100, 128), (1000, 128), (130, 256)])
+@pytest.mark.parametrize("M,H", [(300, 128), (1000, 128), (390, 256)])
 def test_prefill_splits_without_stages(orc, M, H):
     """Four K splits over one or two 64-wide stages: some splits have no stage
     and contribute zero partials, but still take part in the exchange."""
@@ -147,7 +147,7 @@ def test_prefill_experts(orc, E, k, scoring):
 
 
 def test_prefill_scale_extremes(orc):
-    case = W.mxfp8_case(130, H=1024, seed=16, E=64, k=8)
+    case = W.mxfp8_case(390, H=1024, seed=16, E=64, k=8)
     sc = case.scales.copy()
     sc[3, :] = 10
     sc[7, 5] = min(246, int(sc[7, 5]) + 40)
@@ -158,10 +158,10 @@ def test_prefill_scale_extremes(orc):
 
 def test_prefill_handover_path_matches(orc):
     """Zero exchange wait: every split but the last hands its rows over; results unchanged."""
-    case = W.mxfp8_case(200, H=1024, seed=17, with_bias=True)
+    case = W.mxfp8_case(520, H=1024, seed=17, with_bias=True)
     args = (bf16_dev(case.x), u8_dev(case.elems), u8_dev(case.scales), f32_dev(case.bias), case.k,
             case.scoring, case.renorm)
-    say("mxfp8 prefill hand-over M=200")
+    say("mxfp8 prefill hand-over M=520")
     ref = R.router_fwd_mxfp8(*args, return_logits=True)
     try:
         R.set_exchange_timeout_us(0)

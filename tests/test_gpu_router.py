@@ -136,7 +136,7 @@ def test_route_table_m2_matches_general(orc):
         assert torch.equal(a[name].view(torch.int32), b[name].view(torch.int32)), name
 
 
-@pytest.mark.parametrize("M", [65, 100, 333, 1000])
+@pytest.mark.parametrize("M", [257, 300, 333, 1000])
 @pytest.mark.parametrize("scoring,with_bias", [(W.SOFTMAX, True), (W.SOFTMAX, False),
                                                (W.SQRT_SOFTPLUS, True)])
 def test_prefill_ragged(orc, M, scoring, with_bias):
@@ -145,6 +145,21 @@ def test_prefill_ragged(orc, M, scoring, with_bias):
     if not with_bias:
         case.bias = None
     say(f"router prefill M={M} scoring={scoring} bias={with_bias}")
+    gi, gw, gl = run_fwd(case)
+    check_router(orc, case, gi, gw, gl)
+
+
+@pytest.mark.parametrize("M", [65, 100, 128, 129, 200, 256])
+@pytest.mark.parametrize("scoring,with_bias", [(W.SOFTMAX, True), (W.SQRT_SOFTPLUS, True),
+                                               (W.SOFTMAX, False)])
+def test_decode_many_row_blocks(orc, M, scoring, with_bias):
+    """65..256 tokens take the split decode kernel with 5..16 row blocks (and
+    one split per workgroup once the row blocks alone fill the CUs)."""
+    case = W.prefill_case(M=M, H=1024, seed=500 + M)
+    case.scoring = scoring
+    if not with_bias:
+        case.bias = None
+    say(f"router decode M={M} scoring={scoring} bias={with_bias}")
     gi, gw, gl = run_fwd(case)
     check_router(orc, case, gi, gw, gl)
 
@@ -158,7 +173,7 @@ def test_prefill_two_and_one_splits(orc, M, H):
     check_router(orc, case, gi, gw, gl)
 
 
-@pytest.mark.parametrize("M", [200, 8192])
+@pytest.mark.parametrize("M", [520, 8192])
 def test_prefill_handover_path_matches(orc, M):
     """Zero exchange wait: every split but the last hands its rows over; results unchanged."""
     case = W.prefill_case(M=M, H=1024 if M < 8192 else 7168, seed=77)
@@ -196,7 +211,7 @@ def test_prefill_full_size_every_row(orc, H):
 def test_fused_equals_unfused(orc):
     """Gate G-A analogue: router_fwd == router_topk_from_logits(router_fwd's own logits)."""
     cases = [W.decode_case(8, seed=11), W.biased_case(64, seed=12), W.metric_case(3),
-             W.prefill_case(M=200, H=512, seed=13)]
+             W.prefill_case(M=520, H=512, seed=13), W.prefill_case(M=200, H=512, seed=14)]
     for case in cases:
         say(f"fused vs unfused {case.name}")
         gi, gw, gl = run_fwd(case)
@@ -208,7 +223,8 @@ def test_fused_equals_unfused(orc):
 
 
 def test_logits_output_does_not_perturb():
-    for case in (W.decode_case(2, seed=21), W.biased_case(16, seed=22), W.prefill_case(M=96, H=512)):
+    for case in (W.decode_case(2, seed=21), W.biased_case(16, seed=22), W.prefill_case(M=96, H=512),
+                 W.prefill_case(M=384, H=512)):
         x, w, b = bf16_dev(case.x), bf16_dev(case.w), f32_dev(case.bias)
         say(f"logits on/off {case.name}")
         i1, w1 = R.router_fwd(x, w, b, case.k, case.scoring, case.renorm)

@@ -45,10 +45,13 @@ DECODE_EDGES = [
     (2, 64, 1, 1, SM, False, True),         # E = 1
     (5, 64, 17, 3, SSP, False, False),      # E = 17: two blocks, one mostly padding; raw weights
     (16, 7176, 256, 16, SM, True, True),    # k = 16, H just past 7168
-    (64, 4096, 255, 9, SSP, True, True),    # M at the decode limit, E % 4 != 0
+    (64, 4096, 255, 9, SSP, True, True),    # four row blocks, E % 4 != 0
+    (80, 1000, 100, 4, SSP, True, True),    # five row blocks: several splits per CU's share
+    (256, 520, 256, 8, SM, True, True),     # M at the decode limit: 16 row blocks, one split
+    (241, 256, 17, 16, SM, False, True),    # ragged last row block, k = 16 with E = 17
     (9, 4096, 256, 8, SM, False, False),    # softmax without renorm: full-row probabilities
-    (4, 4096, 256, 8, SM, True, True),      # largest narrow-geometry row block
-    (5, 4096, 256, 8, SM, True, True),      # smallest wide-geometry row block
+    (4, 4096, 256, 8, SM, True, True),      # the most tokens of the one-expert kernel
+    (5, 4096, 256, 8, SM, True, True),      # the fewest tokens of the split kernel
 ]
 
 
@@ -58,8 +61,8 @@ def test_decode_edges(orc, M, H, E, k, scoring, bias, renorm):
 
 
 PREFILL_EDGES = [
-    (65, 200, 256, 8, SM, True, True),      # first prefill size, H % 64 != 0
-    (129, 1000, 100, 4, SSP, True, True),   # ragged second tile, E % 16 != 0
+    (257, 200, 256, 8, SM, True, True),     # first prefill size, H % 64 != 0
+    (385, 1000, 100, 4, SSP, True, True),   # ragged fourth tile, E % 16 != 0
     (300, 520, 17, 16, SM, False, True),    # k = 16 with E = 17
     (1000, 64, 256, 1, SSP, False, False),  # k = 1, a single k-step
     (8192, 64, 256, 8, SM, True, True),     # 64 tiles: the last size with 4 splits

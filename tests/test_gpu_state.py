@@ -36,7 +36,8 @@ def _shapes():
     fwd_case("biased M=16", W.biased_case(16, seed=8), logits=False)
     fwd_case("ragged E=100 k=4 M=3 H=256", W.decode_case(3, H=256, seed=9, E=100, k=4))
     fwd_case("tiny E=16 k=2", W.tiny_case(1))
-    fwd_case("prefill M=200 H=512", W.prefill_case(M=200, H=512, seed=10))
+    fwd_case("decode M=200 H=512", W.prefill_case(M=200, H=512, seed=10))
+    fwd_case("prefill M=520 H=512", W.prefill_case(M=520, H=512, seed=12))
 
     case = W.biased_case(2, seed=11)
     x, w, b = bf16_dev(case.x), bf16_dev(case.w), f32_dev(case.bias)
