@@ -160,7 +160,7 @@ constexpr DecodeGeometry kDecodeWide{8, 128, kDecodeMaxSplits};
 // Prefill geometry: 128-row tiles; K split S ways while tiles * S <= 256.
 constexpr int kPrefillTileRows = 128;
 constexpr int kPrefillMaxPairs = 256;          // (tile, split) pairs with published partials
-constexpr int kPrefillCountersPerTile = 8;     // arrive, done, abandoned[4], pad
+constexpr int kPrefillCountersPerTile = 32;    // arrive, done, abandoned[16], pad
 constexpr int kPrefillMaxSplitTiles = kPrefillMaxPairs / 2;
 
 }  // namespace gpt

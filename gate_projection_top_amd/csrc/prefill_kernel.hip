@@ -8,7 +8,8 @@
 // logits meet in one workgroup.  With E = 256 columns only, a 32-row tile
 // would re-read the whole gate matrix from L2 for every 32 tokens; 128-row
 // tiles cut that traffic 4x.  To still occupy every CU, the K (= H) range of
-// a tile is split S ways (S = 4 for <= 64 tiles): S workgroups of 8 waves
+// a tile is split S ways (S = 16, 8, 4 or 2: as many as the exchange buffer's
+// 256 (tile, split) pairs allow for the tile count): S workgroups of 8 waves
 // each compute the tile's 128 x 256 partial over their K slice.  The waves
 // split the work by role: four producers issue every load of the LDS rings,
 // so that only they ever queue on the memory pipeline, and four compute
@@ -196,7 +197,7 @@ __device__ __forceinline__ void route_tile_rows(const PrefillLaunch& p, float* t
 }
 
 // ---------------------------------------------------------------------------
-// split exchange (S = 2 or 4 splits of one 128-row tile)
+// split exchange (S = 2, 4, 8 or 16 splits of one 128-row tile)
 // ---------------------------------------------------------------------------
 // Sum every split's partial of tile-local rows [r0, r0 + rows) in split order
 // into the LDS tile (hand-over path: all splits published these rows).
@@ -231,11 +232,56 @@ __device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, float*
                                                   int s, int64_t row0, int r0, int rows, int wave,
                                                   int lane, const float (&bv)[kPerLane])
 {
-    constexpr int G = 4;
     const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(p.partials);
     const RowSpec spec{p.E, p.k, p.scoring, p.renorm, p.bias != nullptr};
     const int col = lane * kPerLane;
     const int r_end = r0 + rows;
+    if constexpr (S >= 8) {
+        // 16 or 8 own rows: wave w takes rows w and w + 8 (two in lockstep)
+        // or w alone, every other split's partial of them loaded at once
+        constexpr int G = kBM / S / kWaves;
+        static_assert(G >= 1 && G <= kRowGroup, "rows per wave");
+        f32x4 part[G][S];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int t = r0 + wave + g * kWaves;
+#pragma unroll
+            for (int q = 0; q < S; ++q)
+                if (q != s && t < r_end) part[g][q] = fetch4(prs, partial_off(p, tile, q, t, col));
+        }
+        float v[G][kPerLane];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int t = r0 + wave + g * kWaves;
+            if (t >= r_end) {
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j) v[g][j] = 0.f;
+                continue;
+            }
+            const f32x4 mine = *reinterpret_cast<const f32x4*>(&tile_f[t * kTileStride + col]);
+            f32x4 sum = (s == 0) ? mine : part[g][0];
+#pragma unroll
+            for (int q = 1; q < S; ++q) sum += (q == s) ? mine : part[g][q];
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) v[g][j] = col + j < p.E ? sum[j] : 0.f;
+            if (p.logits_out && row0 + t < p.M) {
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j)
+                    if (col + j < p.E) p.logits_out[(row0 + t) * p.E + col + j] = v[g][j];
+            }
+        }
+        RowResult res[G];
+        route_rows<G, kFilter>(v, bv, spec, res, wave_sel(tile_f, wave));
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int t = r0 + wave + g * kWaves;
+            if (t >= r_end || row0 + t >= p.M || lane >= p.k) continue;
+            p.inds[(row0 + t) * p.k + lane] = res[g].idx;
+            p.weights[(row0 + t) * p.k + lane] = res[g].w;
+        }
+        return;
+    }
+    constexpr int G = 4;
     f32x4 cur[G][S], nxt[G][S];
     auto issue = [&](int t0, f32x4 (&dst)[G][S]) {
 #pragma unroll
@@ -304,7 +350,8 @@ __device__ __forceinline__ void exchange_and_route(const PrefillLaunch& p, float
 {
     constexpr int kRowsPer = kBM / S;
     constexpr int kVecPerRow = kBN / 4;
-    constexpr int kPubCells = (kBM - kRowsPer) * kVecPerRow / kThreads;  // 12 (S=4) or 8 (S=2)
+    constexpr int kPubCells = (kBM - kRowsPer) * kVecPerRow / kThreads;  // 8, 12, 14, 15 (S = 2..16)
+    static_assert((kBM - kRowsPer) * kVecPerRow % kThreads == 0, "published cells per thread");
     const int my_r0 = s * kRowsPer;
     uint32_t* arrive = p.counters + tile * kPrefillCountersPerTile;
     uint32_t* done = arrive + 1;
@@ -613,7 +660,11 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
         route_tile_rows(p, tile_f, row0, 0, kBM, wave, lane, bv);
         return;
     }
-    if (p.S == 4)
+    if (p.S == 16)
+        exchange_and_route<16>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
+    else if (p.S == 8)
+        exchange_and_route<8>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
+    else if (p.S == 4)
         exchange_and_route<4>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
     else
         exchange_and_route<2>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
@@ -621,11 +672,15 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
 
 }  // namespace
 
+// K splits per tile: as many as keep (tiles, padded to the 8 XCDs) x splits
+// within the 256 (tile, split) pairs of the exchange buffer, so few tiles
+// still fill the CUs.
 int prefill_splits(int64_t M)
 {
     const int64_t tiles = (M + kBM - 1) / kBM;
-    if (tiles <= kPrefillMaxPairs / 4) return 4;
-    if (tiles <= kPrefillMaxPairs / 2) return 2;
+    const int64_t padded = (tiles + kXcds - 1) / kXcds * kXcds;
+    for (int S = 16; S >= 2; S /= 2)
+        if (padded * S <= kPrefillMaxPairs) return S;
     return 1;
 }
 

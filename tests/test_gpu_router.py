@@ -136,10 +136,11 @@ def test_route_table_m2_matches_general(orc):
         assert torch.equal(a[name].view(torch.int32), b[name].view(torch.int32)), name
 
 
-@pytest.mark.parametrize("M", [257, 300, 333, 1000])
+@pytest.mark.parametrize("M", [257, 300, 333, 1000, 2100, 4000])
 @pytest.mark.parametrize("scoring,with_bias", [(W.SOFTMAX, True), (W.SOFTMAX, False),
                                                (W.SQRT_SOFTPLUS, True)])
 def test_prefill_ragged(orc, M, scoring, with_bias):
+    """257-2048 tokens take 16 K splits per tile, up to 4096 eight, then four."""
     case = W.prefill_case(M=M, H=1024, seed=M)
     case.scoring = scoring
     if not with_bias:
