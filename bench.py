@@ -30,9 +30,10 @@ Also reported (same JSON line):
                 routed gather + shared-expert add at M=2 (explicit rows, all
                 remote, table rows) and at M=4096, the expert GEMM1 on the
                 table at M=2 (F=4096, D=7168, 15 GB of expert weights), the
-                standalone top-k at M=4096, and the 8192-token prefill
+                standalone top-k at M=4096, the 8192-token prefill
                 (tokens/s, fraction of bf16 MFMA and HBM peak, and a roofline
-                block of its own).
+                block of its own), and router_fwd across batch sizes from 16
+                to 4096 tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
 """
@@ -74,7 +75,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--section", choices=["all", "decode", "widths", "mxfp4", "mxfp8", "gather", "gemm1", "prefill",
-                                          "topk", "floor"],
+                                          "topk", "floor", "sizes"],
                     default="all",
                     help="restrict to one workload (for counter-collection runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -227,6 +228,8 @@ def main():
         out["extras"].update(topk_extras(torch, R, W, dev, args))
     if args.section in ("all", "prefill"):
         out["extras"].update(prefill_extras(torch, R, W, dev, args))
+    if args.section in ("all", "sizes"):
+        out["extras"].update(size_extras(torch, R, W, dev, args))
     if args.section == "all" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
         out["extras"]["cpu_baseline_all_threads"] = cpu_baseline_threads(W, args.cpu_seconds)
@@ -641,6 +644,26 @@ def prefill_extras(torch, R, W, dev, args):
     except RuntimeError as exc:  # library GEMM not capturable
         log(f"torch.mm context skipped: {exc}")
     log("prefill done")
+    return ex
+
+
+def size_extras(torch, R, W, dev, args):
+    """router_fwd across batch sizes (H=7168, E=256, k=8, softmax with a
+    U(-0.02,0.02) bias, one activation per size, four calls per graph): which
+    kernel takes each size and what it costs."""
+    ex = {}
+    H, E, k = 7168, 256, 8
+    w = W.torch_gaussian_bf16((E, H), 1.0 / H ** 0.5, seed=21, device=dev)
+    b = W.torch_uniform_f32(E, -0.02, 0.02, seed=22, device=dev)
+    for M in (16, 64, 128, 256, 257, 512, 1024, 2048, 4096):
+        x = W.torch_gaussian_bf16((M, H), 1.0, seed=23, device=dev)
+        oi = torch.empty((M, k), dtype=torch.int32, device=dev)
+        ow = torch.empty((M, k), dtype=torch.float32, device=dev)
+        us = graph_call_us(torch, [lambda: R.router_fwd(x, w, b, k, W.SOFTMAX, True, out_inds=oi, out_weights=ow)] * 4,
+                           max(args.steps // 2, 2), 2)
+        ex[f"sizes_M{M}_H7168_us_per_call"] = round(us, 2)
+        del x
+    log("sizes done")
     return ex
 
 
