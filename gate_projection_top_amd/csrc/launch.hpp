@@ -146,18 +146,19 @@ constexpr uint32_t kStatusWaitLimit = 1u;  // a finisher stopped waiting at the 
 // Default bound on a decode finisher's wait: 100 ms (100 MHz realtime clock).
 constexpr uint32_t kDecodeWaitTicksDefault = 10000000u;
 
-// Split decode geometry (more than kExpertMaxRows tokens): about 128
-// workgroups of 8 load waves, so the finisher has enough waves to route 16
-// rows; each workgroup also has one control wave (which routes a row too).
-// Sweeps of 4/6/7/8/16 load waves and 64/128/256 workgroups chose these.
+// Split decode geometry (kExpertSplitMinRows tokens and more): workgroups of
+// 8 load waves, so a finisher has enough waves to route its rows, plus one
+// control wave; as many H-splits (up to max_splits) as keep the grid within
+// target_workgroups, one per CU.
 struct DecodeGeometry {
     int load_waves;
     int target_workgroups;
     int max_splits;
 };
-constexpr DecodeGeometry kDecodeWide{8, 128, kDecodeMaxSplits};
+constexpr DecodeGeometry kDecodeWide{8, 256, kDecodeMaxSplits};
 
-// Prefill geometry: 128-row tiles; K split S ways while tiles * S <= 256.
+// Prefill geometry: 128-row tiles; K split S ways (16, 8, 4 or 2) while
+// tiles (padded to the 8 XCDs) * S <= 256.
 constexpr int kPrefillTileRows = 128;
 constexpr int kPrefillMaxPairs = 256;          // (tile, split) pairs with published partials
 constexpr int kPrefillCountersPerTile = 32;    // arrive, done, abandoned[16], pad

@@ -169,11 +169,12 @@ void decode_splits(int M, int KS, int E, int* S_out, int* ks_per_split_out, int*
     const gpt::DecodeGeometry g = gpt::kDecodeWide;
     const int R = (M + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
     const int B = (E + gpt::kDecodeTile - 1) / gpt::kDecodeTile;
-    // Up to 4 row blocks: about the geometry's target workgroup count.  More
-    // row blocks: as many splits as keep one workgroup per CU (256), since a
-    // second workgroup on a CU shares its load path and doubles the launch
-    // (measured at 320 tokens: 36 us against 20 us at 256).
-    int S = R <= 4 ? (g.target_workgroups + R * B - 1) / (R * B) : 256 / (R * B);
+    // As many splits as keep one workgroup per CU (256): a second workgroup
+    // on a CU shares its load path (measured at 320 tokens: 36 us against 20
+    // us at 256), while more workgroups up to that point shorten each one's
+    // k range (32-64 tokens: 9.8-13.1 us at 128 workgroups, 8.6-10.0 us at
+    // 256).
+    int S = g.target_workgroups / (R * B);
     const int by_work = KS / g.load_waves > 1 ? KS / g.load_waves : 1;
     if (S > by_work) S = by_work;
     if (S > g.max_splits) S = g.max_splits;
