@@ -266,10 +266,12 @@ __device__ __forceinline__ int count_at_least(const uint32_t (&c)[kPerLane], uin
 
 // The filter's threshold: T = top - D in code space with k <= n <= cap
 // codes at or above it (n returned), D moved by doubling, halving and
-// bisection; false when no try within the budget finds one.
-__device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], int k, uint32_t& T, int& n)
+// bisection; false when no try within the budget finds one.  top: the
+// largest code of the row (returned).
+__device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], int k, uint32_t& T, int& n,
+                                                 uint32_t& top)
 {
-    const uint32_t top = wave_max_u32(c[0]);
+    top = wave_max_u32(max(max(c[0], c[1]), max(c[2], c[3])));
     // distances in code space: dlo gave fewer than k codes, dhi more than the cap
     uint32_t D = 3u << 21, dlo = 0u, dhi = 0u;
     T = 1u;
@@ -291,13 +293,79 @@ __device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], 
     return false;
 }
 
-__device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uint32_t order, int k,
-                                              uint64_t* lds, int& my_idx, uint32_t& my_code)
+// Rank of each candidate word among the n (k <= n <= kFilterCap) words of
+// `table` (entries n .. kFilterCap-1 zero, below every word): the number of
+// words above it.  With span = 16 when n <= 16, else 32, lane L holds
+// candidate L mod span (`mine`), and the 64/span lanes holding the same
+// candidate each compare it with their own slice of the table (4 or 16
+// entries, one round of reads), their counts summed across the wave's rows
+// with the permlane swaps; every lane ends with its candidate's rank.
+// `between(mine)` runs while the reads are in flight (the scheduling
+// barriers keep it there).
+template <class F>
+__device__ __forceinline__ int filter_rank(const uint64_t* table, int n, uint64_t& mine, F&& between)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    uint32_t T = 1u;
+    uint32_t part = 0u;
+    if (n <= 16) {
+        const int p = lane >> 4;
+        mine = table[lane & 15];
+        uint64_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = table[4 * p + i];
+        between(mine);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += q[i] > mine ? 1u : 0u;
+        const auto r = __builtin_amdgcn_permlane16_swap(part, part, false, false);  // rows 0+1, 2+3
+        part = r[0] + r[1];
+    } else {
+        const int p = lane >> 5;
+        mine = table[lane & 31];
+        uint64_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = table[16 * p + i];
+        between(mine);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part += q[i] > mine ? 1u : 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = table[16 * p + 8 + i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part += q[i] > mine ? 1u : 0u;
+    }
+    const auto h = __builtin_amdgcn_permlane32_swap(part, part, false, false);  // halves 0+1
+    return (int)(h[0] + h[1]);
+}
+
+// The first k candidates to lanes 0 .. k-1 by rank: lane L < n (which holds
+// candidate L, L < span) with rank r < k sends its value to lane r through
+// the LDS crossbar (ds_permute, no LDS memory); every other lane sends to
+// lane 63, which no rank reaches (k <= 16).
+__device__ __forceinline__ uint32_t push_by_rank(int dst, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_ds_permute(dst << 2, (int)v);
+}
+
+__device__ __forceinline__ uint64_t push_by_rank64(int dst, uint64_t v)
+{
+    const uint32_t lo = push_by_rank(dst, (uint32_t)v), hi = push_by_rank(dst, (uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// kScore (rows with no bias, so that a candidate's key is its logit):
+// kSoftmax or kSqrtSoftplus has each candidate's unbiased score computed too,
+// exp(l - max l) in double or sqrt(softplus(l)), while the ranking's reads
+// are in flight; it travels with the candidate to its rank (my_u; 0 past
+// rank k-1), so the winners' scores cost no time after the selection.
+// kScore < 0: no scores.
+template <int kScore>
+__device__ __forceinline__ bool select_filter_impl(const uint32_t (&c)[kPerLane], uint32_t order, int k,
+                                                   uint64_t* lds, int& my_idx, uint32_t& my_code, double& my_u)
+{
+    constexpr bool kScored = kScore >= 0;
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t T = 1u, top = 0u;
     int n = 0;
-    const bool found = filter_threshold(c, k, T, n);
+    const bool found = filter_threshold(c, k, T, n, top);
     if (!found) return false;
     // compaction: lane L's candidates go to [at, ...), at counting the
     // candidates of the lower lanes, in slot order; its other entries go to
@@ -321,27 +389,38 @@ __device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uin
     lds[(lane >= n && lane < kFilterCap) ? lane : kFilterCap] = 0ull;
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    // every lane reads the table (broadcast reads, half of it per batch to
-    // bound the registers) and ranks its own entry: the number above it
-    const uint64_t mine = lds[lane & (kFilterCap - 1)];
-    int rank = 0;
-#pragma unroll
-    for (int h = 0; h < kFilterCap; h += kFilterCap / 2) {
-        uint64_t q[kFilterCap / 2];
-#pragma unroll
-        for (int i = 0; i < kFilterCap / 2; ++i) q[i] = lds[h + i];
-#pragma unroll
-        for (int i = 0; i < kFilterCap / 2; ++i) rank += q[i] > mine ? 1 : 0;
+    double u = 0.0;
+    uint64_t mine = 0ull;
+    const int rank = filter_rank(lds, n, mine, [&](uint64_t w) {
+        if constexpr (kScored) {
+            __builtin_amdgcn_sched_barrier(0);
+            const float l = order_value((uint32_t)(w >> 32));
+            if constexpr (kScore == kSoftmax)
+                u = exp((double)l - (double)order_value(top));
+            else
+                u = sqrt_softplus(l);
+            asm volatile("" ::"v"(u));  // computed here, not where it is used
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    });
+    const int dst = (lane < n && rank < k) ? rank : kWave - 1;
+    const uint64_t got = push_by_rank64(dst, mine);
+    if constexpr (kScored) {
+        const uint64_t ub = push_by_rank64(dst, __builtin_bit_cast(uint64_t, u));
+        my_u = lane < k ? __builtin_bit_cast(double, ub) : 0.0;
     }
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-    if (lane < n && rank < k) lds[rank] = mine;
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-    const uint64_t got = lane < k ? lds[lane] : 0ull;
-    my_code = (uint32_t)(got >> 32);
+    my_code = lane < k ? (uint32_t)(got >> 32) : 0u;
     my_idx = lane < k ? (int)(0xFFFFu - (uint32_t)got) : 0;
+    // the table is rewritten by the next selection on this wave's entries:
+    // LDS operations of one wave complete in order
     return true;
+}
+
+__device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uint32_t order, int k,
+                                              uint64_t* lds, int& my_idx, uint32_t& my_code)
+{
+    double unused = 0.0;
+    return select_filter_impl<-1>(c, order, k, lds, my_idx, my_code, unused);
 }
 
 // Sqrt-softplus scores with a bias, decided with as little double precision
@@ -359,7 +438,7 @@ __device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uin
 // Returns false (outputs untouched) for rows with a logit beyond +-40 or too
 // many candidates; the caller then scores every expert in double.
 // `lds`: kRefineSlots 8-byte entries owned by this wave.
-constexpr int kRefineSlots = 3 * kFilterSlots + kMaxK;
+constexpr int kRefineSlots = 3 * kFilterSlots;
 
 __device__ __forceinline__ bool select_refined_softplus(const float (&v)[kPerLane], const float (&bv)[kPerLane],
                                                         const bool (&valid)[kPerLane], int k, uint64_t* lds,
@@ -384,16 +463,15 @@ __device__ __forceinline__ bool select_refined_softplus(const float (&v)[kPerLan
         clo[j] = valid[j] ? (lo > 1u ? lo - 1u : 1u) : 0u;
         chi[j] = valid[j] ? hi + 1u : 0u;
     }
-    uint32_t T = 1u;
+    uint32_t T = 1u, top = 0u;
     int n = 0;
-    if (!filter_threshold(clo, k, T, n)) return false;
+    if (!filter_threshold(clo, k, T, n, top)) return false;
     const int nc = count_at_least(chi, T);
     if (nc > kFilterCap) return false;
 
     uint64_t* cand = lds;                      // (logit bits, bias bits) of candidate i
     uint64_t* cidx = lds + kFilterSlots;       // its expert index
     uint64_t* table = lds + 2 * kFilterSlots;  // ranking words
-    double* urank = reinterpret_cast<double*>(lds + 3 * kFilterSlots);  // winners' scores by rank
     uint32_t at = 0u;
     bool take[kPerLane];
 #pragma unroll
@@ -423,26 +501,14 @@ __device__ __forceinline__ bool select_refined_softplus(const float (&v)[kPerLan
     table[(lane < kFilterCap) ? lane : kFilterCap] = word;  // zeros past the candidates
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    int rank = 0;
-#pragma unroll
-    for (int h = 0; h < kFilterCap; h += kFilterCap / 2) {
-        uint64_t q[kFilterCap / 2];
-#pragma unroll
-        for (int i = 0; i < kFilterCap / 2; ++i) q[i] = table[h + i];
-#pragma unroll
-        for (int i = 0; i < kFilterCap / 2; ++i) rank += q[i] > word ? 1 : 0;
-    }
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-    if (lane < nc && rank < k) {
-        cand[rank] = word;
-        urank[rank] = u;
-    }
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-    const uint64_t got = lane < k ? cand[lane] : 0ull;
-    my_u = lane < k ? urank[lane] : 0.0;
-    my_code = (uint32_t)(got >> 32);
+    // lane j < nc holds candidate j and its score (nc <= the ranking's span)
+    uint64_t mine = 0ull;
+    const int rank = filter_rank(table, nc, mine, [](uint64_t) {});
+    const int dst = (lane < nc && rank < k) ? rank : kWave - 1;
+    const uint64_t got = push_by_rank64(dst, mine);
+    const uint64_t ub = push_by_rank64(dst, __builtin_bit_cast(uint64_t, u));
+    my_u = lane < k ? __builtin_bit_cast(double, ub) : 0.0;
+    my_code = lane < k ? (uint32_t)(got >> 32) : 0u;
     my_idx = lane < k ? (int)(0xFFFFu - (uint32_t)got) : 0;
     return true;
 }
@@ -694,19 +760,13 @@ __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const 
 
 // One row: the same steps as route_rows, written for a single row (the
 // generic form costs the single-row decode path ~0.3 us of latency).  The
-// two give bit-identical results on identical inputs.
-//
-// ext_u (optional, only where no score is needed before the selection, i.e.
-// !kNeedAll): the row's unbiased scores by expert, written by another wave
-// with row_unbiased_scores() below; this wave waits until *ext_ready reaches
-// ext_want and then reads its winner's score from there instead of
-// computing it.  The scores are the same function of the same logits, so the
-// result is bit-identical either way.
+// two give bit-identical results on identical inputs.  Without a bias the
+// filter also scores its candidates (select_filter_impl<true>), which takes
+// the winners' scores off the end of the routing.
 template <bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
                                                     const float (&bv)[kPerLane], const RowSpec& s,
-                                                    uint64_t* lds, const double* ext_u = nullptr,
-                                                    int* ext_ready = nullptr, int ext_want = 0)
+                                                    uint64_t* lds)
 {
     const int lane = threadIdx.x & (kWave - 1);
     bool valid[kPerLane];
@@ -777,7 +837,17 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     // the filter needs no order inside a lane (its words carry the index);
     // the lane's entries are sorted only for the rounds
     bool selected = false;
-    if constexpr (kStyle == kFilter) selected = select_filter(c, 0xE4u, s.k, lds, my_idx, my_code);
+    if constexpr (kStyle == kFilter) {
+        double su = 0.0;  // the winner's unbiased score, when the filter scored its candidates
+        if constexpr (need_all) {
+            selected = select_filter_impl<-1>(c, 0xE4u, s.k, lds, my_idx, my_code, su);
+        } else {
+            // no bias: softmax with renorm, or sqrt-softplus
+            selected = softmax ? select_filter_impl<kSoftmax>(c, 0xE4u, s.k, lds, my_idx, my_code, su)
+                               : select_filter_impl<kSqrtSoftplus>(c, 0xE4u, s.k, lds, my_idx, my_code, su);
+            if (selected) return RowResult{my_idx, s.renorm ? (float)(su / rank_sum(su)) : (float)su};
+        }
+    }
     if (!selected) {
         order_pair(c[0], slot[0], c[1], slot[1]);
         order_pair(c[2], slot[2], c[3], slot[3]);
@@ -814,10 +884,6 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
         }
         u = j == 0 ? got[0] : (j == 1 ? got[1] : (j == 2 ? got[2] : got[3]));
         if (lane >= s.k) u = 0.0;
-    } else if (ext_u) {
-        while (__hip_atomic_load(ext_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < ext_want)
-            __builtin_amdgcn_s_sleep(1);
-        if (lane < s.k) u = ext_u[my_idx];
     } else {
         if (softmax) mx = order_value(readlane_u32(my_code, 0));  // rank 0 holds the max
         if (lane < s.k) {
@@ -835,51 +901,14 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     return RowResult{my_idx, w};
 }
 
-// Every expert's unbiased score of one row (lane L: experts 4L..4L+3) into
-// u[e], for a row whose selection needs no score (no bias, and renorm on or
-// sqrt-softplus scoring): exp(l - max l) or sqrt(softplus(l)), in double,
-// as route_row_impl computes them for its winners.  Then *ready is raised
-// to `mark` (workgroup scope, after the stores).
-__device__ __forceinline__ void row_unbiased_scores(const float (&v)[kPerLane], const RowSpec& s, double* u,
-                                                    int* ready, int mark)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const bool softmax = s.scoring == kSoftmax;
-    float mx = 0.0f;
-    if (softmax) {
-        uint32_t m = 0u;
-#pragma unroll
-        for (int j = 0; j < kPerLane; ++j)
-            if (lane * kPerLane + j < s.E) m = max(m, order_code(v[j]));
-        mx = order_value(wave_max_u32(m));
-    }
-#pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-        const double x = softmax ? exp((double)v[j] - (double)mx) : sqrt_softplus(v[j]);
-        if (lane * kPerLane + j < s.E) u[lane * kPerLane + j] = x;
-    }
-    __hip_atomic_store(ready, mark, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// lds: kRefineSlots entries owned by this wave (kFilter only).  ext_u,
-// ext_ready, ext_want: see route_row_impl (used only when the row needs no
-// score before its selection; ignored otherwise).
+// lds: kRefineSlots entries owned by this wave (kFilter only).
 template <RoundStyle kStyle = kRoundsLane>
 __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
                                                const float (&bv)[kPerLane], const RowSpec& s,
-                                               uint64_t* lds = nullptr, const double* ext_u = nullptr,
-                                               int* ext_ready = nullptr, int ext_want = 0)
+                                               uint64_t* lds = nullptr)
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
-    return need_all ? route_row_impl<true, kStyle>(v, bv, s, lds)
-                    : route_row_impl<false, kStyle>(v, bv, s, lds, ext_u, ext_ready, ext_want);
-}
-
-// Whether a row of this spec can take its winners' scores from
-// row_unbiased_scores() (no score is needed before the selection).
-__device__ __forceinline__ bool row_scores_after_selection(const RowSpec& s)
-{
-    return !(s.has_bias || (s.scoring == kSoftmax && !s.renorm));
+    return need_all ? route_row_impl<true, kStyle>(v, bv, s, lds) : route_row_impl<false, kStyle>(v, bv, s, lds);
 }
 
 // ---------------------------------------------------------------------------
