@@ -58,11 +58,11 @@ MX_TRAFFIC_SUMMARY = {f: os.path.join(ROOT, "profiles", f"decode_expert_{f}_M1_H
                       for f in ("mxfp4", "mxfp8")}
 GATHER_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gather_shared_add_M2_k6_D7168_traffic.txt")
 GEMM1_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_gemm1_M2_k6_F4096_D7168_traffic.txt")
-KERNEL_SOURCES = ["route_common.hpp", "coherent.hpp", "decode_expert_kernel.hip", "launch.hpp", "router_api.cpp"]
+KERNEL_SOURCES = ["route_common.hpp", "softmax_exp.hpp", "coherent.hpp", "decode_expert_kernel.hip", "launch.hpp", "router_api.cpp"]
 PREFILL_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_router_M8192_H7168_traffic.txt")
-PREFILL_SOURCES = ["route_common.hpp", "coherent.hpp", "prefill_kernel.hip", "launch.hpp", "router_api.cpp"]
-GATHER_SOURCES = ["gather_kernel.hip", "route_common.hpp", "launch.hpp", "router_api.cpp"]
-GEMM1_SOURCES = ["gemm1_kernel.hip", "route_common.hpp", "coherent.hpp", "launch.hpp", "router_api.cpp"]
+PREFILL_SOURCES = ["route_common.hpp", "softmax_exp.hpp", "coherent.hpp", "prefill_kernel.hip", "launch.hpp", "router_api.cpp"]
+GATHER_SOURCES = ["gather_kernel.hip", "route_common.hpp", "softmax_exp.hpp", "launch.hpp", "router_api.cpp"]
+GEMM1_SOURCES = ["gemm1_kernel.hip", "route_common.hpp", "softmax_exp.hpp", "coherent.hpp", "launch.hpp", "router_api.cpp"]
 
 
 def log(msg):

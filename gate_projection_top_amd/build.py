@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "librouter.so")
 
 SOURCES = ["router_api.cpp", "topk_kernel.hip", "decode_kernel.hip", "decode_expert_kernel.hip",
            "prefill_kernel.hip", "gather_kernel.hip", "gemm1_kernel.hip"]
-HEADERS = ["route_common.hpp", "launch.hpp", "coherent.hpp"]
+HEADERS = ["route_common.hpp", "softmax_exp.hpp", "launch.hpp", "coherent.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

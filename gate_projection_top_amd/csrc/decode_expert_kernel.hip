@@ -134,6 +134,9 @@ __global__ __launch_bounds__(kBlockOf<kRows>) void decode_expert_kernel(DecodeLa
     __shared__ int s_loaded;  // load waves whose sums are in `red`
     __shared__ int s_ctl;     // 1: s_tag written; 2: s_role written too
     __shared__ int s_role;    // 0: publisher, 1: finisher
+    __shared__ double s_exp2[kWave][2];  // the exp table (load_exp2_lane), for the routing waves
+    __shared__ float s_bias[kMaxE];      // the selection bias (0 past E and without one)
+    __shared__ int s_aux;                // 1: s_exp2 and s_bias written
 
     const int e = blockIdx.x;  // this workgroup's expert
     const int tid = threadIdx.x;
@@ -145,21 +148,36 @@ __global__ __launch_bounds__(kBlockOf<kRows>) void decode_expert_kernel(DecodeLa
     if (tid == 0) {
         s_loaded = 0;
         s_ctl = 0;
+        s_aux = 0;
     }
     __syncthreads();  // the only barrier before the routing: the warm-up wave never waits
 
     if (wave == kWarmWave) {
-        // Runs the routing code once on a dummy row, at once: whichever
-        // workgroup turns out to be the finisher then finds that code in its
-        // CU's instruction cache when its rows' logits arrive, instead of
-        // fetching it instruction block by block while the row waits.
+        // Fetches the routing waves' exp table and selection bias into LDS
+        // (fetched by a routing wave, a cold line would hold up its poll or
+        // its loads: loads complete in order), then runs the routing code
+        // once on a dummy row: whichever workgroup turns out to be the
+        // finisher then finds that code in its CU's instruction cache when
+        // its rows' logits arrive, instead of fetching it instruction block
+        // by block while the row waits.
+        const Exp2Lane et = load_exp2_lane();
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
         float v[kPerLane], bv[kPerLane];
 #pragma unroll
+        for (int j = 0; j < kPerLane; ++j)  // bias past E reads as 0 (out-of-range loads return zero)
+            bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  brs, (lane * kPerLane + j) * 4, 0, 0));
+        s_exp2[lane][0] = et.hi;
+        s_exp2[lane][1] = et.lo;
+#pragma unroll
         for (int j = 0; j < kPerLane; ++j) {
+            s_bias[lane * kPerLane + j] = bv[j];
             v[j] = 0.0625f * (float)(lane * kPerLane + j);
             bv[j] = 0.f;
         }
-        const RowResult res = route_row<kFilter>(v, bv, spec, sel[kWarmWave]);
+        __hip_atomic_store(&s_aux, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const RowResult res = route_row<kFilter>(v, bv, spec, sel[kWarmWave], et);
         asm volatile("; warm-up row %0 %1" ::"v"(res.idx), "v"(res.w));  // keep the pass
         return;
     }
@@ -300,12 +318,15 @@ __global__ __launch_bounds__(kBlockOf<kRows>) void decode_expert_kernel(DecodeLa
 
     // ---- phase 2 (finisher): load wave t routes token t
     const uint32_t tag = s_tag;
-    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
     if (wave < M) {
         const int t = wave;
+        // the warm-up wave's table and bias (in LDS before the poll starts)
+        wait_lds_at_least(&s_aux, 1);
+        const Exp2Lane et{s_exp2[lane][0], s_exp2[lane][1]};
+        float bv[kPerLane];
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) bv[j] = s_bias[lane * kPerLane + j];
         float v[kPerLane];
-        float bv[kPerLane] = {0.f, 0.f, 0.f, 0.f};
         bool gave_up = false;
         const int off = (t * kMaxE + lane * kPerLane) * 8;
         // valid[j]: expert 4L+j exists (slots past E are never published)
@@ -367,17 +388,13 @@ __global__ __launch_bounds__(kBlockOf<kRows>) void decode_expert_kernel(DecodeLa
             const u32x4v zero = {0u, 0u, 0u, 0u};
             __builtin_amdgcn_raw_buffer_store_b128(zero, srs, off, 0, kCoherent);
             __builtin_amdgcn_raw_buffer_store_b128(zero, srs, off + 16, 0, kCoherent);
-#pragma unroll
-            for (int j = 0; j < kPerLane; ++j)
-                bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                      brs, (lane * kPerLane + j) * 4, 0, 0));
             if (a.logits_out) {
                 float* lo = a.logits_out + (int64_t)t * a.E + lane * kPerLane;
 #pragma unroll
                 for (int j = 0; j < kPerLane; ++j)
                     if (lane * kPerLane + j < a.E) lo[j] = v[j];
             }
-            const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave]);
+            const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave], et);
             if (lane < a.k) {
                 const int64_t o = (int64_t)t * a.k + lane;
                 a.inds[o] = res.idx;

@@ -118,6 +118,8 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     __shared__ int fin_index;  // this workgroup's finisher index, -1: not a finisher
     __shared__ uint32_t s_tag;  // this launch's tag (row block epoch)
     __shared__ uint64_t sel[kWaves][kRefineSlots];  // selection scratch, one per routing wave
+    __shared__ double exp2_tab[kWave][2];  // the exp table (load_exp2_lane), for the routing waves
+    __shared__ float bias_tab[kMaxE];       // the selection bias (0 past E and without one)
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -180,6 +182,26 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
             }
             fin_index = fin;
         }
+        // The routing waves' exp table and selection bias (past E, and with
+        // no bias, out-of-range buffer loads return 0), fetched here after the
+        // ticket (fetched before it, they would hold up its atomics: loads
+        // complete in order), during the load waves' loads, and handed over
+        // in LDS at the barrier: fetched by a routing wave after the barrier,
+        // a cold line would hold up its poll.
+        const Exp2Lane t = load_exp2_lane();
+        float tb[kPerLane];
+        {
+            const __amdgpu_buffer_rsrc_t brs0 = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j)
+                tb[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      brs0, (lane * kPerLane + j) * 4, 0, 0));
+        }
+        exp2_tab[lane][0] = t.hi;
+        exp2_tab[lane][1] = t.lo;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) bias_tab[lane * kPerLane + j] = tb[j];
     } else {
         // ---- phase 1: partial logits of 16 tokens x 16 experts over one H-split
         const int arow = r * kDecodeTile + (lane & 15);  // MFMA A row  = token
@@ -329,9 +351,6 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
     // the table's (index, tag) slots (routed slot s = t*k + j of the block)
     const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
         a.counters + kDecodeTableSlotWord, 0, a.table_ids ? 64 * 8 : 0, 0x00020000);
-    // bias beyond E reads as 0 (out-of-range buffer loads return zero)
-    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.bias), 0, a.bias ? a.E * 4 : 0, 0x00020000);
 
     // Rows go to the waves in turn starting at wave 1 (wave 0 has just spent
     // its time on the publish, and the others reach this point first).
@@ -366,6 +385,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
             }
         }
     }
+    const Exp2Lane et{exp2_tab[lane][0], exp2_tab[lane][1]};
     for (int it = 0; it < passes; ++it) {
         const int i = slot_of_wave + it * kWaves;  // the finisher's i-th row
         const bool real = i < nrows;               // wave-uniform
@@ -420,9 +440,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
                 }
             }
 #pragma unroll
-            for (int j = 0; j < kPerLane; ++j)
-                bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                      brs, (lane * kPerLane + j) * 4, 0, 0));
+            for (int j = 0; j < kPerLane; ++j) bv[j] = bias_tab[lane * kPerLane + j];
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j) v[j] = (lane * kPerLane + j < a.E) ? sum[j] : 0.f;
             if (a.logits_out) {
@@ -437,7 +455,7 @@ __global__ __launch_bounds__((kLoadWaves + 1) * kWave) void decode_router_kernel
         }
         // a routing wave has a SIMD to itself in the narrow geometry; the
         // wide one puts two or three waves on each SIMD
-        const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave]);
+        const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave], et);
         if (!real) {
             asm volatile("; dummy row %0 %1" :: "v"(res.idx), "v"(res.w));  // keep the pass
             continue;

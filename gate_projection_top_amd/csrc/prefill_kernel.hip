@@ -164,7 +164,7 @@ __device__ __forceinline__ uint64_t* wave_sel(float* tile_f, int wave)
 
 __device__ __forceinline__ void route_tile_rows(const PrefillLaunch& p, float* tile,
                                                 int64_t row0, int r_begin, int r_end, int wave,
-                                                int lane, const float (&bv)[kPerLane])
+                                                int lane, const float (&bv)[kPerLane], const Exp2Lane& et)
 {
     const RowSpec spec{p.E, p.k, p.scoring, p.renorm, p.bias != nullptr};
     const int col = lane * kPerLane;
@@ -178,7 +178,7 @@ __device__ __forceinline__ void route_tile_rows(const PrefillLaunch& p, float* t
                 v[g][j] = (t < r_end && col + j < p.E) ? tile[t * kTileStride + col + j] : 0.f;
         }
         RowResult res[kRowGroup];
-        route_rows<kRowGroup, kFilter>(v, bv, spec, res, wave_sel(tile, wave));
+        route_rows<kRowGroup, kFilter>(v, bv, spec, res, wave_sel(tile, wave), et);
 #pragma unroll
         for (int g = 0; g < kRowGroup; ++g) {
             const int t = t0 + g * kWaves;
@@ -230,7 +230,7 @@ __device__ __forceinline__ void pf_gather_rows(const PrefillLaunch& p, float* ti
 template <int S>
 __device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, float* tile_f, int tile,
                                                   int s, int64_t row0, int r0, int rows, int wave,
-                                                  int lane, const float (&bv)[kPerLane])
+                                                  int lane, const float (&bv)[kPerLane], const Exp2Lane& et)
 {
     const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(p.partials);
     const RowSpec spec{p.E, p.k, p.scoring, p.renorm, p.bias != nullptr};
@@ -271,7 +271,7 @@ __device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, float*
             }
         }
         RowResult res[G];
-        route_rows<G, kFilter>(v, bv, spec, res, wave_sel(tile_f, wave));
+        route_rows<G, kFilter>(v, bv, spec, res, wave_sel(tile_f, wave), et);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int t = r0 + wave + g * kWaves;
@@ -318,7 +318,7 @@ __device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, float*
         }
         RowResult res[G];
         static_assert(G == kRowGroup, "selection scratch holds kRowGroup rows per wave");
-        route_rows<G, kFilter>(v, bv, spec, res, wave_sel(tile_f, wave));
+        route_rows<G, kFilter>(v, bv, spec, res, wave_sel(tile_f, wave), et);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int t = t0 + g * kWaves;
@@ -346,7 +346,7 @@ __device__ __forceinline__ void pf_route_own_rows(const PrefillLaunch& p, float*
 template <int S>
 __device__ __forceinline__ void exchange_and_route(const PrefillLaunch& p, float* tile_f, int& flag,
                                                    int tile, int s, int64_t row0, int tid, int wave,
-                                                   int lane, const float (&bv)[kPerLane])
+                                                   int lane, const float (&bv)[kPerLane], const Exp2Lane& et)
 {
     constexpr int kRowsPer = kBM / S;
     constexpr int kVecPerRow = kBN / 4;
@@ -411,7 +411,7 @@ __device__ __forceinline__ void exchange_and_route(const PrefillLaunch& p, float
     // The done ticket is drawn before routing; its result is needed only after.
     uint32_t prev = 0;
     if (tid == 0) prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (ok) pf_route_own_rows<S>(p, tile_f, tile, s, row0, my_r0, kRowsPer, wave, lane, bv);
+    if (ok) pf_route_own_rows<S>(p, tile_f, tile, s, row0, my_r0, kRowsPer, wave, lane, bv, et);
     __syncthreads();
     if (tid == 0) flag = (prev == (uint32_t)S - 1u);
     __syncthreads();
@@ -424,7 +424,7 @@ __device__ __forceinline__ void exchange_and_route(const PrefillLaunch& p, float
         __syncthreads();
         pf_gather_rows<S>(p, tile_f, tile, q * kRowsPer, kRowsPer, tid);
         __syncthreads();
-        route_tile_rows(p, tile_f, row0, q * kRowsPer, (q + 1) * kRowsPer, wave, lane, bv);
+        route_tile_rows(p, tile_f, row0, q * kRowsPer, (q + 1) * kRowsPer, wave, lane, bv, et);
         if (tid == 0) __hip_atomic_store(abandoned + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid == 0) {
@@ -656,18 +656,19 @@ __global__ __launch_bounds__(kThreads) void prefill_router_kernel(PrefillLaunch 
             if (e < p.E) bv[j] = p.bias[e];
         }
     }
+    const Exp2Lane et = load_exp2_lane();
     if (p.S == 1) {
-        route_tile_rows(p, tile_f, row0, 0, kBM, wave, lane, bv);
+        route_tile_rows(p, tile_f, row0, 0, kBM, wave, lane, bv, et);
         return;
     }
     if (p.S == 16)
-        exchange_and_route<16>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
+        exchange_and_route<16>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv, et);
     else if (p.S == 8)
-        exchange_and_route<8>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
+        exchange_and_route<8>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv, et);
     else if (p.S == 4)
-        exchange_and_route<4>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
+        exchange_and_route<4>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv, et);
     else
-        exchange_and_route<2>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv);
+        exchange_and_route<2>(p, tile_f, flag, tile, s, row0, tid, wave, lane, bv, et);
 }
 
 }  // namespace

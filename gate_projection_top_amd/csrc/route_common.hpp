@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "softmax_exp.hpp"
+
 namespace gpt {
 
 constexpr int kWave = 64;
@@ -256,20 +258,34 @@ constexpr int kFilterCap = 32;
 constexpr int kFilterSlots = kFilterCap + 2;  // + a discard slot, rows kept 16-byte aligned
 constexpr int kFilterTries = 6;
 
-__device__ __forceinline__ int count_at_least(const uint32_t (&c)[kPerLane], uint32_t T)
+// m[j]: the lanes whose code in slot j is at least T (the whole wavefront
+// active).  The four compares write four scalar pairs back to back, so none
+// waits for the previous one's mask to be read (a compare into VCC would);
+// the trailing wait states cover a vector instruction reading the masks.
+__device__ __forceinline__ void masks_at_least(const uint32_t (&c)[kPerLane], uint32_t T, uint64_t (&m)[kPerLane])
 {
-    return __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[0] >= T)) +
-           __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[1] >= T)) +
-           __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[2] >= T)) +
-           __builtin_popcountll(__builtin_amdgcn_ballot_w64(c[3] >= T));
+    asm("v_cmp_le_u32_e64 %0, %4, %5\n\t"
+        "v_cmp_le_u32_e64 %1, %4, %6\n\t"
+        "v_cmp_le_u32_e64 %2, %4, %7\n\t"
+        "v_cmp_le_u32_e64 %3, %4, %8\n\t"
+        "s_nop 4"
+        : "=&s"(m[0]), "=&s"(m[1]), "=&s"(m[2]), "=&s"(m[3])
+        : "s"(T), "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]));
 }
+
+__device__ __forceinline__ int count_masks(const uint64_t (&m)[kPerLane])
+{
+    return (__builtin_popcountll(m[0]) + __builtin_popcountll(m[1])) +
+           (__builtin_popcountll(m[2]) + __builtin_popcountll(m[3]));
+}
+
 
 // The filter's threshold: T = top - D in code space with k <= n <= cap
 // codes at or above it (n returned), D moved by doubling, halving and
 // bisection; false when no try within the budget finds one.  top: the
-// largest code of the row (returned).
+// largest code of the row (returned); m: the masks of T (masks_at_least).
 __device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], int k, uint32_t& T, int& n,
-                                                 uint32_t& top)
+                                                 uint32_t& top, uint64_t (&m)[kPerLane])
 {
     top = wave_max_u32(max(max(c[0], c[1]), max(c[2], c[3])));
     // distances in code space: dlo gave fewer than k codes, dhi more than the cap
@@ -278,7 +294,8 @@ __device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], 
     n = 0;
     for (int t = 0; t < kFilterTries; ++t) {
         T = top > D ? top - D : 1u;  // valid codes are >= 1; absent entries are 0
-        n = count_at_least(c, T);
+        masks_at_least(c, T, m);
+        n = count_masks(m);
         if (n >= k && n <= kFilterCap) return true;
         if (n < k) {
             if (T == 1u) break;  // fewer than k valid codes cannot happen; stop
@@ -359,26 +376,27 @@ __device__ __forceinline__ uint64_t push_by_rank64(int dst, uint64_t v)
 // kScore < 0: no scores.
 template <int kScore>
 __device__ __forceinline__ bool select_filter_impl(const uint32_t (&c)[kPerLane], uint32_t order, int k,
-                                                   uint64_t* lds, int& my_idx, uint32_t& my_code, double& my_u)
+                                                   uint64_t* lds, int& my_idx, uint32_t& my_code, double& my_u,
+                                                   const Exp2Lane& et)
 {
     constexpr bool kScored = kScore >= 0;
     const int lane = threadIdx.x & (kWave - 1);
     uint32_t T = 1u, top = 0u;
     int n = 0;
-    const bool found = filter_threshold(c, k, T, n, top);
+    uint64_t m[kPerLane];
+    const bool found = filter_threshold(c, k, T, n, top, m);
     if (!found) return false;
     // compaction: lane L's candidates go to [at, ...), at counting the
-    // candidates of the lower lanes, in slot order; its other entries go to
-    // the discard slot, and lanes n .. cap-1 zero the unused tail, so that
-    // entries 0 .. cap-1 hold the n candidates and then zeros (below every
-    // candidate word).  No write needs a lane mask.
+    // candidates of the lower lanes (from the threshold's masks), in slot
+    // order; its other entries go to the discard slot, and lanes n .. cap-1
+    // zero the unused tail, so that entries 0 .. cap-1 hold the n candidates
+    // and then zeros (below every candidate word).  No write needs a lane mask.
     uint32_t at = 0u;
     bool take[kPerLane];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
         take[j] = c[j] >= T;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(take[j]);
-        at += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        at += __builtin_amdgcn_mbcnt_hi((uint32_t)(m[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], 0u));
     }
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
@@ -396,7 +414,7 @@ __device__ __forceinline__ bool select_filter_impl(const uint32_t (&c)[kPerLane]
             __builtin_amdgcn_sched_barrier(0);
             const float l = order_value((uint32_t)(w >> 32));
             if constexpr (kScore == kSoftmax)
-                u = exp((double)l - (double)order_value(top));
+                u = softmax_exp((double)l - (double)order_value(top), et);
             else
                 u = sqrt_softplus(l);
             asm volatile("" ::"v"(u));  // computed here, not where it is used
@@ -420,7 +438,7 @@ __device__ __forceinline__ bool select_filter(const uint32_t (&c)[kPerLane], uin
                                               uint64_t* lds, int& my_idx, uint32_t& my_code)
 {
     double unused = 0.0;
-    return select_filter_impl<-1>(c, order, k, lds, my_idx, my_code, unused);
+    return select_filter_impl<-1>(c, order, k, lds, my_idx, my_code, unused, Exp2Lane{0.0, 0.0});
 }
 
 // Sqrt-softplus scores with a bias, decided with as little double precision
@@ -465,8 +483,11 @@ __device__ __forceinline__ bool select_refined_softplus(const float (&v)[kPerLan
     }
     uint32_t T = 1u, top = 0u;
     int n = 0;
-    if (!filter_threshold(clo, k, T, n, top)) return false;
-    const int nc = count_at_least(chi, T);
+    uint64_t mlo[kPerLane];
+    if (!filter_threshold(clo, k, T, n, top, mlo)) return false;
+    uint64_t m[kPerLane];
+    masks_at_least(chi, T, m);
+    const int nc = count_masks(m);
     if (nc > kFilterCap) return false;
 
     uint64_t* cand = lds;                      // (logit bits, bias bits) of candidate i
@@ -477,8 +498,7 @@ __device__ __forceinline__ bool select_refined_softplus(const float (&v)[kPerLan
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
         take[j] = chi[j] >= T;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(take[j]);
-        at += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        at += __builtin_amdgcn_mbcnt_hi((uint32_t)(m[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], 0u));
     }
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
@@ -600,7 +620,7 @@ __device__ __forceinline__ void select_rounds(uint32_t (&c)[N][kPerLane], const 
 template <int N, bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
                                                 const float (&bv)[kPerLane], const RowSpec& s,
-                                                RowResult (&out)[N], uint64_t* lds)
+                                                RowResult (&out)[N], uint64_t* lds, const Exp2Lane& et)
 {
     const int lane = threadIdx.x & (kWave - 1);
     bool valid[kPerLane];
@@ -638,8 +658,10 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
 #pragma unroll
             for (int n = 0; n < N; ++n)
 #pragma unroll
-                for (int j = 0; j < kPerLane; ++j)
-                    un[n][j] = valid[j] ? exp((double)v[n][j] - (double)mx[n]) : 0.0;
+                for (int j = 0; j < kPerLane; ++j) {
+                    const double e = softmax_exp((double)v[n][j] - (double)mx[n], et);  // whole wave
+                    un[n][j] = valid[j] ? e : 0.0;
+                }
 #pragma unroll
             for (int n = 0; n < N; ++n)
                 Z[n] = wave_sum_f64(((un[n][0] + un[n][1]) + un[n][2]) + un[n][3]);
@@ -725,10 +747,13 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
             u[n] = j == 0 ? got[0] : (j == 1 ? got[1] : (j == 2 ? got[2] : got[3]));
             if (lane >= s.k) u[n] = 0.0;
         } else {
-            if (softmax) mx[n] = order_value(readlane_u32(my_code[n], 0));  // rank 0 holds the max
-            if (lane < s.k) {
-                const float my_logit = order_value(my_code[n]);
-                u[n] = softmax ? exp((double)my_logit - (double)mx[n]) : sqrt_softplus(my_logit);
+            const float my_logit = order_value(my_code[n]);
+            if (softmax) {
+                mx[n] = order_value(readlane_u32(my_code[n], 0));  // rank 0 holds the max
+                const double e = softmax_exp((double)my_logit - (double)mx[n], et);  // whole wave
+                u[n] = lane < s.k ? e : 0.0;
+            } else if (lane < s.k) {
+                u[n] = sqrt_softplus(my_logit);
             }
         }
     }
@@ -746,16 +771,18 @@ __device__ __forceinline__ void route_rows_impl(const float (&v)[N][kPerLane],
 }
 
 // N rows in lockstep (same spec); rows n carry logits v[n] and get out[n].
-// lds: N * kFilterSlots entries owned by this wave (kFilter only).
+// lds: N * kFilterSlots entries owned by this wave (kFilter only); et: the
+// wave's exp table (load_exp2_lane).
 template <int N, RoundStyle kStyle = kRoundsScalar>
 __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const float (&bv)[kPerLane],
-                                           const RowSpec& s, RowResult (&out)[N], uint64_t* lds = nullptr)
+                                           const RowSpec& s, RowResult (&out)[N], uint64_t* lds,
+                                           const Exp2Lane& et)
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
     if (need_all)
-        route_rows_impl<N, true, kStyle>(v, bv, s, out, lds);
+        route_rows_impl<N, true, kStyle>(v, bv, s, out, lds, et);
     else
-        route_rows_impl<N, false, kStyle>(v, bv, s, out, lds);
+        route_rows_impl<N, false, kStyle>(v, bv, s, out, lds, et);
 }
 
 // One row: the same steps as route_rows, written for a single row (the
@@ -766,7 +793,7 @@ __device__ __forceinline__ void route_rows(const float (&v)[N][kPerLane], const 
 template <bool kNeedAll, RoundStyle kStyle>
 __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
                                                     const float (&bv)[kPerLane], const RowSpec& s,
-                                                    uint64_t* lds)
+                                                    uint64_t* lds, const Exp2Lane& et)
 {
     const int lane = threadIdx.x & (kWave - 1);
     bool valid[kPerLane];
@@ -803,8 +830,10 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
                 if (valid[j]) m = max(m, order_code(v[j]));
             mx = order_value(max_code<kStyle>(m));
 #pragma unroll
-            for (int j = 0; j < kPerLane; ++j)
-                un[j] = valid[j] ? exp((double)v[j] - (double)mx) : 0.0;
+            for (int j = 0; j < kPerLane; ++j) {
+                const double e = softmax_exp((double)v[j] - (double)mx, et);  // whole wave
+                un[j] = valid[j] ? e : 0.0;
+            }
             Z = wave_sum_f64(((un[0] + un[1]) + un[2]) + un[3]);
             // z * (1/Z): within an ulp of z / Z in double, so its rounding
             // to fp32 (all the key keeps) agrees but for ~1e-8 of values
@@ -840,11 +869,11 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     if constexpr (kStyle == kFilter) {
         double su = 0.0;  // the winner's unbiased score, when the filter scored its candidates
         if constexpr (need_all) {
-            selected = select_filter_impl<-1>(c, 0xE4u, s.k, lds, my_idx, my_code, su);
+            selected = select_filter_impl<-1>(c, 0xE4u, s.k, lds, my_idx, my_code, su, et);
         } else {
             // no bias: softmax with renorm, or sqrt-softplus
-            selected = softmax ? select_filter_impl<kSoftmax>(c, 0xE4u, s.k, lds, my_idx, my_code, su)
-                               : select_filter_impl<kSqrtSoftplus>(c, 0xE4u, s.k, lds, my_idx, my_code, su);
+            selected = softmax ? select_filter_impl<kSoftmax>(c, 0xE4u, s.k, lds, my_idx, my_code, su, et)
+                               : select_filter_impl<kSqrtSoftplus>(c, 0xE4u, s.k, lds, my_idx, my_code, su, et);
             if (selected) return RowResult{my_idx, s.renorm ? (float)(su / rank_sum(su)) : (float)su};
         }
     }
@@ -885,10 +914,13 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
         u = j == 0 ? got[0] : (j == 1 ? got[1] : (j == 2 ? got[2] : got[3]));
         if (lane >= s.k) u = 0.0;
     } else {
-        if (softmax) mx = order_value(readlane_u32(my_code, 0));  // rank 0 holds the max
-        if (lane < s.k) {
-            const float my_logit = order_value(my_code);
-            u = softmax ? exp((double)my_logit - (double)mx) : sqrt_softplus(my_logit);
+        const float my_logit = order_value(my_code);
+        if (softmax) {
+            mx = order_value(readlane_u32(my_code, 0));  // rank 0 holds the max
+            const double e = softmax_exp((double)my_logit - (double)mx, et);  // whole wave
+            u = lane < s.k ? e : 0.0;
+        } else if (lane < s.k) {
+            u = sqrt_softplus(my_logit);
         }
     }
     // The bias never enters the weights.
@@ -901,14 +933,16 @@ __device__ __forceinline__ RowResult route_row_impl(const float (&v)[kPerLane],
     return RowResult{my_idx, w};
 }
 
-// lds: kRefineSlots entries owned by this wave (kFilter only).
+// lds: kRefineSlots entries owned by this wave (kFilter only); et: the
+// wave's exp table (load_exp2_lane).
 template <RoundStyle kStyle = kRoundsLane>
 __device__ __forceinline__ RowResult route_row(const float (&v)[kPerLane],
                                                const float (&bv)[kPerLane], const RowSpec& s,
-                                               uint64_t* lds = nullptr)
+                                               uint64_t* lds, const Exp2Lane& et)
 {
     const bool need_all = s.has_bias || (s.scoring == kSoftmax && !s.renorm);
-    return need_all ? route_row_impl<true, kStyle>(v, bv, s, lds) : route_row_impl<false, kStyle>(v, bv, s, lds);
+    return need_all ? route_row_impl<true, kStyle>(v, bv, s, lds, et)
+                    : route_row_impl<false, kStyle>(v, bv, s, lds, et);
 }
 
 // ---------------------------------------------------------------------------

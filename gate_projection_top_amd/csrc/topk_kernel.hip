@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_from_logits_kernel(To
     // one row per wave: no loop, so that nothing is held across rows
     const int64_t row = (int64_t)blockIdx.x * kTopkWaves + wave;
     if (row >= a.M) return;
+    const Exp2Lane et = load_exp2_lane();
     const float* r = a.logits + row * a.E;
     float v[kPerLane] = {0.f, 0.f, 0.f, 0.f};
     if (a.vector_rows) {
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_from_logits_kernel(To
             if (e < a.E) v[j] = r[e];
         }
     }
-    const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave]);
+    const RowResult res = route_row<kFilter>(v, bv, spec, sel[wave], et);
     if (lane < a.k) {
         a.inds[row * a.k + lane] = res.idx;
         a.weights[row * a.k + lane] = res.w;
