@@ -174,10 +174,11 @@ def test_prefill_two_and_one_splits(orc, M, H):
     check_router(orc, case, gi, gw, gl)
 
 
-@pytest.mark.parametrize("M", [520, 8192])
+@pytest.mark.parametrize("M", [520, 4000, 8192, 10000])
 def test_prefill_handover_path_matches(orc, M):
-    """Zero exchange wait: every split but the last hands its rows over; results unchanged."""
-    case = W.prefill_case(M=M, H=1024 if M < 8192 else 7168, seed=77)
+    """Zero exchange wait: splits hand their rows over (16, 8, 4 and 2 K splits);
+    results unchanged."""
+    case = W.prefill_case(M=M, H={8192: 7168, 10000: 256}.get(M, 1024), seed=77)
     x, w, b = bf16_dev(case.x), bf16_dev(case.w), f32_dev(case.bias)
     say(f"prefill hand-over M={M}")
     ref = R.router_fwd(x, w, b, case.k, case.scoring, case.renorm, return_logits=True)
@@ -189,7 +190,7 @@ def test_prefill_handover_path_matches(orc, M):
         R.set_exchange_timeout_us(200)
     for a, g in zip(ref, got):
         assert torch.equal(a.view(torch.int32), g.view(torch.int32))
-    if M < 8192:
+    if M != 8192:
         check_router(orc, case, host(got[0]), host(got[1]), host(got[2]))
 
 
