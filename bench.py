@@ -24,15 +24,17 @@ Also reported (same JSON line):
                 widths M=1/2/8 at H=4096 (cache-hot, and cold from a 537 MB
                 pool), the fused-vs-unfused A/B at those widths (a library GEMM
                 writing logits + router_topk_from_logits), the biased M=2 table
-                on/off delta and M=16/64, the launch-floor probes
-                (libfloorprobes.so), the MXFP4 and MXFP8 gates at M=1 and M=8
+                on/off delta and M=16/64, the launch-floor probes and the
+                streaming-read ceiling of HBM (libfloorprobes.so), the MXFP4
+                and MXFP8 gates at M=1 and M=8
                 (H=7168, 585 / 606 MB pools) and at the 8192-token prefill, the
                 routed gather + shared-expert add at M=2 (explicit rows, all
                 remote, table rows) and at M=4096, the expert GEMM1 on the
                 table at M=2 (F=4096, D=7168, 15 GB of expert weights), the
                 standalone top-k at M=4096, the 8192-token prefill
                 (tokens/s, fraction of bf16 MFMA and HBM peak, and a roofline
-                block of its own), and router_fwd across batch sizes from 16
+                block of its own; with X cold and cache-hot), and router_fwd
+                across batch sizes from 16
                 to 4096 tokens.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--section S]
@@ -635,6 +637,11 @@ def prefill_extras(torch, R, W, dev, args):
         "launch_us": round(p_us, 2),
         "launch_timing": "HIP event pair on the launching stream around the timed graph replays / launch count",
     }
+    # the same call with X cache-hot: one 117 MB activation (inside the 256 MB
+    # Infinity Cache) every call
+    hot_us = graph_call_us(torch, calls[:1] * 4, max(args.steps // 2, 2), 2)
+    ex["prefill_M8192_H7168_hot_x_event_us_per_call"] = round(hot_us, 2)
+    ex["prefill_hot_x_mfma_frac"] = round(flops / (hot_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     # context: the vendor GEMM (hipBLASLt through torch) on the same projection, logits only
     xf = xs[0]
     wpt = wp.t().contiguous()  # [H, E]: no transposed view reaches the library GEMM
@@ -740,6 +747,31 @@ def floor_extras(torch, W, dev, args):
     ex["floor_coherent_load_rtt_us"] = round(acc[1] / 100.0, 3)
     ex["floor_cold_load_rtt_us"] = round(acc[2] / 100.0, 3)
     del pool
+    # the practical HBM read ceiling: a 2 GiB buffer (8x the Infinity Cache)
+    # read once per launch with 16-byte loads, at several grid sizes
+    lib.floor_stream_read.argtypes = [P, ctypes.c_int64, ci, P]
+    nbytes = 2 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+    sums = torch.zeros(16384, dtype=torch.float32, device=dev)
+    best = 0.0
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        run = lambda: check(lib.floor_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, grid,
+                                                  ctypes.c_void_p(sums.data_ptr()), stream()))
+        run()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        start.record()
+        for _ in range(reps):
+            run()
+        end.record()
+        torch.cuda.synchronize()
+        tbs = nbytes * reps / (start.elapsed_time(end) * 1e-3) / 1e12
+        ex[f"hbm_stream_read_{grid}wg_TBs"] = round(tbs, 3)
+        best = max(best, tbs)
+    ex["hbm_stream_read_best_TBs"] = round(best, 3)
+    ex["hbm_stream_read_best_frac_of_8TBs"] = round(best / (HBM_PEAK_GBS / 1000.0), 4)
+    del buf
     log("floor probes done")
     return ex
 

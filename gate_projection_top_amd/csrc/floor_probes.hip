@@ -23,6 +23,10 @@
 // floor_latency: one wave times dependent round trips with the 100 MHz
 // realtime clock: a device-scope atomic, a device-coherent load of a line
 // another XCD wrote, and a plain load of a line not yet in any cache.
+// floor_stream_read: the practical HBM read ceiling the roofline fractions
+// sit under: every 16-byte unit of a buffer far larger than the Infinity
+// Cache read once (each workgroup a contiguous chunk, four loads in flight
+// per thread), one value written per workgroup.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -206,6 +210,28 @@ __global__ __launch_bounds__(64) void floor_latency_kernel(uint32_t* scratch, co
     out[3] = (float)acc;  // keeps the chains alive
 }
 
+// Every unit i < n16 read once: workgroup b reads the contiguous units
+// [b*per, (b+1)*per) (per = n16 / grid rounded up), 1024 units (16 KiB) per
+// round with four 16-byte loads in flight per thread.
+__global__ __launch_bounds__(kThreads) void floor_stream_read_kernel(const u32x4* p, int64_t n16, float* out)
+{
+    __shared__ float part[kThreads / 64];
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < n16 ? lo + per : n16;
+    int64_t i = lo + threadIdx.x;
+    float s = 0.f;
+    for (; i + 3 * kThreads < hi; i += 4 * kThreads) {
+        const u32x4 a = p[i], b = p[i + kThreads], c = p[i + 2 * kThreads], d = p[i + 3 * kThreads];
+        s += (lane_sum(a) + lane_sum(b)) + (lane_sum(c) + lane_sum(d));
+    }
+    for (; i < hi; i += kThreads) s += lane_sum(p[i]);
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +271,15 @@ int floor_latency(uint32_t* scratch, const uint32_t* cold, int reps, float* out,
 {
     if (reps < 1 || !scratch || !cold || !out) return -1;
     hipLaunchKernelGGL(floor_latency_kernel, dim3(1), dim3(64), 0, stream, scratch, cold, reps, out);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// p: bytes (a multiple of 16) readable; out: grid floats.
+int floor_stream_read(const void* p, int64_t bytes, int grid, float* out, hipStream_t stream)
+{
+    if (grid < 1 || bytes < 16 || bytes % 16 != 0 || !p || !out) return -1;
+    hipLaunchKernelGGL(floor_stream_read_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4*>(p), bytes / 16, out);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
