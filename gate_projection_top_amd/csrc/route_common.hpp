@@ -126,12 +126,13 @@ __device__ __forceinline__ double wave_sum_f64(double v)
 // ---------------------------------------------------------------------------
 // Monotone map from a finite fp32 key to uint32 (larger key -> larger code),
 // with -0 folded onto +0.  Code 0 is below every finite key and marks an
-// entry that is absent or already selected.
+// entry that is absent or already selected.  Adding +0 turns -0 into +0
+// (round to nearest) and leaves every other finite value unchanged; then a
+// negative key has all its bits flipped and a non-negative one its sign bit.
 __device__ __forceinline__ uint32_t order_code(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    u = (f == 0.0f) ? 0u : u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // Inverse of order_code (a folded -0 comes back as +0).
