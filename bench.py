@@ -24,8 +24,9 @@ Also reported (same JSON line):
                 widths M=1/2/8 at H=4096 (cache-hot, and cold from a 537 MB
                 pool), the fused-vs-unfused A/B at those widths (a library GEMM
                 writing logits + router_topk_from_logits), the biased M=2 table
-                on/off delta and M=16/64, the launch-floor probes and the
-                streaming-read ceiling of HBM (libfloorprobes.so), the MXFP4
+                on/off delta and M=16/64, the launch-floor probes, the
+                streaming-read ceiling of HBM and the prefill main loop's
+                load streams taken apart (libfloorprobes.so), the MXFP4
                 and MXFP8 gates at M=1 and M=8
                 (H=7168, 585 / 606 MB pools) and at the 8192-token prefill, the
                 routed gather + shared-expert add at M=2 (explicit rows, all
@@ -771,7 +772,31 @@ def floor_extras(torch, W, dev, args):
         best = max(best, tbs)
     ex["hbm_stream_read_best_TBs"] = round(best, 3)
     ex["hbm_stream_read_best_frac_of_8TBs"] = round(best / (HBM_PEAK_GBS / 1000.0), 4)
-    del buf
+    del buf, sums
+    # the 8192-token prefill's main loop taken apart (prefill_stream_probe.hip):
+    # its X and W load streams alone and together, W always hitting, and the
+    # loop with its fragment reads and MFMAs; four activations cycled (cold X)
+    lib.pf_stream_probe.argtypes = [P, P, ci, ci, ci, P, P]
+    Mx, Hx = 8192, 7168
+    xs = W.torch_gaussian_bf16((4, Mx, Hx), 1.0, seed=21, device=dev)
+    wq = W.torch_gaussian_bf16((256, Hx), 1.0 / Hx ** 0.5, seed=22, device=dev)
+    po = torch.zeros(Mx // 128 * 4, dtype=torch.float32, device=dev)
+    for mode, name in ((0, "x_and_w"), (1, "x_only"), (2, "w_only"), (3, "x_and_w_hits"), (4, "main_loop")):
+        def launch(i, mode=mode):
+            check(lib.pf_stream_probe(ctypes.c_void_p(xs[i % 4].data_ptr()), ctypes.c_void_p(wq.data_ptr()),
+                                      Mx, Hx, mode, ctypes.c_void_p(po.data_ptr()), stream()))
+        for i in range(4):
+            launch(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        start.record()
+        for i in range(reps):
+            launch(i)
+        end.record()
+        torch.cuda.synchronize()
+        ex[f"prefill_streams_{name}_us"] = round(start.elapsed_time(end) * 1e3 / reps, 2)
+    del xs, wq, po
     log("floor probes done")
     return ex
 

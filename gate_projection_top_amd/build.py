@@ -41,12 +41,13 @@ FLAGS = [
 ]
 
 
-PROBE_SOURCES = ["floor_probes.hip"]
+PROBE_SOURCES = ["floor_probes.hip", "prefill_stream_probe.hip"]
 PROBE_LIB_PATH = os.path.join(PKG, "libfloorprobes.so")
 
 
 def build_probes(out: str = PROBE_LIB_PATH, verbose: bool = False) -> str:
-    """Compile the launch-floor probes the benchmark times (not part of the router)."""
+    """Compile the measurement probes the benchmark times (launch floor, HBM read
+    ceiling, the prefill main loop's streams); not part of the router."""
     return build(out, verbose, sources=PROBE_SOURCES)
 
 
