@@ -254,10 +254,15 @@ __device__ __forceinline__ uint32_t max_code(uint32_t v)
 // the index and the code of rank j.  Rows where no such T exists within the
 // try budget (many equal or nearly equal codes near the top) return false
 // and leave the outputs untouched; the caller runs the rounds instead.
+// The budget covers biased softmax keys too, whose k-th largest can sit
+// several binades below the top when a peaked probability leads a tail that
+// the bias spreads (logits of standard deviation 4: up to 9 tries, 6 on
+// average, where plain logits need 1-2).
 // `lds`: kFilterSlots entries owned by this wave.
 constexpr int kFilterCap = 32;
 constexpr int kFilterSlots = kFilterCap + 2;  // + a discard slot, rows kept 16-byte aligned
-constexpr int kFilterTries = 6;
+constexpr int kFilterTries = 12;
+constexpr int kFilterTriesUnrolled = 6;  // most rows need one to three
 
 // m[j]: the lanes whose code in slot j is at least T (the whole wavefront
 // active).  The four compares write four scalar pairs back to back, so none
@@ -285,6 +290,8 @@ __device__ __forceinline__ int count_masks(const uint64_t (&m)[kPerLane])
 // codes at or above it (n returned), D moved by doubling, halving and
 // bisection; false when no try within the budget finds one.  top: the
 // largest code of the row (returned); m: the masks of T (masks_at_least).
+// The first tries are unrolled; rows of peaked keys that need more continue
+// in a loop.
 __device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], int k, uint32_t& T, int& n,
                                                  uint32_t& top, uint64_t (&m)[kPerLane])
 {
@@ -293,20 +300,40 @@ __device__ __forceinline__ bool filter_threshold(const uint32_t (&c)[kPerLane], 
     uint32_t D = 3u << 21, dlo = 0u, dhi = 0u;
     T = 1u;
     n = 0;
-    for (int t = 0; t < kFilterTries; ++t) {
+    bool open = true;  // no try has settled the row yet
+#pragma unroll
+    for (int t = 0; t < kFilterTriesUnrolled; ++t) {
         T = top > D ? top - D : 1u;  // valid codes are >= 1; absent entries are 0
         masks_at_least(c, T, m);
         n = count_masks(m);
         if (n >= k && n <= kFilterCap) return true;
         if (n < k) {
-            if (T == 1u) break;  // fewer than k valid codes cannot happen; stop
+            if (T == 1u) { open = false; break; }  // fewer than k valid codes cannot happen; stop
             dlo = D;
             D = dhi ? dlo + ((dhi - dlo) >> 1) : (D > 0x7fffffffu ? 0xffffffffu : 2u * D);
         } else {
             dhi = D;
             D = dlo + ((dhi - dlo) >> 1);
         }
-        if (dhi && dhi - dlo <= 1u) break;  // no threshold separates k..cap codes
+        if (dhi && dhi - dlo <= 1u) { open = false; break; }  // no threshold separates k..cap codes
+    }
+    if (open) {
+#pragma nounroll
+        for (int t = kFilterTriesUnrolled; t < kFilterTries; ++t) {
+            T = top > D ? top - D : 1u;
+            masks_at_least(c, T, m);
+            n = count_masks(m);
+            if (n >= k && n <= kFilterCap) return true;
+            if (n < k) {
+                if (T == 1u) break;
+                dlo = D;
+                D = dhi ? dlo + ((dhi - dlo) >> 1) : (D > 0x7fffffffu ? 0xffffffffu : 2u * D);
+            } else {
+                dhi = D;
+                D = dlo + ((dhi - dlo) >> 1);
+            }
+            if (dhi && dhi - dlo <= 1u) break;
+        }
     }
     return false;
 }
