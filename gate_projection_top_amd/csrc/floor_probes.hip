@@ -26,7 +26,8 @@
 // floor_stream_read: the practical HBM read ceiling the roofline fractions
 // sit under: every 16-byte unit of a buffer far larger than the Infinity
 // Cache read once (each workgroup a contiguous chunk, four loads in flight
-// per thread), one value written per workgroup.
+// per thread), one value written per workgroup; floor_stream_read_nt: the
+// same with non-temporal loads (streaming replacement in the caches).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -213,6 +214,16 @@ __global__ __launch_bounds__(64) void floor_latency_kernel(uint32_t* scratch, co
 // Every unit i < n16 read once: workgroup b reads the contiguous units
 // [b*per, (b+1)*per) (per = n16 / grid rounded up), 1024 units (16 KiB) per
 // round with four 16-byte loads in flight per thread.
+template <bool kNT>
+__device__ __forceinline__ u32x4 stream_load(const u32x4* p)
+{
+    if constexpr (kNT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <bool kNT>
 __global__ __launch_bounds__(kThreads) void floor_stream_read_kernel(const u32x4* p, int64_t n16, float* out)
 {
     __shared__ float part[kThreads / 64];
@@ -222,10 +233,11 @@ __global__ __launch_bounds__(kThreads) void floor_stream_read_kernel(const u32x4
     int64_t i = lo + threadIdx.x;
     float s = 0.f;
     for (; i + 3 * kThreads < hi; i += 4 * kThreads) {
-        const u32x4 a = p[i], b = p[i + kThreads], c = p[i + 2 * kThreads], d = p[i + 3 * kThreads];
+        const u32x4 a = stream_load<kNT>(p + i), b = stream_load<kNT>(p + i + kThreads);
+        const u32x4 c = stream_load<kNT>(p + i + 2 * kThreads), d = stream_load<kNT>(p + i + 3 * kThreads);
         s += (lane_sum(a) + lane_sum(b)) + (lane_sum(c) + lane_sum(d));
     }
-    for (; i < hi; i += kThreads) s += lane_sum(p[i]);
+    for (; i < hi; i += kThreads) s += lane_sum(stream_load<kNT>(p + i));
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
     __syncthreads();
@@ -278,7 +290,15 @@ int floor_latency(uint32_t* scratch, const uint32_t* cold, int reps, float* out,
 int floor_stream_read(const void* p, int64_t bytes, int grid, float* out, hipStream_t stream)
 {
     if (grid < 1 || bytes < 16 || bytes % 16 != 0 || !p || !out) return -1;
-    hipLaunchKernelGGL(floor_stream_read_kernel, dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(floor_stream_read_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4*>(p), bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int floor_stream_read_nt(const void* p, int64_t bytes, int grid, float* out, hipStream_t stream)
+{
+    if (grid < 1 || bytes < 16 || bytes % 16 != 0 || !p || !out) return -1;
+    hipLaunchKernelGGL(floor_stream_read_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const u32x4*>(p), bytes / 16, out);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
