@@ -64,6 +64,14 @@ def test_shapes(orc, M, k, D, pattern):
     check_case(orc, W.gather_case(M, k, D, pattern, seed=M + k))
 
 
+@pytest.mark.parametrize("M,k", [(85, 3), (32, 8), (64, 4)])
+@pytest.mark.parametrize("pattern", ["typical", "some_remote"])
+def test_streaming_load_threshold(orc, M, k, pattern):
+    # 255 rows per call take plain row loads, 256 the non-temporal ones:
+    # both sides of the switch against the oracle
+    check_case(orc, W.gather_case(M, k, 1032, pattern, seed=M * k))
+
+
 def test_large_m(orc):
     check_case(orc, W.gather_case(2048, 8, 4096, "some_remote", seed=5, R=3000))
 
