@@ -546,7 +546,9 @@ def gather_extras(torch, R, W, dev, args):
     ub = W.torch_uniform_f32(Mb * kb, 0.05, 1.0, seed=45, device=dev).view(Mb, kb)
     wb = (ub / ub.sum(dim=1, keepdim=True)).contiguous()
     ob = torch.empty((Mb, D), dtype=torch.bfloat16, device=dev)
-    b_us = graph_call_us(torch, [lambda: R.router_gather_shared_add(yb, rb, wb, sb, out=ob)],
+    # eight back-to-back calls per graph, like the other sections (one call
+    # per replay would add each replay's launch gap to the call)
+    b_us = graph_call_us(torch, [lambda: R.router_gather_shared_add(yb, rb, wb, sb, out=ob)] * 8,
                          max(args.steps // 2, 2), 2)
     bbytes = Mb * kb * D * 2 + 2 * Mb * D * 2 + Mb * kb * 8
     ex["gather_M4096_k8_D7168_event_us_per_call"] = round(b_us, 2)
