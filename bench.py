@@ -694,7 +694,7 @@ def floor_extras(torch, W, dev, args):
     E, H = 256, 7168
     n16 = H * 2 // 16
     pool = torch.randn((POOL, E, H), device=dev, dtype=torch.bfloat16)
-    out = torch.zeros(E + 1, dtype=torch.float32, device=dev)
+    out = torch.zeros(2 * E + 1, dtype=torch.float32, device=dev)  # floor_read: one float per workgroup
     ctr = torch.zeros(16 * 17, dtype=torch.int32, device=dev)
     slots = torch.zeros(E * 2, dtype=torch.int32, device=dev)
     epoch = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -722,6 +722,15 @@ def floor_extras(torch, W, dev, args):
                                                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ctr.data_ptr()),
                                                     ctypes.c_void_p(slots.data_ptr()),
                                                     ctypes.c_void_p(epoch.data_ptr()), 1, stream())),
+        # the same bytes on other grids: 512 x 7 KiB and 128 x 28 KiB
+        "read_512x7k": lambda m: check(lib.floor_read(ctypes.c_void_p(pool[m].data_ptr()), n16 // 2, 2 * E,
+                                                      ctypes.c_void_p(out.data_ptr()), stream())),
+        "read_128x28k": lambda m: check(lib.floor_read(ctypes.c_void_p(pool[m].data_ptr()), 2 * n16, E // 2,
+                                                       ctypes.c_void_p(out.data_ptr()), stream())),
+        "handoff_128x28k": lambda m: check(lib.floor_ticket(ctypes.c_void_p(pool[m].data_ptr()), 2 * n16, E // 2,
+                                                            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ctr.data_ptr()),
+                                                            ctypes.c_void_p(slots.data_ptr()),
+                                                            ctypes.c_void_p(epoch.data_ptr()), 1, stream())),
         "handoff_fixed": lambda m: check(lib.floor_ticket(ctypes.c_void_p(pool[m].data_ptr()), n16, E,
                                                           ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ctr.data_ptr()),
                                                           ctypes.c_void_p(slots.data_ptr()),
