@@ -165,6 +165,20 @@ def test_decode_many_row_blocks(orc, M, scoring, with_bias):
     check_router(orc, case, gi, gw, gl)
 
 
+@pytest.mark.parametrize("scale", [4, 8])
+def test_prefill_peaked_softmax_with_bias(orc, scale):
+    # the prefill case's gate scaled by 4 or 8 (exact in bf16): logits of that
+    # standard deviation, peaked softmax keys with the bias spreading the
+    # tail, so the lockstep groups' threshold searches run past six tries
+    base = W.prefill_case(M=1024, H=1024, seed=90 + scale)
+    w = W.f32_to_bf16_bits(W.bf16_bits_to_f32(base.w) * np.float32(scale))
+    case = W.RouterCase(base.x, w, base.bias, base.k, base.scoring, base.renorm,
+                        name=f"prefill peaked x{scale}")
+    say(f"router {case.name}")
+    gi, gw, gl = run_fwd(case)
+    check_router(orc, case, gi, gw, gl)
+
+
 @pytest.mark.parametrize("M,H", [(10000, 256), (20000, 128)])
 def test_prefill_two_and_one_splits(orc, M, H):
     """10000 rows = 79 tiles (two K splits); 20000 rows = 157 tiles (no split)."""

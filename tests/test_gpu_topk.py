@@ -48,6 +48,23 @@ def test_scoring_variants(orc, scoring, renorm, with_bias):
     check_topk(host(gi), host(gw), ri, rw, what=f"variant s{scoring} r{renorm} b{with_bias}")
 
 
+@pytest.mark.parametrize("std", [4.0, 8.0, 40.0])
+def test_peaked_softmax_with_bias(orc, std):
+    # Logits this wide make the softmax peaked: with a U(-0.02, 0.02) bias
+    # the k-th key sits in the bias-spread tail binades below the top, so the
+    # filter's threshold search runs past its first six (unrolled) tries on
+    # many rows (a CPU simulation of the search at standard deviation 3.65:
+    # 44 % of rows), and at 40 nearly every probability but the top is 0
+    rng = np.random.default_rng(int(std * 10) + 5)
+    logits = (rng.standard_normal((1024, 256)) * std).astype(np.float32)
+    bias = rng.uniform(-0.02, 0.02, 256).astype(np.float32)
+    say(f"topk peaked softmax + bias std={std}")
+    gi, gw = R.router_topk_from_logits(f32_dev(logits), f32_dev(bias), 8, W.SOFTMAX, True)
+    torch.cuda.synchronize()
+    ri, rw = orc.topk_from_logits(logits, bias, 8, W.SOFTMAX, True)
+    check_topk(host(gi), host(gw), ri, rw, what=f"peaked std {std}")
+
+
 @pytest.mark.parametrize("E,k", [(16, 2), (16, 16), (100, 7), (255, 16), (256, 1), (256, 16),
                                  (1, 1), (3, 2), (64, 8)])
 def test_shapes(orc, E, k):
