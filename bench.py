@@ -731,6 +731,11 @@ def floor_extras(torch, W, dev, args):
                                                             ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ctr.data_ptr()),
                                                             ctypes.c_void_p(slots.data_ptr()),
                                                             ctypes.c_void_p(epoch.data_ptr()), 1, stream())),
+        "handoff_after_publish": lambda m: check(lib.floor_ticket(ctypes.c_void_p(pool[m].data_ptr()), n16, E,
+                                                                  ctypes.c_void_p(out.data_ptr()),
+                                                                  ctypes.c_void_p(ctr.data_ptr()),
+                                                                  ctypes.c_void_p(slots.data_ptr()),
+                                                                  ctypes.c_void_p(epoch.data_ptr()), 3, stream())),
         "handoff_fixed": lambda m: check(lib.floor_ticket(ctypes.c_void_p(pool[m].data_ptr()), n16, E,
                                                           ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ctr.data_ptr()),
                                                           ctypes.c_void_p(slots.data_ptr()),

@@ -103,7 +103,9 @@ __global__ __launch_bounds__(kThreads) void floor_read_kernel(const u32x4* w, in
 }
 
 // mode 0: ticket only; mode 1: ticket + tagged publish + poll; mode 2: the
-// tagged publish and poll with no ticket, workgroup 0 the fixed finisher.
+// tagged publish and poll with no ticket, workgroup 0 the fixed finisher;
+// mode 3: publish first, wait for the store, then the ticket: the last
+// arrival reads every slot once (all were published before their tickets).
 // ctr: 16 * 17 words, zero between launches; slots: G 8-byte slots;
 // epoch: one word, advanced by the last arrival (tags are epoch + 1, never 0).
 __global__ __launch_bounds__(kThreads + 64) void floor_ticket_kernel(const u32x4* w, int n16, float* out,
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kThreads + 64) void floor_ticket_kernel(const u32x4
         if (lane == 0) {
             const uint32_t tag = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
             s_tag = tag;  // read before the ticket: the last arrival advances it
-            s_last = mode == 2 ? (blockIdx.x == 0 ? 1 : 0) : (last_arrival(ctr) ? 1 : 0);
+            if (mode != 3) s_last = mode == 2 ? (blockIdx.x == 0 ? 1 : 0) : (last_arrival(ctr) ? 1 : 0);
         }
     }
     // the read (the control wave takes part in the barrier only)
@@ -146,7 +148,12 @@ __global__ __launch_bounds__(kThreads + 64) void floor_ticket_kernel(const u32x4
     if (mode >= 1 && threadIdx.x == 0) {
         const u32x2 v = {__float_as_uint(s), s_tag};
         __builtin_amdgcn_raw_buffer_store_b64(v, rs, (int)blockIdx.x * 8, 0, kCoherent);
+        if (mode == 3) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the write-through store has completed
+            s_last = last_arrival(ctr) ? 1 : 0;
+        }
     }
+    if (mode == 3) __syncthreads();  // s_last
     if (!s_last) return;
     if (mode == 0) {
         if (threadIdx.x == 0) out[0] = s;
@@ -271,7 +278,7 @@ int floor_ticket(const void* w, int n16, int grid, float* out, uint32_t* ctr, vo
                  int mode, hipStream_t stream)
 {
     if (grid < 1 || grid > 256 || n16 < 1 || n16 > kThreads * kMaxLoads || !w || !out || !ctr || !slots ||
-        !epoch || mode < 0 || mode > 2)
+        !epoch || mode < 0 || mode > 3)
         return -1;
     hipLaunchKernelGGL(floor_ticket_kernel, dim3(grid), dim3(kThreads + 64), 0, stream,
                        static_cast<const u32x4*>(w), n16, out, ctr, static_cast<u32x2*>(slots), epoch, mode);
