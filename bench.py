@@ -24,8 +24,10 @@ Also reported (same JSON line):
                 widths M=1/2/8 at H=4096 (cache-hot, and cold from a 537 MB
                 pool), the fused-vs-unfused A/B at those widths (a library GEMM
                 writing logits + router_topk_from_logits), the biased M=2 table
-                on/off delta and M=16/64, the launch-floor probes, the
-                streaming-read ceiling of HBM and the prefill main loop's
+                on/off delta and M=16/64, the launch-floor probes (other
+                grid sizes and hand-off protocols too), the
+                streaming-read ceiling of HBM (plain and non-temporal
+                loads) and the prefill main loop's
                 load streams taken apart (libfloorprobes.so), the MXFP4
                 and MXFP8 gates at M=1 and M=8
                 (H=7168, 585 / 606 MB pools) and at the 8192-token prefill, the
