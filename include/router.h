@@ -311,7 +311,7 @@ int router_set_exchange_timeout_us(int microseconds);
 /* router_fwd for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same
  * one-gate-row-per-workgroup decode kernel, bit-identical results, with its
- * workspace (tagged logit slots, arrival words, a status word: about 17 KiB)
+ * workspace (tagged logit slots, arrival words, a status word: 9,536 bytes)
  * in a statically allocated device array that each GPU holds until the
  * process ends, instead of router_init's workspace.  The call allocates
  * nothing, on the host or the device; router_init (or the first call on a
